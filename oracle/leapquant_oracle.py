@@ -1,0 +1,297 @@
+"""LeapQuant CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+This module is the plain, slow, fp64 reference that the HIP decode path is
+checked against.  Only the test suite, the package's smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does, and it
+shares no code with the HIP kernels or their host library.
+
+Sources (web pages about one preprint; cited by title and section):
+  [EL] "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
+       Quantization" (paper listing page): Abstract, Figure 2, Figure 4,
+       Appendix Table 4.
+  [NL] "LeapQuant: Near-Lossless 8-Bit Recurrent State Quantization for Linear
+       Attention LLMs" (summary card): Key points.
+  [TM] "LeapQuant trims the memory burden of linear-attention models" (news
+       write-up): section "Quantize less often, protect the outliers".
+
+What is computed (all floating point in fp64 unless a step says fp32):
+
+* The delta-rule recurrence, one instance per row of [EL] Appendix Table 4
+  (the equation it instantiates is not printed; the only form that fits every
+  row and its record size is used):
+      u_t = v_t - S_{t-1}^T b_t,   S_t = D_t S_{t-1} + k~_t u_t^T,   o_t = S_t^T q_t
+  with S in R^{dk x dv}.  Gated DeltaNet: D_t = alpha_t I, k~_t = beta_t k_t,
+  b_t = alpha_t k_t.  Kimi Delta Attention (named in [EL] Abstract, absent from
+  the table): D_t = Diag(alpha_t), k~_t = beta_t k_t, b_t = alpha_t * k_t.
+
+* Per-window quantization ([EL] Abstract, Figure 2; [TM]): the quantized
+  boundary state stays fixed for a window of p tokens; within the window the
+  state evolves exactly from it (outputs are the exact recurrence started at
+  the boundary state, which is what the buffered high-precision updates
+  reproduce); after the p-th token the whole state is quantized once.  The
+  oracle writes that definition out densely: no buffer algebra.
+
+* Compensator Tokens ([EL] Abstract, Figure 4; [NL] Key points): r rows of the
+  state kept in fp32; they are part of the boundary state, so they follow the
+  same recurrence as everything else.  Extraction rule (not given by the
+  pages; this build's reading): the r rows of largest L2 norm, ties to the
+  lower row index, stored in descending-norm order.
+
+* Residual smoothing ([EL] Abstract; [TM]): not specified by the pages; this
+  build's reading is a per-value-column absmax scale s_j of the residual
+  (after extraction), 1 for an all-zero column.
+
+* 8-bit quantizer ([EL] Abstract, 8-bit state): symmetric int8 in [-127, 127]
+  with one fp32 scale per row of the smoothed residual.  Every step that
+  decides a code runs in fp32 (the format's precision and the kernel's), with
+  correctly rounded IEEE operations in this exact order:
+      sigma_j = 1/s_j;  q_ij = R_ij*sigma_j;  m_i = max_j |q_ij|;
+      a_i = m_i/127;    inv_i = 127/m_i;      c_ij = clamp(rne(q_ij*inv_i), +-127)
+  (a_i = inv_i = 0 and c_i = 0 for an all-zero row).  Dequantized value:
+  c_ij * a_i * s_j (evaluated in fp64 here).
+
+Parity pins (tests/test_oracle_pins.py): Table 4 closed forms for every row,
+hand-derived quantizer fixtures (tests/golden/), the half-step error bound,
+extraction/smoothing invariants, exact recurrence when quantization is off,
+the p=1 reduction to per-token quantization, and a brute-force dense
+implementation on tiny heads.  Parity unpinned: agreement with the authors'
+own extraction and smoothing rules, which the pages do not state.
+"""
+import numpy as np
+
+GATE_GDN = 0   # D_t = alpha_t I           (Gated DeltaNet row of Table 4)
+GATE_KDA = 1   # D_t = Diag(alpha_t)       (Kimi Delta Attention reading)
+NO_SMOOTH = 1  # flag: s_j = 1 (ablation of residual smoothing)
+
+_F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# Recurrence ([EL] Appendix Table 4)
+# --------------------------------------------------------------------------
+def transition(gate, k, beta, alpha, dk):
+    """Return (d, k~, b) for a batch of states.
+
+    d is the diagonal of D_t as an [n, dk] array.  Shapes: k [n, dk],
+    beta [n], alpha [n] (GDN) or [n, dk] (KDA).
+    """
+    k = np.asarray(k, np.float64)
+    beta = np.asarray(beta, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    n = k.shape[0]
+    if gate == GATE_GDN:
+        d = np.broadcast_to(alpha.reshape(n, 1), (n, dk))
+    elif gate == GATE_KDA:
+        d = alpha.reshape(n, dk)
+    else:
+        raise ValueError("unknown gate")
+    kt = beta.reshape(n, 1) * k
+    b = d * k
+    return d, kt, b
+
+
+def step(S, q, k, v, beta, alpha, gate):
+    """One exact token update on dense fp64 states S [n, dk, dv].
+
+    Returns (o [n, dv], S_new [n, dk, dv], record) where record = (d, k~, u),
+    the buffered update of [EL] Table 4's last column.
+    """
+    n, dk, dv = S.shape
+    d, kt, b = transition(gate, k, beta, alpha, dk)
+    u = np.asarray(v, np.float64) - np.einsum("nij,ni->nj", S, b)
+    S_new = d[:, :, None] * S + kt[:, :, None] * u[:, None, :]
+    o = np.einsum("nij,ni->nj", S_new, np.asarray(q, np.float64))
+    return o, S_new, (d.copy(), kt, u)
+
+
+def replay(B, records):
+    """State after applying buffered records (d_i, k~_i, u_i) to B in order."""
+    S = np.array(B, np.float64, copy=True)
+    for d, kt, u in records:
+        S = np.asarray(d)[:, :, None] * S + np.asarray(kt)[:, :, None] * np.asarray(u)[:, None, :]
+    return S
+
+
+def sequential_exact(S0, tokens, gate, keep_every=0):
+    """Unquantized recurrence over all tokens (fp64).
+
+    tokens: dict of arrays q [T,n,dk], k, v [T,n,dv], beta [T,n], alpha.
+    Returns (outputs [T,n,dv], final state, {t: state after t tokens}) where
+    states are kept every `keep_every` tokens (0: none).
+    """
+    S = np.array(S0, np.float64, copy=True)
+    T = tokens["q"].shape[0]
+    outs = np.empty((T,) + (S.shape[0], S.shape[2]))
+    kept = {}
+    for t in range(T):
+        o, S, _ = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
+                       tokens["beta"][t], tokens["alpha"][t], gate)
+        outs[t] = o
+        if keep_every and (t + 1) % keep_every == 0:
+            kept[t + 1] = S.copy()
+    return outs, S, kept
+
+
+# --------------------------------------------------------------------------
+# Quantized boundary state ([EL] Abstract, Figure 4; [TM])
+# --------------------------------------------------------------------------
+def quantize(S, r, flags=0):
+    """Split an fp32 state into compensator rows + smoothed int8 residual.
+
+    S: [n, dk, dv], values taken as fp32 (the reconstructed FP32 state of
+    [EL] Figure 4).  Returns a dict with codes int8 [n,dk,dv], row_scale
+    fp32 [n,dk], col_scale fp32 [n,dv], comp_idx int32 [n,r], comp_val fp32
+    [n,r,dv].
+    """
+    S32 = np.asarray(S, dtype=_F32)
+    n, dk, dv = S32.shape
+    if not 0 <= r <= dk:
+        raise ValueError("r out of range")
+    # 1. row L2 norms (squared, fp64 sum of exact fp32 squares)
+    S64 = S32.astype(np.float64)
+    norm2 = np.einsum("nij,nij->ni", S64, S64)
+    # 2. top-r rows: descending norm, ties to the lower index (stable sort)
+    comp_idx = np.argsort(-norm2, axis=1, kind="stable")[:, :r].astype(np.int32)
+    # 3. compensator rows keep their fp32 values
+    comp_val = np.take_along_axis(S32, comp_idx[:, :, None].astype(np.int64), axis=1).copy()
+    # 4. residual: extracted rows zeroed
+    R = S32.copy()
+    for s in range(n):
+        R[s, comp_idx[s], :] = 0
+    # 5. smoothing scale per value column (absmax of the residual column)
+    if flags & NO_SMOOTH:
+        col_scale = np.ones((n, dv), _F32)
+    else:
+        col_scale = np.abs(R).max(axis=1).astype(_F32)
+        col_scale[col_scale == 0] = _F32(1)
+    # 6. smoothed residual, fp32 multiply by the fp32 reciprocal
+    sigma = (_F32(1) / col_scale).astype(_F32)
+    Q = (R * sigma[:, None, :]).astype(_F32)
+    # 7. per-row absmax scale and its reciprocal, fp32 divisions
+    m = np.abs(Q).max(axis=2).astype(_F32)
+    nz = m > 0
+    row_scale = np.zeros((n, dk), _F32)
+    inv = np.zeros((n, dk), _F32)
+    row_scale[nz] = (m[nz] / _F32(127)).astype(_F32)
+    inv[nz] = (_F32(127) / m[nz]).astype(_F32)
+    # 8. codes: round half to even, clamp to the symmetric range
+    X = (Q * inv[:, :, None]).astype(_F32)
+    codes = np.clip(np.rint(X), -127, 127).astype(np.int8)
+    return {"codes": codes, "row_scale": row_scale, "col_scale": col_scale,
+            "comp_idx": comp_idx, "comp_val": comp_val}
+
+
+def prerounding_codes(S, boundary):
+    """fp32 values that step 8 of `quantize` rounds, for a given selection.
+
+    Used by tests to tell a code decided at a rounding boundary from a wrong
+    one; the selection, scales and zeroed rows are taken from `boundary`.
+    """
+    S32 = np.asarray(S, dtype=_F32)
+    n = S32.shape[0]
+    R = S32.copy()
+    for s in range(n):
+        R[s, boundary["comp_idx"][s], :] = 0
+    sigma = (_F32(1) / boundary["col_scale"]).astype(_F32)
+    Q = (R * sigma[:, None, :]).astype(_F32)
+    m = np.abs(Q).max(axis=2).astype(_F32)
+    inv = np.zeros_like(m)
+    inv[m > 0] = (_F32(127) / m[m > 0]).astype(_F32)
+    return (Q * inv[:, :, None]).astype(_F32)
+
+
+def dequantize(boundary):
+    """Boundary state B = deQ(codes, a, s) + compensator rows, in fp64."""
+    c = boundary["codes"].astype(np.float64)
+    a = boundary["row_scale"].astype(np.float64)
+    s = boundary["col_scale"].astype(np.float64)
+    B = c * a[:, :, None] * s[:, None, :]
+    idx = boundary["comp_idx"]
+    w = boundary["comp_val"].astype(np.float64)
+    n, r = idx.shape
+    for st in range(n):
+        for c_ in range(r):
+            B[st, idx[st, c_], :] += w[st, c_]
+    return B
+
+
+def copy_boundary(b, sel=None):
+    """Deep copy of a boundary-state dict, optionally restricted to states `sel`."""
+    if sel is None:
+        return {k: np.array(v, copy=True) for k, v in b.items()}
+    return {k: np.array(v[sel], copy=True) for k, v in b.items()}
+
+
+# --------------------------------------------------------------------------
+# Per-window decode ([EL] Figure 2) and the per-token baseline
+# --------------------------------------------------------------------------
+def window(boundary, tokens, t0, length, gate, r, flags=0, quantizer=True):
+    """Decode `length` tokens from `boundary`, then close the window.
+
+    Tokens t0 .. t0+length-1 of `tokens` are used.  Returns
+    (outputs [length, n, dv], records, S_end fp64, next boundary).  With
+    quantizer=False the next boundary is the exact fp64 state instead of a
+    quantized split (used to check that windowing alone changes nothing).
+    """
+    B = dequantize(boundary) if quantizer else np.array(boundary, np.float64, copy=True)
+    S = B
+    outs = []
+    records = []
+    for t in range(t0, t0 + length):
+        o, S, rec = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
+                         tokens["beta"][t], tokens["alpha"][t], gate)
+        outs.append(o)
+        records.append(rec)
+    nxt = quantize(S, r, flags) if quantizer else S
+    return np.stack(outs), records, S, nxt
+
+
+def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None):
+    """Free-running per-window quantized decode over all tokens.
+
+    Returns (outputs [T, n, dv], boundaries) where boundaries[w] is the
+    boundary state at the start of window w (w = 0 is Quantize(S_init));
+    `keep` optionally limits which window indices are stored (plus the last).
+    A final partial window (T not a multiple of p) is closed after its
+    last token.
+    """
+    T = tokens["q"].shape[0]
+    b = quantize(S_init, r, flags) if quantizer else np.array(S_init, np.float64, copy=True)
+    outs = []
+    bounds = {}
+    w = 0
+    t0 = 0
+    while True:
+        if keep is None or w in keep:
+            bounds[w] = b
+        if t0 >= T:
+            break
+        length = min(p, T - t0)
+        o, _, _, b = window(b, tokens, t0, length, gate, r, flags, quantizer)
+        outs.append(o)
+        t0 += length
+        w += 1
+    bounds[w] = b
+    return np.concatenate(outs, axis=0), bounds
+
+
+def run_per_token(S_init, tokens, r, gate, flags=0):
+    """Per-token quantization baseline ([EL] Figure 2, left): the whole state
+    is re-quantized after every update; the token's output is read from the
+    updated state before it is quantized."""
+    T = tokens["q"].shape[0]
+    b = quantize(S_init, r, flags)
+    outs = []
+    for t in range(T):
+        S = dequantize(b)
+        o, S, _ = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
+                       tokens["beta"][t], tokens["alpha"][t], gate)
+        outs.append(o)
+        b = quantize(S, r, flags)
+    return np.stack(outs), b
+
+
+def state_mse(boundary, S_exact):
+    """mean((B - S_exact)^2) per state, B the dequantized boundary state."""
+    B = dequantize(boundary)
+    return ((B - S_exact) ** 2).mean(axis=(1, 2))

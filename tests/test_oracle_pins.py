@@ -1,0 +1,316 @@
+"""Pins that tie the CPU oracle to what the pages and mathematics fix.
+
+Each test names the passage it follows.  Page abbreviations:
+  [EL] "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
+       Quantization" (paper listing page)
+  [TM] "LeapQuant trims the memory burden of linear-attention models"
+None of these tests needs a GPU.
+"""
+import glob
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import leapquant_oracle as O
+from tests import brute
+from workloads import generators as G
+from workloads.configs import CONFIGS, WorkloadConfig
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hx(x):
+    return float.fromhex(x) if isinstance(x, str) else float(x)
+
+
+def _rand_tokens(rng, T, n, dk, dv, kda, alpha_lo=0.05, alpha_hi=1.0):
+    q = rng.standard_normal((T, n, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((T, n, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, n, dv))
+    beta = rng.uniform(0.05, 1.0, (T, n))
+    alpha = rng.uniform(alpha_lo, alpha_hi, (T, n, dk) if kda else (T, n))
+    return {"q": q, "k": k, "v": v, "beta": beta, "alpha": alpha}
+
+
+# ---------------------------------------------------------------------------
+# [EL] Appendix Table 4: closed forms of the recurrence instances
+# ---------------------------------------------------------------------------
+def test_gated_deltanet_closed_form():
+    """Gated DeltaNet row: S_t = alpha (I - beta k k^T) S + beta k v^T, o = S_t^T q.
+
+    dk != dv so a transposed state or operand cannot pass."""
+    rng = np.random.default_rng(1)
+    n, dk, dv = 3, 5, 3
+    S = rng.standard_normal((n, dk, dv))
+    tok = _rand_tokens(rng, 1, n, dk, dv, kda=False)
+    o, S1, rec = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], tok["alpha"][0], O.GATE_GDN)
+    for s in range(n):
+        a, b_ = tok["alpha"][0][s], tok["beta"][0][s]
+        k = tok["k"][0][s]
+        want = a * (np.eye(dk) - b_ * np.outer(k, k)) @ S[s] + b_ * np.outer(k, tok["v"][0][s])
+        np.testing.assert_allclose(S1[s], want, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(o[s], want.T @ tok["q"][0][s], rtol=1e-13, atol=1e-14)
+        # record = (d, k~, u) with u = v - S^T (alpha k): [EL] Table 4 last column
+        np.testing.assert_allclose(rec[1][s], b_ * k, rtol=1e-15)
+        np.testing.assert_allclose(rec[2][s], tok["v"][0][s] - S[s].T @ (a * k), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(rec[0][s], np.full(dk, a), rtol=0)
+
+
+def test_deltanet_row_is_gdn_with_unit_gate():
+    """DeltaNet row (D = I, b = k): S - beta k (k^T S) + beta k v^T."""
+    rng = np.random.default_rng(2)
+    n, dk, dv = 2, 4, 6
+    S = rng.standard_normal((n, dk, dv))
+    tok = _rand_tokens(rng, 1, n, dk, dv, kda=False)
+    alpha = np.ones(n)
+    _, S1, _ = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], alpha, O.GATE_GDN)
+    for s in range(n):
+        k, b_ = tok["k"][0][s], tok["beta"][0][s]
+        want = S[s] - b_ * np.outer(k, k @ S[s]) + b_ * np.outer(k, tok["v"][0][s])
+        np.testing.assert_allclose(S1[s], want, rtol=1e-13, atol=1e-14)
+
+
+def test_kda_closed_form():
+    """Kimi Delta Attention (named in [EL] Abstract; channel-wise decay):
+    S_t = (I - beta k k^T) Diag(alpha) S + beta k v^T."""
+    rng = np.random.default_rng(3)
+    n, dk, dv = 2, 6, 4
+    S = rng.standard_normal((n, dk, dv))
+    tok = _rand_tokens(rng, 1, n, dk, dv, kda=True)
+    o, S1, _ = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], tok["alpha"][0], O.GATE_KDA)
+    for s in range(n):
+        k, b_, al = tok["k"][0][s], tok["beta"][0][s], tok["alpha"][0][s]
+        want = (np.eye(dk) - b_ * np.outer(k, k)) @ np.diag(al) @ S[s] + b_ * np.outer(k, tok["v"][0][s])
+        np.testing.assert_allclose(S1[s], want, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(o[s], want.T @ tok["q"][0][s], rtol=1e-13, atol=1e-14)
+
+
+def test_kda_with_equal_channels_is_gdn():
+    rng = np.random.default_rng(4)
+    n, dk, dv = 3, 8, 5
+    S = rng.standard_normal((n, dk, dv))
+    tok = _rand_tokens(rng, 1, n, dk, dv, kda=False)
+    a_diag = np.repeat(tok["alpha"][0][:, None], dk, axis=1)
+    o1, S1, _ = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], tok["alpha"][0], O.GATE_GDN)
+    o2, S2, _ = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], a_diag, O.GATE_KDA)
+    np.testing.assert_allclose(S1, S2, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-15, atol=0)
+
+
+def test_zero_decay_forgets_state():
+    """alpha = 0: D = 0 and b = 0, so S_t = beta k v^T whatever S_{t-1} was."""
+    rng = np.random.default_rng(5)
+    n, dk, dv = 2, 4, 3
+    S = rng.standard_normal((n, dk, dv)) * 100
+    tok = _rand_tokens(rng, 1, n, dk, dv, kda=False)
+    o, S1, _ = O.step(S, tok["q"][0], tok["k"][0], tok["v"][0], tok["beta"][0], np.zeros(n), O.GATE_GDN)
+    for s in range(n):
+        kq = tok["beta"][0][s] * tok["k"][0][s] @ tok["q"][0][s]
+        np.testing.assert_allclose(o[s], kq * tok["v"][0][s], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Quantizer: hand-derived fixtures, error bound, invariants
+# ---------------------------------------------------------------------------
+QUANT_FIXTURES = sorted(f for f in glob.glob(os.path.join(GOLDEN, "quant_*.json")))
+
+
+@pytest.mark.parametrize("path", QUANT_FIXTURES, ids=[os.path.basename(p) for p in QUANT_FIXTURES])
+def test_quantizer_golden(path):
+    fx = json.load(open(path))
+    S = np.asarray(fx["S"], np.float32)[None]
+    b = O.quantize(S, fx["r"], fx["flags"])
+    e = fx["expect"]
+    dv = S.shape[2]
+    np.testing.assert_array_equal(b["comp_idx"][0], np.asarray(e["comp_idx"], np.int32))
+    np.testing.assert_array_equal(b["comp_val"][0], np.asarray(e["comp_val"], np.float32).reshape(-1, dv))
+    np.testing.assert_array_equal(b["col_scale"][0], np.asarray([_hx(x) for x in e["col_scale"]], np.float32))
+    np.testing.assert_array_equal(b["row_scale"][0], np.asarray([_hx(x) for x in e["row_scale"]], np.float32))
+    np.testing.assert_array_equal(b["codes"][0], np.asarray(e["codes"], np.int8))
+
+
+def _random_states(rng, n, dk, dv, outliers=True):
+    S = (0.02 * rng.standard_normal((n, dk, dv))).astype(np.float32)
+    if outliers:
+        for s in range(n):
+            rows = rng.choice(dk, 3, replace=False)
+            cols = rng.choice(dv, 2, replace=False)
+            S[s, rows] *= rng.uniform(10, 30, (3, 1)).astype(np.float32)
+            S[s, :, cols] *= rng.uniform(10, 30, (2, 1)).astype(np.float32)
+    return S
+
+
+@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (8, 0), (4, O.NO_SMOOTH)])
+def test_half_step_bound(r, flags):
+    """|R - c a s| <= (a s / 2)(1 + 1e-4) for every residual entry; compensator
+    rows reproduce the fp32 state exactly.  The 1e-4 slack covers the five
+    fp32 roundings between R and the rounded code (each <= 2^-24 relative,
+    times |code| <= 127): 0.5 + 127 * 5 * 2^-24 < 0.5 (1 + 1e-4)."""
+    rng = np.random.default_rng(10 + r)
+    S = _random_states(rng, 6, 128, 128)
+    b = O.quantize(S, r, flags)
+    B = O.dequantize(b)
+    for s in range(S.shape[0]):
+        comp = set(b["comp_idx"][s].tolist())
+        for i in range(128):
+            if i in comp:
+                np.testing.assert_array_equal(B[s, i], S[s, i].astype(np.float64))
+                continue
+            step_ = b["row_scale"][s, i].astype(np.float64) * b["col_scale"][s].astype(np.float64)
+            err = np.abs(S[s, i].astype(np.float64) - B[s, i])
+            assert np.all(err <= 0.5 * step_ * (1 + 1e-4) + 0.0), (s, i, (err / step_).max())
+
+
+def test_extraction_and_smoothing_invariants():
+    rng = np.random.default_rng(20)
+    S = _random_states(rng, 8, 128, 128)
+    r = 4
+    b = O.quantize(S, r)
+    for s in range(S.shape[0]):
+        norms = np.linalg.norm(S[s].astype(np.float64), axis=1)
+        idx = b["comp_idx"][s]
+        rest = np.setdiff1d(np.arange(128), idx)
+        # every extracted row is at least as large as every residual row
+        assert norms[idx].min() >= norms[rest].max()
+        # stored in descending-norm order
+        assert np.all(np.diff(norms[idx]) <= 0)
+        R = S[s].copy()
+        R[idx] = 0
+        # smoothing scale is the residual column absmax, so each smoothed
+        # nonzero column peaks at magnitude 1 (up to one reciprocal rounding)
+        np.testing.assert_array_equal(b["col_scale"][s], np.abs(R).max(axis=0))
+        sm = np.abs(R.astype(np.float64) / b["col_scale"][s].astype(np.float64)).max(axis=0)
+        np.testing.assert_allclose(sm, 1.0, rtol=2e-7)
+        # every nonzero residual row uses the full code range
+        c = b["codes"][s].astype(np.int32)
+        assert np.all(np.abs(c[rest]).max(axis=1) == 127)
+        assert np.all(c[idx] == 0)
+        assert c.min() >= -127
+
+
+def test_config0_planted_rows_are_extracted():
+    """The four x20 rows planted in the single-head workload are exactly the
+    compensator rows of the first boundary state ([EL] Abstract: compensators
+    keep the largest outliers)."""
+    cfg = CONFIGS[0]
+    g = G.make_generator(cfg.seed, "cpu")
+    S = G.initial_state(cfg, 1, g, "cpu").numpy()
+    norms = np.linalg.norm(S[0].astype(np.float64), axis=1)
+    planted = np.nonzero(norms > 5 * np.median(norms))[0]
+    assert len(planted) == 4
+    b = O.quantize(S, cfg.r)
+    assert sorted(b["comp_idx"][0].tolist()) == sorted(planted.tolist())
+
+
+# ---------------------------------------------------------------------------
+# Per-window quantization ([EL] Figure 2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("p", [1, 2, 5, 16])
+def test_windowing_without_quantization_is_exact(kda, p):
+    """With the quantizer switched off, windowed decode equals the sequential
+    recurrence: windowing changes nothing but where rounding enters."""
+    rng = np.random.default_rng(30 + p)
+    n, dk, dv, T = 3, 16, 12, 37
+    S0 = rng.standard_normal((n, dk, dv))
+    tok = _rand_tokens(rng, T, n, dk, dv, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    o_ref, S_ref, _ = O.sequential_exact(S0, tok, gate)
+    o_w, bounds = O.run_windowed(S0, tok, p, 0, gate, quantizer=False)
+    np.testing.assert_allclose(o_w, o_ref, rtol=1e-12, atol=1e-13)
+    last = bounds[max(bounds)]
+    np.testing.assert_allclose(last, S_ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_window_of_one_is_per_token_quantization(kda):
+    """p = 1, r = 0 reduces per-window quantization to the per-token baseline
+    that re-quantizes after every update ([EL] Figure 2)."""
+    rng = np.random.default_rng(40)
+    n, dk, dv, T = 2, 16, 16, 25
+    S0 = _random_states(rng, n, dk, dv)
+    tok = _rand_tokens(rng, T, n, dk, dv, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    o_w, bounds = O.run_windowed(S0, tok, 1, 0, gate)
+    o_p, b_last = O.run_per_token(S0, tok, 0, gate)
+    np.testing.assert_allclose(o_w, o_p, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(bounds[T]["codes"], b_last["codes"])
+
+
+def test_worked_window_example():
+    fx = json.load(open(os.path.join(GOLDEN, "window_gdn_p2.json")))
+    S0 = np.asarray(fx["S_init"], np.float64)[None]
+    tok = {k: np.asarray(v, np.float64) for k, v in fx["tokens"].items()}
+    gate = O.GATE_GDN if fx["gate"] == "gdn" else O.GATE_KDA
+    outs, bounds = O.run_windowed(S0, tok, fx["p"], fx["r"], gate, fx["flags"])
+    want = np.asarray([[[_hx(x) for x in row] for row in t] for t in fx["expect"]["outputs"]])
+    np.testing.assert_array_equal(outs, want)
+    for w in (0, 1):
+        e = fx["expect"][f"boundary_{w}"]
+        np.testing.assert_array_equal(bounds[w]["codes"][0], np.asarray(e["codes"], np.int8))
+        np.testing.assert_array_equal(bounds[w]["row_scale"][0],
+                                      np.asarray([_hx(x) for x in e["row_scale"]], np.float32))
+
+
+@pytest.mark.parametrize("kda", [False, True])
+@pytest.mark.parametrize("dk,dv,p,r", [(2, 2, 1, 0), (3, 4, 2, 1), (4, 3, 3, 2), (8, 8, 5, 2), (8, 4, 2, 0)])
+def test_brute_force_tiny_heads(kda, dk, dv, p, r):
+    """Independent dense brute force (explicit A_t, scalar-loop quantizer,
+    full sort) agrees with the oracle on tiny heads: outputs to 1e-12,
+    codes, scales and compensators exactly."""
+    rng = np.random.default_rng(dk * 100 + dv * 10 + p + r)
+    n, T = 2, 11
+    S0 = (rng.standard_normal((n, dk, dv)) * 0.3).astype(np.float32)
+    tok = _rand_tokens(rng, T, n, dk, dv, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    outs, bounds = O.run_windowed(S0, tok, p, r, gate)
+    for s in range(n):
+        a_s = tok["alpha"][:, s]
+        bo, bb = brute.brute_windowed(S0[s], tok["q"][:, s], tok["k"][:, s], tok["v"][:, s],
+                                      tok["beta"][:, s], a_s, p, r, kda)
+        np.testing.assert_allclose(outs[:, s], bo, rtol=1e-12, atol=1e-13)
+        for w, (codes, a, sc, idx, wv) in enumerate(bb):
+            ob = bounds[w]
+            np.testing.assert_array_equal(ob["codes"][s], np.asarray(codes, np.int8))
+            np.testing.assert_array_equal(ob["row_scale"][s], np.asarray(a, np.float32))
+            np.testing.assert_array_equal(ob["col_scale"][s], np.asarray(sc, np.float32))
+            np.testing.assert_array_equal(ob["comp_idx"][s], np.asarray(idx, np.int32))
+            np.testing.assert_array_equal(ob["comp_val"][s], np.asarray(wv, np.float32).reshape(r, dv))
+
+
+def test_per_window_beats_per_token_state_error():
+    """Qualitative claim of [EL] Figure 3: quantizing once per window keeps the
+    state closer to the exact recurrence than quantizing every token.  The
+    pages print no values, so only the ordering is checked."""
+    cfg = WorkloadConfig(99, "mse", "gdn", 1, 4, 1, 256, 16, 4, "pct1")
+    g = G.make_generator(7, "cpu")
+    S0 = G.initial_state(cfg, 4, g, "cpu").numpy()
+    tok = {k: v.numpy().astype(np.float64) for k, v in G.token_inputs(cfg, 4, 256, g, "cpu").items()}
+    _, S_exact, _ = O.sequential_exact(S0, tok, O.GATE_GDN)
+    _, bw = O.run_windowed(S0, tok, 16, 4, O.GATE_GDN)
+    _, bp = O.run_per_token(S0, tok, 0, O.GATE_GDN)
+    mse_w = O.state_mse(bw[max(bw)], S_exact).mean()
+    mse_p = O.state_mse(bp, S_exact).mean()
+    assert mse_w < mse_p, (mse_w, mse_p)
+
+
+def test_generators_match_recipe():
+    """Input recipe: unit-norm q and k, beta in (0,1), alpha in (0,1)."""
+    cfg = CONFIGS[3]
+    g = G.make_generator(0, "cpu")
+    tok = G.token_inputs(cfg, 5, 4, g, "cpu")
+    assert tok["alpha"].shape == (4, 5, 128)
+    torch.testing.assert_close(torch.linalg.vector_norm(tok["q"], dim=-1), torch.ones(4, 5))
+    torch.testing.assert_close(torch.linalg.vector_norm(tok["k"], dim=-1), torch.ones(4, 5))
+    assert float(tok["beta"].min()) > 0 and float(tok["beta"].max()) < 1
+    assert float(tok["alpha"].min()) > 0 and float(tok["alpha"].max()) < 1
+    # same seed, same draws
+    g2 = G.make_generator(0, "cpu")
+    tok2 = G.token_inputs(cfg, 5, 4, g2, "cpu")
+    for k in tok:
+        assert torch.equal(tok[k], tok2[k])
