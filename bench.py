@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Decode throughput of the LeapQuant per-window int8 state path on one MI355X.
+
+Workload (default): Gated DeltaNet decode at batch 256 x 32 heads with four
+stacked layers' states resident (4 slabs of 8,192 states, dk = dv = 128),
+window p = 16, r = 4 compensator rows, 1,024 tokens.  One step is the whole
+decode of that batch: quantize the initial states, then 64 windows of
+(16 tokens x 4 layer launches + 4 window closes).  Inputs are synthetic
+(seeded generators) and resident in HBM before timing starts.
+
+Prints one JSON line (see the fields below).  --gpus > 1 is refused: this
+path runs on one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode head-tokens/s (dk=dv=128, int8 state, p=16) + % of HBM BW roofline"
+UNIT = "head-tokens/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def step_bytes(t, dk, dv, r, kda):
+    """Algorithmic HBM bytes of one decode step at window position t (t
+    records already buffered) for one state: int8 codes, row and column
+    scales, compensator rows and indices, t buffered records, the token's
+    inputs, its output and the record it appends."""
+    G = dk if kda else 1
+    R = G + dk + dv
+    return (dk * dv + 4 * (dk + dv) + r * (4 * dv + 4) + 4 * t * R
+            + 4 * (2 * dk + dv + 1 + G) + 4 * dv + 4 * R)
+
+
+def close_bytes(p, dk, dv, r, kda):
+    """Algorithmic HBM bytes of one window close for one state: read and
+    write the boundary state, read the p buffered records."""
+    G = dk if kda else 1
+    R = G + dk + dv
+    boundary = dk * dv + 4 * (dk + dv) + r * (4 * dv + 4)
+    return 2 * boundary + 4 * p * R
+
+
+def bytes_per_head_token(p, dk, dv, r, kda):
+    dec = sum(step_bytes(t, dk, dv, r, kda) for t in range(p)) / p
+    return dec + close_bytes(p, dk, dv, r, kda) / p
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=2, help="workload id (default: the batch-256 4-layer workload)")
+    ap.add_argument("--tokens", type=int, default=0, help="tokens per step (default: the workload's)")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-states", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(states shard with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import recurrent_state_quant_amd as lq
+    from workloads import generators as G
+    from workloads.configs import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda = cfg.gate == "kda"
+    T = args.tokens or cfg.steps
+    assert T % cfg.p == 0
+    L, nl = cfg.layers, cfg.states_per_layer
+    n = cfg.n_states
+    windows = T // cfg.p
+
+    # ---- inputs, resident in HBM (untimed)
+    t_gen = time.time()
+    g = G.make_generator(cfg.seed, dev)
+    S_init = G.initial_state(cfg, n, g, dev)
+    tok = G.token_inputs(cfg, n, T, g, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] generated {n} states x {T} tokens in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    slabs = [lq.LeapQuantState(nl, cfg.p, cfg.r, cfg.gate, dev) for _ in range(L)]
+    outs = [torch.empty((nl, cfg.dv), device=dev) for _ in range(L)]
+    S_l = [S_init[l * nl:(l + 1) * nl] for l in range(L)]
+
+    def sl(x, t, l):
+        return x[t, l * nl:(l + 1) * nl]
+
+    def quantize_phase():
+        for l in range(L):
+            lq.leapquant_quantize_state(slabs[l], S_l[l])
+
+    def decode_phase(w):
+        for j in range(cfg.p):
+            t = w * cfg.p + j
+            for l in range(L):
+                lq.leapquant_decode_step(slabs[l], j, sl(tok["q"], t, l), sl(tok["k"], t, l),
+                                         sl(tok["v"], t, l), sl(tok["beta"], t, l),
+                                         sl(tok["alpha"], t, l), outs[l])
+
+    def close_phase():
+        for l in range(L):
+            lq.leapquant_window_close(slabs[l], cfg.p)
+
+    if args.mode == "graph":
+        stream = torch.cuda.Stream(device=dev)
+        # one warm eager pass on the capture stream before capturing
+        with torch.cuda.stream(stream):
+            quantize_phase(); decode_phase(0); close_phase()
+        torch.cuda.synchronize()
+        gq = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gq, stream=stream):
+            quantize_phase()
+        gd = []
+        for w in range(windows):
+            gw = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gw, stream=stream):
+                decode_phase(w)
+            gd.append(gw)
+        gc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gc, stream=stream):
+            close_phase()
+        torch.cuda.synchronize()
+        run_q, run_d, run_c = gq.replay, (lambda w: gd[w].replay()), gc.replay
+    else:
+        stream = torch.cuda.current_stream(dev)
+        run_q, run_d, run_c = quantize_phase, decode_phase, close_phase
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(windows)]
+
+    def one_step(record):
+        run_q()
+        for w in range(windows):
+            if record:
+                ev[w][0].record(stream)
+            run_d(w)
+            if record:
+                ev[w][1].record(stream)
+            run_c()
+            if record:
+                ev[w][2].record(stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            one_step(False)
+        torch.cuda.synchronize()
+        dec_ms = close_ms = 0.0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            one_step(True)
+            torch.cuda.synchronize()   # events are reused per step: read them now
+            dec_ms += sum(e[0].elapsed_time(e[1]) for e in ev)
+            close_ms += sum(e[1].elapsed_time(e[2]) for e in ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    ms_per_step = 1e3 * wall / args.steps
+    head_tokens = n * T
+    value = head_tokens / (wall / args.steps)
+    bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda)
+    n_dec = args.steps * windows * cfg.p * L
+    dec_avg_ms = dec_ms / n_dec
+    dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(cfg.p)) / cfg.p
+    dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    close_avg_ms = close_ms / (args.steps * windows * L)
+    close_gbs = nl * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda) / (close_avg_ms * 1e-3) / 1e9
+    whole_gbs = value * bpht / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "gate": cfg.gate, "batch": cfg.batch, "heads": cfg.heads,
+                   "layers": L, "states": n, "dk": cfg.dk, "dv": cfg.dv, "p": cfg.p, "r": cfg.r,
+                   "tokens": T, "state_storage": "int8 codes + fp32 scales, fp32 compensators",
+                   "launch": args.mode},
+        "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": round(dec_bytes),
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
+        "window_close": {"avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1)},
+        "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
+                       "bytes_per_head_token": round(bpht, 1)},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, cfg, S_init, tok)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, cfg, S_init, tok):
+    """The CPU oracle, free-running on a bounded sample of the same inputs."""
+    import numpy as np
+    import torch
+
+    from oracle import leapquant_oracle as O
+
+    ns = min(args.cpu_sample_states, cfg.states_per_layer)
+    Ts = min(args.cpu_sample_tokens, tok["q"].shape[0])
+    idx = torch.arange(ns, device=S_init.device)
+    S0 = S_init.index_select(0, idx).cpu().numpy()
+    tk = {k: v[:Ts].index_select(1, idx).cpu().numpy().astype(np.float64) for k, v in tok.items()}
+    gate = O.GATE_GDN if cfg.gate == "gdn" else O.GATE_KDA
+    c0, t0 = os.times(), time.perf_counter()
+    O.run_windowed(S0, tk, cfg.p, cfg.r, gate, keep=set())
+    wall = time.perf_counter() - t0
+    c1 = os.times()
+    cpu = (c1.user + c1.system) - (c0.user + c0.system)
+    return {"value": round(ns * Ts / wall, 1), "unit": UNIT, "cores": max(1, round(cpu / wall)),
+            "kind": "oracle", "sample": f"{ns} states x {Ts} tokens of layer 0, free-running, fp64 numpy",
+            "wall_s": round(wall, 2), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * leapquant.h -- C ABI of the LeapQuant decode hot path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operations follow the pages about LeapQuant:
+ *   [EL] "LeapQuant: Efficient Linear Attention with Accurate Recurrent State
+ *        Quantization" (paper listing page): Abstract, Figure 2 (per-token
+ *        vs per-window quantization), Figure 4 (state = quantized residual +
+ *        compensator tokens + buffered updates), Appendix Table 4 (the
+ *        delta-rule instances and the buffered record (d_i, k~_i, u_i)).
+ *   [TM] "LeapQuant trims the memory burden of linear-attention models"
+ *        (news write-up), section "Quantize less often, protect the
+ *        outliers" (window, compensators, smoothing across channels).
+ *
+ * Model.  Each of n independent states S (dk x dv, one per sequence, head and
+ * layer) evolves by the delta rule of [EL] Table 4:
+ *     u_t = v_t - S_{t-1}^T b_t,   S_t = D_t S_{t-1} + k~_t u_t^T,   o_t = S_t^T q_t
+ *   LQ_GATE_GDN (Gated DeltaNet row): D_t = alpha_t I, k~_t = beta_t k_t,
+ *                b_t = alpha_t k_t (alpha_t one scalar per state).
+ *   LQ_GATE_KDA (Kimi Delta Attention): D_t = Diag(alpha_t), k~_t = beta_t k_t,
+ *                b_t = alpha_t * k_t (alpha_t one value per key channel).
+ * Between window boundaries the state is kept as ([EL] Figure 2, Figure 4)
+ *   B  = deQ(codes, a, s) + sum_c e_{idx_c} w_c^T      (fixed, low-bit)
+ *   records (d_i, k~_i, u_i), i < t                    (fp32 buffer)
+ * and S_{t-1} is exactly the recurrence started from B and replayed through
+ * the records.  deQ(c, a, s)_ij = c_ij * a_i * s_j.  At the end of a window
+ * the state is rebuilt and split again: the r rows of largest L2 norm become
+ * compensator rows w_c (fp32, descending norm, ties to the lower row), the
+ * remaining residual R is smoothed per value column by s_j = max_i |R_ij|
+ * (1 for a zero column, or 1 everywhere with LQ_NO_SMOOTH) and quantized
+ * per row: m_i = max_j |R_ij * (1/s_j)|, a_i = m_i / 127,
+ * c_ij = clamp(rne(R_ij * (1/s_j) * (127/m_i)), -127, 127), all in fp32.
+ *
+ * Conventions for every entry point.
+ *   - All array pointers are DEVICE memory owned by the caller; the library
+ *     allocates, frees and synchronizes nothing and keeps no global state,
+ *     so calls are reentrant.  lq_params and lq_state are host structs read
+ *     only during the call.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without waiting.  Device faults surface at the caller's next
+ *     synchronization.
+ *   - Arrays are dense, row-major, in the shapes given below; n is the
+ *     leading dimension of every per-state array.
+ *   - Alignment: codes and every float array whose per-state extent is a
+ *     multiple of 128 floats must be 16-byte aligned; beta, a scalar alpha,
+ *     comp_idx and a scalar buf_gate need 4-byte alignment.
+ *   - Argument errors are returned synchronously and nothing is launched:
+ *       LQ_ERR_NULL        a required pointer is NULL
+ *       LQ_ERR_SHAPE       n < 1, p outside [1, 64], r outside [0, 16],
+ *                          unknown gate or flag, t or len out of range
+ *       LQ_ERR_UNSUPPORTED dk != 128 or dv != 128
+ *       LQ_ERR_ALIGN       a pointer violates the alignment above
+ *       LQ_ERR_ALIAS       an output range overlaps an input range
+ *     A failed launch returns LQ_ERR_HIP.
+ *   - Values are not checked: NaN or Inf inputs give unspecified (but
+ *     in-bounds) results.  comp_idx entries outside [0, dk) are ignored when
+ *     the state is read.
+ */
+#ifndef LEAPQUANT_H
+#define LEAPQUANT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LEAPQUANT_ABI_VERSION 1
+
+typedef enum lq_status {
+  LQ_OK = 0,
+  LQ_ERR_NULL = -1,
+  LQ_ERR_SHAPE = -2,
+  LQ_ERR_UNSUPPORTED = -3,
+  LQ_ERR_ALIGN = -4,
+  LQ_ERR_ALIAS = -5,
+  LQ_ERR_HIP = -6
+} lq_status;
+
+typedef enum lq_gate {
+  LQ_GATE_GDN = 0, /* scalar decay per state and token (Gated DeltaNet)  */
+  LQ_GATE_KDA = 1  /* per-key-channel decay (Kimi Delta Attention)       */
+} lq_gate;
+
+enum { LQ_NO_SMOOTH = 1u /* ablation: s_j = 1 for every column */ };
+
+typedef struct lq_params {
+  int32_t n;      /* number of independent states in the slab (>= 1)     */
+  int32_t dk;     /* key dimension, rows of S; must be 128                */
+  int32_t dv;     /* value dimension, columns of S; must be 128           */
+  int32_t p;      /* window length in tokens, 1..64                       */
+  int32_t r;      /* compensator rows per state, 0..16                    */
+  int32_t gate;   /* lq_gate                                              */
+  uint32_t flags; /* 0 or LQ_NO_SMOOTH                                    */
+} lq_params;
+
+/* One slab of n states.  The first five arrays are the boundary state
+ * (the prefix-cache snapshot); the last three are the window buffer.  For
+ * r == 0, comp_idx and comp_val may be NULL. */
+typedef struct lq_state {
+  int8_t *codes;     /* [n][dk][dv] int8 residual codes c_ij                */
+  float *row_scale;  /* [n][dk]     a_i                                     */
+  float *col_scale;  /* [n][dv]     s_j                                     */
+  int32_t *comp_idx; /* [n][r]      row index of each compensator row       */
+  float *comp_val;   /* [n][r][dv]  compensator rows w_c                    */
+  float *buf_gate;   /* GDN: [n][p]; KDA: [n][p][dk]   d_i (alpha_i)        */
+  float *buf_k;      /* [n][p][dk]  k~_i = beta_i k_i                       */
+  float *buf_u;      /* [n][p][dv]  u_i                                     */
+} lq_state;
+
+/* Split fp32 states S [n][dk][dv] into the boundary state of `st` (codes,
+ * row_scale, col_scale, comp_idx, comp_val); the window buffer is neither
+ * read nor written.  This is the window-boundary split of [EL] Figure 4
+ * applied to a state that has no buffered updates, i.e. the quantized
+ * boundary state that precedes the first window of [EL] Figure 2.  S must
+ * not overlap the boundary-state arrays. */
+int leapquant_quantize_state(const lq_params *prm, const float *S,
+                             const lq_state *st, hipStream_t stream);
+
+/* Decode token t (0-based position inside the current window, 0 <= t < p)
+ * for all n states ([EL] Figure 2, per-window quantization; [EL] Abstract,
+ * compensators share the update path of real tokens).  Reads the boundary
+ * state and the records 0..t-1 of the buffer, writes
+ *   o[n][dv] = S_t^T q_t, with S_t the exact recurrence from the boundary
+ *              state through the buffered records and this token,
+ * and appends record t: buf_gate[.][t] = alpha_t, buf_k[.][t] = beta_t k_t,
+ * buf_u[.][t] = v_t - S_{t-1}^T b_t.
+ * Inputs: q, k [n][dk]; v [n][dv]; beta [n]; alpha [n] (GDN) or [n][dk]
+ * (KDA); all read-only.  o must not overlap any input or state array.
+ * The caller closes the window (leapquant_window_close with len = p)
+ * after t = p - 1 and before the next t = 0. */
+int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t,
+                          const float *q, const float *k, const float *v,
+                          const float *beta, const float *alpha, float *o,
+                          hipStream_t stream);
+
+/* Close a window of len buffered records (1 <= len <= p; len < p only for
+ * a final partial window): rebuild S_len = D_len..D_1 B + sum_i
+ * (D_len..D_{i+1}) k~_i u_i^T in fp32, then split it into compensator rows,
+ * smoothing scales, row scales and int8 codes, overwriting the boundary
+ * state in place ([EL] Figure 2: quantize once per window; [EL] Figure 4).
+ * The buffer is read, not cleared. */
+int leapquant_window_close(const lq_params *prm, const lq_state *st,
+                           int32_t len, hipStream_t stream);
+
+/* Write the boundary state B = deQ(codes, a, s) + compensator rows as fp32
+ * S_out [n][dk][dv] (the state the next window starts from; used for state
+ * error tracking and prefix-cache reads).  S_out must not overlap `st`. */
+int leapquant_dequantize_state(const lq_params *prm, const lq_state *st,
+                               float *S_out, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *leapquant_status_string(int status);
+
+/* LEAPQUANT_ABI_VERSION of the loaded library. */
+int leapquant_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEAPQUANT_H */

@@ -1,0 +1,19 @@
+"""LeapQuant decode hot path for AMD Instinct MI355X (gfx950).
+
+Per-window int8 recurrent-state decode for Gated DeltaNet and Kimi Delta
+Attention layers, with fp32 compensator rows and per-column residual
+smoothing, as hand-written HIP kernels behind the C ABI of
+include/leapquant.h.  This package is the thin Python binding: it marshals
+torch device tensors and streams into the C calls and runs nothing itself.
+"""
+from ._lib import (LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_SMOOTH, LeapQuantError, LIB_PATH, load)
+from .api import (LeapQuantState, leapquant_abi_version, leapquant_decode_step,
+                  leapquant_dequantize_state, leapquant_quantize_state,
+                  leapquant_status_string, leapquant_window_close)
+
+__all__ = [
+    "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_SMOOTH", "LeapQuantError", "LIB_PATH", "load",
+    "LeapQuantState", "leapquant_abi_version", "leapquant_decode_step",
+    "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",
+    "leapquant_window_close",
+]

@@ -1,0 +1,132 @@
+"""Python binding of the LeapQuant C ABI (argument marshalling only).
+
+The functions carry the C names and forward to libleapquant.so; every step of
+the decode path runs in the HIP kernels.  PyTorch provides device memory and
+streams.  See include/leapquant.h for the semantics of each call.
+"""
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_F32, _I32, _I8 = torch.float32, torch.int32, torch.int8
+
+
+def _gate_id(gate):
+    if gate in ("gdn", L.LQ_GATE_GDN):
+        return L.LQ_GATE_GDN
+    if gate in ("kda", L.LQ_GATE_KDA):
+        return L.LQ_GATE_KDA
+    raise ValueError(f"unknown gate {gate!r}")
+
+
+def _ptr(x, dtype, shape, name):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be in device memory")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(x.data_ptr()) if x.numel() else None
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class LeapQuantState:
+    """Device arrays of one slab of n states: boundary state + window buffer.
+
+    codes int8 [n,dk,dv]; row_scale [n,dk]; col_scale [n,dv]; comp_idx int32
+    [n,r]; comp_val [n,r,dv]; buf_gate [n,p] (gdn) or [n,p,dk] (kda);
+    buf_k [n,p,dk]; buf_u [n,p,dv].
+    """
+
+    BOUNDARY = ("codes", "row_scale", "col_scale", "comp_idx", "comp_val")
+
+    def __init__(self, n, p, r, gate="gdn", device="cuda", flags=0, dk=128, dv=128):
+        self.n, self.p, self.r, self.dk, self.dv = int(n), int(p), int(r), int(dk), int(dv)
+        self.gate = _gate_id(gate)
+        self.flags = int(flags)
+        dev = torch.device(device)
+        self.device = dev
+        self.codes = torch.zeros((n, dk, dv), dtype=_I8, device=dev)
+        self.row_scale = torch.zeros((n, dk), dtype=_F32, device=dev)
+        self.col_scale = torch.ones((n, dv), dtype=_F32, device=dev)
+        self.comp_idx = torch.zeros((n, r), dtype=_I32, device=dev)
+        self.comp_val = torch.zeros((n, r, dv), dtype=_F32, device=dev)
+        gshape = (n, p) if self.gate == L.LQ_GATE_GDN else (n, p, dk)
+        self.buf_gate = torch.zeros(gshape, dtype=_F32, device=dev)
+        self.buf_k = torch.zeros((n, p, dk), dtype=_F32, device=dev)
+        self.buf_u = torch.zeros((n, p, dv), dtype=_F32, device=dev)
+
+    def params(self):
+        return L.LqParams(self.n, self.dk, self.dv, self.p, self.r, self.gate, self.flags)
+
+    def ptrs(self):
+        def vp(x):
+            return x.data_ptr() if x.numel() else None
+        return L.LqState(vp(self.codes), vp(self.row_scale), vp(self.col_scale),
+                         vp(self.comp_idx), vp(self.comp_val), vp(self.buf_gate),
+                         vp(self.buf_k), vp(self.buf_u))
+
+    def boundary(self):
+        """The boundary-state tensors (views; clone for a snapshot)."""
+        return {k: getattr(self, k) for k in self.BOUNDARY}
+
+    def snapshot(self):
+        return {k: getattr(self, k).clone() for k in self.BOUNDARY}
+
+    def load_boundary(self, b):
+        """Copy a boundary state (dict of tensors or arrays) into this slab."""
+        for k in self.BOUNDARY:
+            src = torch.as_tensor(b[k]).to(getattr(self, k).dtype)
+            getattr(self, k).copy_(src.reshape(getattr(self, k).shape), non_blocking=False)
+
+
+def leapquant_quantize_state(state, S, stream=None):
+    n, dk, dv = state.n, state.dk, state.dv
+    s = _ptr(S, _F32, (n, dk, dv), "S")
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_quantize_state(ctypes.byref(prm), s, ctypes.byref(st),
+                                              _stream(stream, state.device)))
+
+
+def leapquant_decode_step(state, t, q, k, v, beta, alpha, o, stream=None):
+    n, dk, dv = state.n, state.dk, state.dv
+    ashape = (n,) if state.gate == L.LQ_GATE_GDN else (n, dk)
+    args = [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
+            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
+            _ptr(o, _F32, (n, dv), "o")]
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_decode_step(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
+                                           _stream(stream, state.device)))
+
+
+def leapquant_window_close(state, length, stream=None):
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), int(length),
+                                            _stream(stream, state.device)))
+
+
+def leapquant_dequantize_state(state, S_out, stream=None):
+    n, dk, dv = state.n, state.dk, state.dv
+    s = _ptr(S_out, _F32, (n, dk, dv), "S_out")
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), s,
+                                                _stream(stream, state.device)))
+
+
+def leapquant_status_string(status):
+    return L.load().leapquant_status_string(int(status)).decode()
+
+
+def leapquant_abi_version():
+    return L.load().leapquant_abi_version()

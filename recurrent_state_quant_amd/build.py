@@ -1,0 +1,37 @@
+"""Build libleapquant.so in-tree with hipcc for gfx950."""
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+LIB_PATH = os.path.join(PKG_DIR, "libleapquant.so")
+SOURCES = [os.path.join(PKG_DIR, "csrc", f) for f in ("lq_kernels.hip", "lq_abi.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc_command(out=LIB_PATH, extra=()):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # packed fp32 VALU ops stay off: only scalar fp32 ops are emitted
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG_DIR, "csrc"),
+            *extra, "-o", out, *SOURCES]
+
+
+def build(verbose=False):
+    """Compile the HIP library; raises CalledProcessError on failure."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = hipcc_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise subprocess.CalledProcessError(res.returncode, cmd, res.stdout, res.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,206 @@
+// C ABI of the LeapQuant decode path: argument validation and launches.
+// Operation semantics are documented in include/leapquant.h.
+#include <stdint.h>
+
+#include "leapquant.h"
+#include "lq_kernels.h"
+
+namespace {
+
+constexpr int kDim = 128;
+constexpr int kMaxP = 64;
+constexpr int kMaxR = 16;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range span(const void *p, size_t bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return Range{b, b + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_params(const lq_params *prm) {
+  if (!prm) return LQ_ERR_NULL;
+  if (prm->dk != kDim || prm->dv != kDim) return LQ_ERR_UNSUPPORTED;
+  if (prm->n < 1 || prm->p < 1 || prm->p > kMaxP || prm->r < 0 || prm->r > kMaxR) return LQ_ERR_SHAPE;
+  if (prm->gate != LQ_GATE_GDN && prm->gate != LQ_GATE_KDA) return LQ_ERR_SHAPE;
+  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_SMOOTH)) return LQ_ERR_SHAPE;
+  return LQ_OK;
+}
+
+// Boundary-state arrays (always needed).
+int check_boundary(const lq_params *prm, const lq_state *st) {
+  if (!st) return LQ_ERR_NULL;
+  if (!st->codes || !st->row_scale || !st->col_scale) return LQ_ERR_NULL;
+  if (prm->r > 0 && (!st->comp_idx || !st->comp_val)) return LQ_ERR_NULL;
+  if (!aligned(st->codes, 16) || !aligned(st->row_scale, 16) || !aligned(st->col_scale, 16))
+    return LQ_ERR_ALIGN;
+  if (prm->r > 0 && (!aligned(st->comp_idx, 4) || !aligned(st->comp_val, 16))) return LQ_ERR_ALIGN;
+  return LQ_OK;
+}
+
+int check_buffer(const lq_params *prm, const lq_state *st) {
+  if (!st->buf_gate || !st->buf_k || !st->buf_u) return LQ_ERR_NULL;
+  const uintptr_t ga = prm->gate == LQ_GATE_KDA ? 16 : 4;
+  if (!aligned(st->buf_gate, ga) || !aligned(st->buf_k, 16) || !aligned(st->buf_u, 16))
+    return LQ_ERR_ALIGN;
+  return LQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int leapquant_abi_version(void) { return LEAPQUANT_ABI_VERSION; }
+
+const char *leapquant_status_string(int status) {
+  switch (status) {
+    case LQ_OK: return "ok";
+    case LQ_ERR_NULL: return "a required pointer is NULL";
+    case LQ_ERR_SHAPE: return "invalid size or parameter (n, p, r, gate, flags, t or len)";
+    case LQ_ERR_UNSUPPORTED: return "unsupported head size (dk and dv must be 128)";
+    case LQ_ERR_ALIGN: return "pointer is not aligned as required";
+    case LQ_ERR_ALIAS: return "an output overlaps an input";
+    case LQ_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_state *st,
+                             hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if ((rc = check_boundary(prm, st))) return rc;
+  if (!S) return LQ_ERR_NULL;
+  if (!aligned(S, 16)) return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const Range src = span(S, n * kDim * kDim * sizeof(float));
+  if (overlap(src, span(st->codes, n * kDim * kDim)) ||
+      overlap(src, span(st->row_scale, n * kDim * sizeof(float))) ||
+      overlap(src, span(st->col_scale, n * kDim * sizeof(float))) ||
+      (prm->r > 0 && (overlap(src, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
+                      overlap(src, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+    return LQ_ERR_ALIAS;
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.S_in = S;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.len = 0;
+  a.flags = prm->flags;
+  return hip_status(lq::launch_quantize_state(a, stream));
+}
+
+int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
+                          const float *k, const float *v, const float *beta, const float *alpha,
+                          float *o, hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if ((rc = check_boundary(prm, st))) return rc;
+  if ((rc = check_buffer(prm, st))) return rc;
+  if (t < 0 || t >= prm->p) return LQ_ERR_SHAPE;
+  if (!q || !k || !v || !beta || !alpha || !o) return LQ_ERR_NULL;
+  const bool kda = prm->gate == LQ_GATE_KDA;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4))
+    return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const size_t vec = n * kDim * sizeof(float);
+  const Range out = span(o, vec);
+  const size_t gate_elems = kda ? n * prm->p * kDim : n * prm->p;
+  if (overlap(out, span(q, vec)) || overlap(out, span(k, vec)) || overlap(out, span(v, vec)) ||
+      overlap(out, span(beta, n * sizeof(float))) ||
+      overlap(out, span(alpha, kda ? vec : n * sizeof(float))) ||
+      overlap(out, span(st->codes, n * kDim * kDim)) ||
+      overlap(out, span(st->row_scale, vec)) || overlap(out, span(st->col_scale, vec)) ||
+      overlap(out, span(st->buf_gate, gate_elems * sizeof(float))) ||
+      overlap(out, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
+      overlap(out, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
+      (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
+                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+    return LQ_ERR_ALIAS;
+  lq::DecodeArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.t = t;
+  return hip_status(lq::launch_decode_step(a, kda, stream));
+}
+
+int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len,
+                           hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if ((rc = check_boundary(prm, st))) return rc;
+  if ((rc = check_buffer(prm, st))) return rc;
+  if (len < 1 || len > prm->p) return LQ_ERR_SHAPE;
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.S_in = nullptr;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.len = len;
+  a.flags = prm->flags;
+  return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
+}
+
+int leapquant_dequantize_state(const lq_params *prm, const lq_state *st, float *S_out,
+                               hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if ((rc = check_boundary(prm, st))) return rc;
+  if (!S_out) return LQ_ERR_NULL;
+  if (!aligned(S_out, 16)) return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const Range out = span(S_out, n * kDim * kDim * sizeof(float));
+  if (overlap(out, span(st->codes, n * kDim * kDim)) ||
+      overlap(out, span(st->row_scale, n * kDim * sizeof(float))) ||
+      overlap(out, span(st->col_scale, n * kDim * sizeof(float))) ||
+      (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
+                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+    return LQ_ERR_ALIAS;
+  lq::DequantArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.S_out = S_out;
+  a.n = prm->n;
+  a.r = prm->r;
+  return hip_status(lq::launch_dequantize(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (lq_abi.cpp) and the gfx950
+// kernels (lq_kernels.hip).  Arguments are validated by the caller.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace lq {
+
+struct DecodeArgs {
+  const int8_t *codes;
+  const float *row_scale;
+  const float *col_scale;
+  const int32_t *comp_idx;
+  const float *comp_val;
+  float *buf_gate;
+  float *buf_k;
+  float *buf_u;
+  const float *q;
+  const float *k;
+  const float *v;
+  const float *beta;
+  const float *alpha;
+  float *o;
+  int n, p, r, t;
+};
+
+struct CloseArgs {
+  int8_t *codes;
+  float *row_scale;
+  float *col_scale;
+  int32_t *comp_idx;
+  float *comp_val;
+  const float *buf_gate;
+  const float *buf_k;
+  const float *buf_u;
+  const float *S_in;  // quantize_state source; nullptr for a window close
+  int n, p, r, len;
+  unsigned flags;
+};
+
+struct DequantArgs {
+  const int8_t *codes;
+  const float *row_scale;
+  const float *col_scale;
+  const int32_t *comp_idx;
+  const float *comp_val;
+  float *S_out;
+  int n, r;
+};
+
+hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream);
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t stream);
+
+}  // namespace lq

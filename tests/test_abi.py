@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: exported symbols and argument validation.
+
+Every call here is rejected by the library's host-side validation before any
+launch, so fake (never dereferenced) device addresses are safe to pass.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recurrent_state_quant_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "leapquant.h")
+FAKE = 0x7F0000000000  # 4 KiB aligned, never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(leapquant_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libleapquant.so not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    decl = _declared_functions()
+    assert decl == sorted(L.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.leapquant_abi_version() == 1
+    for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
+                 L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
+        assert lib.leapquant_status_string(code)
+
+
+def _params(**kw):
+    d = dict(n=4, dk=128, dv=128, p=16, r=4, gate=L.LQ_GATE_GDN, flags=0)
+    d.update(kw)
+    return L.LqParams(d["n"], d["dk"], d["dv"], d["p"], d["r"], d["gate"], d["flags"])
+
+
+def _state(**kw):
+    n, p, r = 4, 16, 4
+    base = FAKE
+    sizes = dict(codes=n * 128 * 128, row_scale=n * 512, col_scale=n * 512, comp_idx=n * r * 4,
+                 comp_val=n * r * 512, buf_gate=n * p * 512, buf_k=n * p * 512, buf_u=n * p * 512)
+    addrs = {}
+    for name, sz in sizes.items():
+        addrs[name] = base
+        base += (sz + 4095) // 4096 * 4096
+    addrs.update(kw)
+    return L.LqState(*[addrs[f] for f, _ in L.LqState._fields_]), base
+
+
+def _decode(lib, prm, st, t=0, **kw):
+    _, base = _state()
+    vec = 4 * 512
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+    a.update(kw)
+    return lib.leapquant_decode_step(ctypes.byref(prm) if prm is not None else None,
+                                     ctypes.byref(st) if st is not None else None, t,
+                                     a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=64), L.LQ_ERR_UNSUPPORTED), (dict(dv=256), L.LQ_ERR_UNSUPPORTED),
+    (dict(n=0), L.LQ_ERR_SHAPE), (dict(p=0), L.LQ_ERR_SHAPE), (dict(p=65), L.LQ_ERR_SHAPE),
+    (dict(r=-1), L.LQ_ERR_SHAPE), (dict(r=17), L.LQ_ERR_SHAPE), (dict(gate=2), L.LQ_ERR_SHAPE),
+    (dict(flags=2), L.LQ_ERR_SHAPE),
+])
+def test_bad_params(lib, kw, code):
+    st, _ = _state()
+    prm = _params(**kw)
+    assert _decode(lib, prm, st) == code
+    assert lib.leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), 16, None) == code
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), FAKE + (1 << 36), ctypes.byref(st), None) == code
+    assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), FAKE + (1 << 36), None) == code
+
+
+def test_null_pointers(lib):
+    st, _ = _state()
+    prm = _params()
+    assert _decode(lib, None, st) == L.LQ_ERR_NULL
+    assert _decode(lib, prm, None) == L.LQ_ERR_NULL
+    for f in ("codes", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_gate", "buf_k", "buf_u"):
+        bad, _ = _state(**{f: 0})
+        assert _decode(lib, prm, bad) == L.LQ_ERR_NULL, f
+    for f in ("q", "k", "v", "beta", "alpha", "o"):
+        assert _decode(lib, prm, st, **{f: 0}) == L.LQ_ERR_NULL, f
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), None, ctypes.byref(st), None) == L.LQ_ERR_NULL
+    assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), None, None) == L.LQ_ERR_NULL
+    # buffer pointers are not needed by quantize/dequantize, compensators not at r = 0
+    nobuf, _ = _state(buf_gate=0, buf_k=0, buf_u=0, comp_idx=0, comp_val=0)
+    assert lib.leapquant_window_close(ctypes.byref(_params(r=0)), ctypes.byref(nobuf), 16, None) == L.LQ_ERR_NULL
+
+
+def test_misaligned(lib):
+    prm = _params()
+    for f in ("codes", "row_scale", "col_scale", "comp_val", "buf_k", "buf_u"):
+        st, _ = _state()
+        setattr(st, f, getattr(st, f) + 4)
+        assert _decode(lib, prm, st) == L.LQ_ERR_ALIGN, f
+    st, _ = _state()
+    st.comp_idx = st.comp_idx + 2
+    assert _decode(lib, prm, st) == L.LQ_ERR_ALIGN
+    for f in ("q", "k", "v", "o"):
+        _, base = _state()
+        vec = 4 * 512
+        addr = dict(q=base, k=base + vec, v=base + 2 * vec, o=base + 4 * vec)[f] + 4
+        assert _decode(lib, prm, _state()[0], **{f: addr}) == L.LQ_ERR_ALIGN, f
+    # KDA alpha is read as vectors: 16-byte alignment required; GDN alpha is scalar
+    kda = _params(gate=L.LQ_GATE_KDA)
+    _, base = _state()
+    assert _decode(lib, kda, _state()[0], alpha=base + 3 * 2048 + 68) == L.LQ_ERR_ALIGN
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), FAKE + (1 << 36) + 8, ctypes.byref(_state()[0]), None) == L.LQ_ERR_ALIGN
+
+
+def test_window_position_ranges(lib):
+    st, _ = _state()
+    prm = _params()
+    assert _decode(lib, prm, st, t=-1) == L.LQ_ERR_SHAPE
+    assert _decode(lib, prm, st, t=16) == L.LQ_ERR_SHAPE
+    assert lib.leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), 0, None) == L.LQ_ERR_SHAPE
+    assert lib.leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), 17, None) == L.LQ_ERR_SHAPE
+
+
+def test_aliasing_rejected(lib):
+    st, base = _state()
+    prm = _params()
+    assert _decode(lib, prm, st, o=base) == L.LQ_ERR_ALIAS            # o == q
+    assert _decode(lib, prm, st, o=st.buf_u + 512) == L.LQ_ERR_ALIAS  # o inside the buffer
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), st.codes, ctypes.byref(st), None) == L.LQ_ERR_ALIAS
+    assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), st.row_scale, None) == L.LQ_ERR_ALIAS

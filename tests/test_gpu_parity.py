@@ -1,0 +1,283 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Entry-point tests feed both sides the same boundary state and buffered
+records; window tests start every window of the GPU from the oracle's own
+boundary state (the oracle never reads a GPU result); free-running tests let
+the GPU run on its own and compare until the two trajectories legitimately
+part at a rounding boundary.
+"""
+import numpy as np
+import pytest
+import torch
+
+import recurrent_state_quant_amd as lq
+from oracle import leapquant_oracle as O
+from tests import parity as P
+from tests.gpu_run import boundary_np, run_window, to_np, tokens_np, upload_boundary
+from workloads import generators as G
+from workloads.configs import CONFIGS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    lq.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _states_with_outliers(rng, n, scale=0.02):
+    S = (scale * rng.standard_normal((n, 128, 128))).astype(np.float32)
+    for s in range(n):
+        rows = rng.choice(128, 3, replace=False)
+        cols = rng.choice(128, 2, replace=False)
+        S[s, rows] *= rng.uniform(10, 30, (3, 1)).astype(np.float32)
+        S[s, :, cols] *= rng.uniform(10, 30, (2, 1)).astype(np.float32)
+    return S
+
+
+def _dev(x, dtype=torch.float32):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(device=DEV, dtype=dtype)
+
+
+def _gate(g):
+    return O.GATE_GDN if g == "gdn" else O.GATE_KDA
+
+
+# ---------------------------------------------------------------------------
+# a9 / a6-a8: quantize_state on the same fp32 input is bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (8, 0), (16, 0), (4, lq.LQ_NO_SMOOTH)])
+def test_quantize_state_bitexact(r, flags):
+    rng = np.random.default_rng(100 + r + 7 * flags)
+    n = 37
+    S = _states_with_outliers(rng, n)
+    S[3] = 0.0                       # all-zero state: ties, zero columns
+    S[5] = 0.0
+    S[5, 17, 99] = -0.25             # single nonzero entry
+    S[7, 10] = S[7, 20]              # duplicated rows: exact norm tie
+    st = lq.LeapQuantState(n, 16, r, "gdn", DEV, flags)
+    lq.leapquant_quantize_state(st, _dev(S))
+    torch.cuda.synchronize()
+    ref = O.quantize(S, r, flags)
+    stats = P.compare_boundary(boundary_np(st), ref, S, r, "quantize_state", exact=True)
+    assert stats["ties"] <= 1
+
+
+def test_quantize_state_workload_initial_states():
+    for cid in (0, 1, 3):
+        cfg = CONFIGS[cid]
+        n = 1 if cid == 0 else 64
+        S = G.initial_state(cfg, n, G.make_generator(cfg.seed, "cpu"), "cpu").numpy()
+        st = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, DEV)
+        lq.leapquant_quantize_state(st, _dev(S))
+        torch.cuda.synchronize()
+        P.compare_boundary(boundary_np(st), O.quantize(S, cfg.r), S, cfg.r, f"cfg{cid} init", exact=True)
+
+
+def test_dequantize_state():
+    rng = np.random.default_rng(5)
+    n, r = 9, 4
+    S = _states_with_outliers(rng, n)
+    b = O.quantize(S, r)
+    st = lq.LeapQuantState(n, 16, r, "gdn", DEV)
+    upload_boundary(st, b)
+    out = torch.empty((n, 128, 128), device=DEV)
+    lq.leapquant_dequantize_state(st, out)
+    P.assert_close(to_np(out), O.dequantize(b), "dequantize", rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# a1-a4: one decode step against synthetic buffered records
+# ---------------------------------------------------------------------------
+def _random_window_inputs(rng, n, p, nrec, gate, r):
+    S = _states_with_outliers(rng, n)
+    b = O.quantize(S, r)
+    kda = gate == "kda"
+    recs = []
+    for _ in range(nrec):
+        a = rng.uniform(0.05, 1.0, (n, 128) if kda else (n,)).astype(np.float32)
+        k = rng.standard_normal((n, 128))
+        k /= np.linalg.norm(k, axis=1, keepdims=True)
+        kt = (rng.uniform(0.05, 1.0, (n, 1)) * k).astype(np.float32)
+        u = (0.5 * rng.standard_normal((n, 128))).astype(np.float32)
+        recs.append((a, kt, u))
+    return b, recs
+
+
+def _upload_records(st, recs, gate):
+    for i, (a, kt, u) in enumerate(recs):
+        st.buf_gate[:, i] = _dev(a)
+        st.buf_k[:, i] = _dev(kt)
+        st.buf_u[:, i] = _dev(u)
+
+
+def _oracle_records(recs, gate):
+    out = []
+    for a, kt, u in recs:
+        n = kt.shape[0]
+        d = np.broadcast_to(a.astype(np.float64).reshape(n, -1), (n, 128))
+        out.append((d, kt.astype(np.float64), u.astype(np.float64)))
+    return out
+
+
+def _token(rng, n, gate):
+    q = rng.standard_normal((n, 128)); q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k = rng.standard_normal((n, 128)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((n, 128))
+    beta = rng.uniform(0.05, 1, n)
+    alpha = rng.uniform(0.05, 1, (n, 128) if gate == "kda" else n)
+    return {x: y.astype(np.float32) for x, y in dict(q=q, k=k, v=v, beta=beta, alpha=alpha).items()}
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("p,t", [(1, 0), (16, 0), (16, 1), (16, 9), (16, 15), (32, 16), (32, 31), (64, 40), (64, 63)])
+@pytest.mark.parametrize("r", [0, 4, 16])
+def test_decode_step_entry(gate, p, t, r):
+    rng = np.random.default_rng(1000 * p + 10 * t + r + (gate == "kda"))
+    n = 19
+    b, recs = _random_window_inputs(rng, n, p, t, gate, r)
+    st = lq.LeapQuantState(n, p, r, gate, DEV)
+    upload_boundary(st, b)
+    _upload_records(st, recs, gate)
+    tok = _token(rng, n, gate)
+    o = torch.empty((n, 128), device=DEV)
+    lq.leapquant_decode_step(st, t, _dev(tok["q"]), _dev(tok["k"]), _dev(tok["v"]), _dev(tok["beta"]),
+                             _dev(tok["alpha"]), o)
+    torch.cuda.synchronize()
+    S_prev = O.replay(O.dequantize(b), _oracle_records(recs, gate))
+    t64 = {k: v.astype(np.float64) for k, v in tok.items()}
+    o_ref, _, (d, kt, u) = O.step(S_prev, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate))
+    P.assert_close(to_np(o), o_ref, "o_t")
+    P.assert_close(to_np(st.buf_u[:, t]), u, "u_t")
+    P.assert_close(to_np(st.buf_k[:, t]), kt, "k~_t", rtol=1e-6, atol=0)
+    np.testing.assert_array_equal(to_np(st.buf_gate[:, t]), tok["alpha"])
+    # records < t untouched
+    for i, (a, ktr, ur) in enumerate(recs):
+        np.testing.assert_array_equal(to_np(st.buf_u[:, i]), ur)
+
+
+# ---------------------------------------------------------------------------
+# a5-a8: window close against synthetic records
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("p,length", [(1, 1), (16, 16), (16, 1), (16, 7), (32, 32), (64, 64), (64, 37)])
+@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (8, 0), (4, lq.LQ_NO_SMOOTH)])
+def test_window_close_entry(gate, p, length, r, flags):
+    rng = np.random.default_rng(7 * p + length + 100 * r + flags + (gate == "kda"))
+    n = 21
+    b, recs = _random_window_inputs(rng, n, p, length, gate, r)
+    st = lq.LeapQuantState(n, p, r, gate, DEV, flags)
+    upload_boundary(st, b)
+    _upload_records(st, recs, gate)
+    lq.leapquant_window_close(st, length)
+    torch.cuda.synchronize()
+    S = O.replay(O.dequantize(b), _oracle_records(recs, gate))
+    ref = O.quantize(S, r, flags)
+    P.compare_boundary(boundary_np(st), ref, S.astype(np.float32), r, "window_close")
+
+
+# ---------------------------------------------------------------------------
+# Whole windows: the GPU starts each window from the oracle's boundary
+# ---------------------------------------------------------------------------
+def _workload(cid, n, steps, device="cpu", seed=None):
+    cfg = CONFIGS[cid]
+    g = G.make_generator(cfg.seed if seed is None else seed, device)
+    S0 = G.initial_state(cfg, n, g, device)
+    tok = G.token_inputs(cfg, n, steps, g, device)
+    return cfg, S0, tok
+
+
+@pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 24, 128), (3, 24, 128)])
+def test_oracle_forced_windows(cid, n, steps):
+    cfg, S0, tok = _workload(cid, n, steps)
+    S0n = S0.numpy()
+    tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
+    o_ref, bounds = O.run_windowed(S0n, tokn, cfg.p, cfg.r, _gate(cfg.gate))
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    st = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, DEV)
+    out = torch.empty((steps, n, 128), device=DEV)
+    total = {"flips": 0, "codes": 0, "ties": 0}
+    for w in range(steps // cfg.p):
+        upload_boundary(st, bounds[w])
+        run_window(st, tokd, w * cfg.p, cfg.p, out)
+        torch.cuda.synchronize()
+        sl = slice(w * cfg.p, (w + 1) * cfg.p)
+        P.assert_close(to_np(out[sl]), o_ref[sl], f"cfg{cid} window {w} outputs")
+        _, _, S_end, _ = O.window(bounds[w], tokn, w * cfg.p, cfg.p, _gate(cfg.gate), cfg.r)
+        s = P.compare_boundary(boundary_np(st), bounds[w + 1], S_end.astype(np.float32), cfg.r,
+                               f"cfg{cid} boundary {w + 1}")
+        for k in total:
+            total[k] += s[k]
+    print(f"cfg{cid}: {total}")
+
+
+# ---------------------------------------------------------------------------
+# Free-running: strict until the first legitimate rounding-boundary flip
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 16, 256), (3, 16, 256)])
+def test_free_running(cid, n, steps):
+    cfg, S0, tok = _workload(cid, n, steps)
+    S0n = S0.numpy()
+    tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
+    o_ref, bounds = O.run_windowed(S0n, tokn, cfg.p, cfg.r, _gate(cfg.gate))
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    st = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, DEV)
+    lq.leapquant_quantize_state(st, S0.to(DEV))
+    out = torch.empty((steps, n, 128), device=DEV)
+    diverged = np.zeros(n, bool)
+    worst_rel = 0.0
+    for w in range(steps // cfg.p):
+        run_window(st, tokd, w * cfg.p, cfg.p, out)
+        torch.cuda.synchronize()
+        sl = slice(w * cfg.p, (w + 1) * cfg.p)
+        og, orf = to_np(out[sl]), o_ref[sl]
+        strict = ~diverged
+        if strict.any():
+            P.assert_close(og[:, strict], orf[:, strict], f"cfg{cid} window {w} outputs")
+        if diverged.any():
+            rel = np.linalg.norm(og[:, diverged] - orf[:, diverged]) / np.linalg.norm(orf[:, diverged])
+            worst_rel = max(worst_rel, rel)
+            assert rel < 2e-2, f"cfg{cid} window {w}: diverged trajectories differ by {rel}"
+        gb = boundary_np(st)
+        same = np.all(gb["codes"] == bounds[w + 1]["codes"], axis=(1, 2))
+        if cfg.r:
+            same &= np.all(gb["comp_idx"] == bounds[w + 1]["comp_idx"], axis=1)
+        diverged |= ~same
+    print(f"cfg{cid}: diverged states {diverged.sum()}/{n}, worst diverged rel err {worst_rel:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Determinism and prefix-cache snapshot / resume
+# ---------------------------------------------------------------------------
+def _run_free(cfg, n, steps, S0d, tokd, snapshot_at=None, start=0, st=None):
+    if st is None:
+        st = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, DEV)
+        lq.leapquant_quantize_state(st, S0d)
+    out = torch.zeros((steps, n, 128), device=DEV)
+    snap = None
+    for w in range(start // cfg.p, steps // cfg.p):
+        run_window(st, tokd, w * cfg.p, cfg.p, out)
+        if snapshot_at is not None and (w + 1) * cfg.p == snapshot_at:
+            snap = st.snapshot()
+    torch.cuda.synchronize()
+    return out, st, snap
+
+
+def test_determinism_and_resume():
+    cfg, S0, tok = _workload(1, 96, 96, device=DEV)
+    out1, st1, snap = _run_free(cfg, 96, 96, S0, tok, snapshot_at=48)
+    out2, st2, _ = _run_free(cfg, 96, 96, S0, tok)
+    assert torch.equal(out1, out2)
+    for k in lq.LeapQuantState.BOUNDARY:
+        assert torch.equal(getattr(st1, k), getattr(st2, k)), k
+    st3 = lq.LeapQuantState(96, cfg.p, cfg.r, cfg.gate, DEV)
+    st3.load_boundary(snap)
+    out3, st3, _ = _run_free(cfg, 96, 96, None, tok, start=48, st=st3)
+    assert torch.equal(out3[48:], out1[48:])
+    for k in lq.LeapQuantState.BOUNDARY:
+        assert torch.equal(getattr(st3, k), getattr(st1, k)), k
