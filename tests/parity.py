@@ -36,15 +36,16 @@ def assert_close(gpu, ref, what, rtol=RTOL, atol=ATOL):
 
 
 def near_tie(S32, r):
-    """Per state: True when the oracle's r-th and (r+1)-th largest row norms
-    (or any two within the top r + 1) are closer than TIE_GAP relative."""
+    """Per state: True when two of the oracle's top r + 1 row norms differ,
+    but by less than TIE_GAP relative.  Exactly equal norms are not a near
+    tie: both sides break them by the lower row index."""
     S = np.asarray(S32, np.float32).astype(np.float64)
     n2 = np.sort(np.einsum("nij,nij->ni", S, S), axis=1)[:, ::-1]
     if r == 0:
         return np.zeros(S.shape[0], bool)
     top = n2[:, :r + 1]
     gaps = (top[:, :-1] - top[:, 1:]) / np.maximum(top[:, :-1], 1e-300)
-    return (gaps < 2 * TIE_GAP).any(axis=1)
+    return ((gaps > 0) & (gaps < 2 * TIE_GAP)).any(axis=1)
 
 
 def compare_boundary(gpu, ref, S_ref, r, what, exact=False):

@@ -65,7 +65,7 @@ def test_quantize_state_bitexact(r, flags):
     torch.cuda.synchronize()
     ref = O.quantize(S, r, flags)
     stats = P.compare_boundary(boundary_np(st), ref, S, r, "quantize_state", exact=True)
-    assert stats["ties"] <= 1
+    assert stats["ties"] == 0
 
 
 def test_quantize_state_workload_initial_states():
