@@ -31,11 +31,36 @@ constexpr int D = 128;  // dk == dv == 128
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+typedef float vf2 __attribute__((ext_vector_type(2)));
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef unsigned int vu2 __attribute__((ext_vector_type(2)));
+typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) accesses: every state array is touched once per
+// launch and the working set of a launch is far larger than the caches, so
+// loads and stores bypass cache retention (measured on MI355X: ~7.1 TB/s
+// for nontemporal 16-byte streaming reads against ~6.3 TB/s for plain ones).
 __device__ __forceinline__ float2 ld2(const float *p) {
-  return *reinterpret_cast<const float2 *>(p);
+  const vf2 t = __builtin_nontemporal_load(reinterpret_cast<const vf2 *>(p));
+  return make_float2(t.x, t.y);
+}
+__device__ __forceinline__ float4 ld4(const float *p) {
+  const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4 *>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint4 ldu4(const void *p) {
+  const vu4 t = __builtin_nontemporal_load(reinterpret_cast<const vu4 *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ldu2(const void *p) {
+  const vu2 t = __builtin_nontemporal_load(reinterpret_cast<const vu2 *>(p));
+  return make_uint2(t.x, t.y);
 }
 __device__ __forceinline__ void st2(float *p, float2 v) {
-  *reinterpret_cast<float2 *>(p) = v;
+  __builtin_nontemporal_store(vf2{v.x, v.y}, reinterpret_cast<vf2 *>(p));
+}
+__device__ __forceinline__ void st4(float *p, float4 v) {
+  __builtin_nontemporal_store(vf4{v.x, v.y, v.z, v.w}, reinterpret_cast<vf4 *>(p));
 }
 
 // DPP lane permutes (gfx9 encodings): quad_perm, row_half_mirror, row_mirror.
@@ -75,8 +100,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 // full rows (1 KiB, fully coalesced 128-bit loads) and both vectors
 // (Gamma*alpha*k and Gamma*alpha*q, scaled by a_i) are accumulated from one
 // pass over the codes.
+//
+// Memory-level parallelism: every load a phase needs is issued before the
+// phase waits on any of them.  The buffered records are read in chunks of
+// kRecChunk (all k~, u and gate loads of a chunk in flight together), the
+// first compensator rows and the whole code stream are issued before the
+// first wait, so a wave pays about one memory latency per chunk.
 // ---------------------------------------------------------------------------
-constexpr int kRedStride = 33;   // padded row of the transposed partials
+constexpr int kRecChunk = 16;    // records in flight per chunk
+constexpr int kCompEarly = 4;    // compensator rows loaded with the records
+constexpr int kRedStride = 36;   // padded row of the transposed partials (16B aligned)
 constexpr int kGemvStride = 260; // padded row of the GEMV partials (16B aligned)
 
 template <bool KDA>
@@ -87,19 +120,13 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 
   __shared__ float2 sh_w[D];   // a_i * Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_gy[D];  // Gamma_i * (y_b, y_q)_i
-  __shared__ float2 sh_h[64];  // record weights (h_b, h_q)
+  __shared__ float2 sh_h[kRecChunk];  // record weights (h_b, h_q) of a chunk
   __shared__ __attribute__((aligned(16))) float sh_red[64 * kRedStride];
 
-  // ---- a3 stream first: the 16 KiB of int8 codes of this state
-  const int cc = lane & 7, rg = lane >> 3;
-  const uint4 *csrc =
-      reinterpret_cast<const uint4 *>(A.codes + (size_t)s * D * D) + rg * 8 + cc;
-  uint4 cv[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) cv[m] = csrc[m * 64];
-
-  // ---- a1 token prep
   const size_t vo = (size_t)s * D + 2 * lane;
+  const size_t rec0 = (size_t)s * p;
+
+  // ---- issue: token inputs, the newest record chunk, early compensators
   const float2 kk = ld2(A.k + vo);
   const float2 qq = ld2(A.q + vo);
   const float2 vv = ld2(A.v + vo);
@@ -111,54 +138,99 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     const float a = A.alpha[s];
     al = make_float2(a, a);
   }
+  int hi = t;
+  int lo = hi > kRecChunk ? hi - kRecChunk : 0;
+  float2 kr[kRecChunk], ur[kRecChunk], gr[kRecChunk];
+  float gs[kRecChunk];
+  auto load_chunk = [&](int lo_, int cnt_) {
+#pragma unroll
+    for (int j = 0; j < kRecChunk; ++j) {
+      if (j < cnt_) {
+        const size_t rr = (rec0 + lo_ + j) * D + 2 * lane;
+        kr[j] = ld2(A.buf_k + rr);
+        ur[j] = ld2(A.buf_u + rr);
+        if (KDA) gr[j] = ld2(A.buf_gate + rr);
+        else gs[j] = A.buf_gate[rec0 + lo_ + j];
+      }
+    }
+  };
+  load_chunk(lo, hi - lo);
+  int cidx[kCompEarly];
+  float2 cw[kCompEarly];
+#pragma unroll
+  for (int c = 0; c < kCompEarly; ++c) {
+    if (c < r) {
+      cidx[c] = A.comp_idx[(size_t)s * r + c];
+      cw[c] = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
+    }
+  }
+  // ---- issue: the 16 KiB of int8 codes of this state
+  const int cc = lane & 7, rg = lane >> 3;
+  const uint4 *csrc =
+      reinterpret_cast<const uint4 *>(A.codes + (size_t)s * D * D) + rg * 8 + cc;
+  uint4 cv[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) cv[m] = ldu4(csrc + m * 64);
+
+  // ---- a1 token prep
   const float2 kt = make_float2(bt * kk.x, bt * kk.y);
   const float2 yb = make_float2(al.x * kk.x, al.y * kk.y);
   const float2 yq = make_float2(al.x * qq.x, al.y * qq.y);
   const float kq = wave_sum(kt.x * qq.x + kt.y * qq.y);
 
-  // ---- a2 history: suffix decay products and record dot products,
-  // records visited from the newest (i = t-1) to the oldest.
-  const size_t rec0 = (size_t)s * p;
-  float Pg = 1.f;                   // GDN: rho_i (uniform)
-  float2 Pk = make_float2(1.f, 1.f);  // KDA: rho_i for rows 2l, 2l+1
-  for (int hi = t - 1; hi >= 0; hi -= 16) {
-    const int cnt = hi + 1 < 16 ? hi + 1 : 16;
-    for (int j = 0; j < cnt; ++j) {
-      const int i = hi - j;
-      const float2 ki = ld2(A.buf_k + (rec0 + i) * D + 2 * lane);
-      float hb, hq;
-      if (KDA) {
-        const float2 kr = make_float2(ki.x * Pk.x, ki.y * Pk.y);
-        hb = kr.x * yb.x + kr.y * yb.y;
-        hq = kr.x * yq.x + kr.y * yq.y;
-        const float2 g = ld2(A.buf_gate + (rec0 + i) * D + 2 * lane);
-        Pk.x *= g.x;
-        Pk.y *= g.y;
-      } else {
-        hb = (ki.x * yb.x + ki.y * yb.y) * Pg;
-        hq = (ki.x * yq.x + ki.y * yq.y) * Pg;
-        Pg *= A.buf_gate[rec0 + i];
+  // ---- a2 history, newest records first: suffix decays rho_i, record dots
+  // h_i = k~_i . (rho_i * y) for both vectors, and sum_i u_i h_i
+  float Pg = 1.f;                     // GDN: rho (uniform)
+  float2 Pk = make_float2(1.f, 1.f);  // KDA: rho for rows 2l, 2l+1
+  float2 zub = make_float2(0.f, 0.f), zuq = make_float2(0.f, 0.f);
+  while (hi > 0) {
+    const int cnt = hi - lo;
+#pragma unroll
+    for (int j = kRecChunk - 1; j >= 0; --j) {
+      if (j < cnt) {
+        float hb, hq;
+        if (KDA) {
+          const float2 kw = make_float2(kr[j].x * Pk.x, kr[j].y * Pk.y);
+          hb = kw.x * yb.x + kw.y * yb.y;
+          hq = kw.x * yq.x + kw.y * yq.y;
+          Pk.x *= gr[j].x;
+          Pk.y *= gr[j].y;
+        } else {
+          hb = (kr[j].x * yb.x + kr[j].y * yb.y) * Pg;
+          hq = (kr[j].x * yq.x + kr[j].y * yq.y) * Pg;
+          Pg *= gs[j];
+        }
+        sh_red[lane * kRedStride + 2 * j] = hb;
+        sh_red[lane * kRedStride + 2 * j + 1] = hq;
       }
-      sh_red[lane * kRedStride + 2 * j] = hb;
-      sh_red[lane * kRedStride + 2 * j + 1] = hq;
     }
     __syncthreads();
     // transpose-reduce: value v = lane & 31 summed over one half of the lanes
-    const int v = lane & 31, half = lane >> 5;
-    float acc = 0.f;
-    if (v < 2 * cnt) {
+    {
+      const int v = lane & 31, half = lane >> 5;
+      float acc = 0.f;
+      if (v < 2 * cnt) {
 #pragma unroll 8
-      for (int m = 0; m < 32; ++m) {
-        const int src = 32 * half + ((m + 16 * half) & 31);
-        acc += sh_red[src * kRedStride + v];
+        for (int m = 0; m < 32; ++m) acc += sh_red[(32 * half + m) * kRedStride + v];
       }
-    }
-    acc += __shfl_xor(acc, 32);
-    if (lane < 2 * cnt) {
-      const int i = hi - (lane >> 1);
-      reinterpret_cast<float *>(&sh_h[i])[lane & 1] = acc;
+      acc += __shfl_xor(acc, 32);
+      if (lane < 2 * cnt) reinterpret_cast<float *>(&sh_h[lane >> 1])[lane & 1] = acc;
     }
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRecChunk; ++j) {
+      if (j < cnt) {
+        const float2 h = sh_h[j];
+        zub.x = fmaf(ur[j].x, h.x, zub.x); zub.y = fmaf(ur[j].y, h.x, zub.y);
+        zuq.x = fmaf(ur[j].x, h.y, zuq.x); zuq.y = fmaf(ur[j].y, h.y, zuq.y);
+      }
+    }
+    hi = lo;
+    lo = hi > kRecChunk ? hi - kRecChunk : 0;
+    if (hi > 0) {
+      __syncthreads();
+      load_chunk(lo, hi - lo);
+    }
   }
 
   // ---- GEMV weights: a_i * Gamma_i * y_i
@@ -217,7 +289,15 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     zb.x *= sc.x; zb.y *= sc.y;
     zq.x *= sc.x; zq.y *= sc.y;
   }
-  for (int c = 0; c < r; ++c) {
+#pragma unroll
+  for (int c = 0; c < kCompEarly; ++c) {
+    if (c < r && (unsigned)cidx[c] < (unsigned)D) {
+      const float2 g = sh_gy[cidx[c]];
+      zb.x = fmaf(cw[c].x, g.x, zb.x); zb.y = fmaf(cw[c].y, g.x, zb.y);
+      zq.x = fmaf(cw[c].x, g.y, zq.x); zq.y = fmaf(cw[c].y, g.y, zq.y);
+    }
+  }
+  for (int c = kCompEarly; c < r; ++c) {
     const int idx = A.comp_idx[(size_t)s * r + c];
     if ((unsigned)idx < (unsigned)D) {
       const float2 g = sh_gy[idx];
@@ -226,12 +306,8 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
       zq.x = fmaf(w.x, g.y, zq.x); zq.y = fmaf(w.y, g.y, zq.y);
     }
   }
-  for (int i = 0; i < t; ++i) {
-    const float2 u = ld2(A.buf_u + (rec0 + i) * D + 2 * lane);
-    const float2 h = sh_h[i];
-    zb.x = fmaf(u.x, h.x, zb.x); zb.y = fmaf(u.y, h.x, zb.y);
-    zq.x = fmaf(u.x, h.y, zq.x); zq.y = fmaf(u.y, h.y, zq.y);
-  }
+  zb.x += zub.x; zb.y += zub.y;
+  zq.x += zuq.x; zq.y += zuq.y;
   const float2 ut = make_float2(vv.x - zb.x, vv.y - zb.y);
   const float2 ot = make_float2(fmaf(kq, ut.x, zq.x), fmaf(kq, ut.y, zq.y));
   st2(A.o + vo, ot);
@@ -252,13 +328,15 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 // columns 8c'+ct, so lane l holds 8 rows (32w + 16rt + 4(l>>4) + v) x 8
 // contiguous columns (8(l&15) .. +7): codes are read and written as 8-byte
 // row segments, 16 lanes covering one 128-byte row.
-//   S_len = Gamma * (deQ + comps)  (accumulator init)
-//         + K_w U                  (v_mfma_f32_16x16x4_f32, K = records)
-// with K_w[i][row] = rho_i[row] k~_i[row].
+//   acc  = K_w U          (v_mfma_f32_16x16x4_f32, K = records, newest
+//                          chunk first so the decays are running products)
+//   acc += Gamma * (deQ + comps)
+// with K_w[i][row] = rho_i[row] k~_i[row].  Each record chunk is staged in
+// LDS with coalesced 128-bit loads issued by all 256 threads at once.
 // Then: row L2 norms (DPP row reductions), top-r rank selection, extraction,
 // column absmax (smoothing scale), per-row absmax and int8 codes.
 // ---------------------------------------------------------------------------
-constexpr int kChunk = 32;  // records staged in LDS per MFMA pass
+constexpr int kChunk = 16;  // records staged in LDS per MFMA pass
 
 template <bool KDA, bool FROM_FP32>
 __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
@@ -270,10 +348,11 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 
   __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
   __shared__ __attribute__((aligned(16))) float sh_U[kChunk * D];
+  __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : 64];
   __shared__ float sh_G[D];
   __shared__ float sh_a[D];
   __shared__ __attribute__((aligned(16))) float sh_s[D];
-  __shared__ float sh_norm[D];
+  __shared__ __attribute__((aligned(16))) float sh_norm[D];
   __shared__ int sh_sel[D];
   __shared__ int sh_oidx[16];
   __shared__ float sh_cm[4 * D];
@@ -286,77 +365,83 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 32 * w + 16 * rt + 4 * lr + v;
-        const float4 *src =
-            reinterpret_cast<const float4 *>(A.S_in + ((size_t)s * D + row) * D + 8 * lc);
-        const float4 x0 = src[0], x1 = src[1];
+        const float *src = A.S_in + ((size_t)s * D + row) * D + 8 * lc;
+        const float4 x0 = ld4(src), x1 = ld4(src + 4);
         acc[rt][0][v] = x0.x; acc[rt][1][v] = x0.y; acc[rt][2][v] = x0.z; acc[rt][3][v] = x0.w;
         acc[rt][4][v] = x1.x; acc[rt][5][v] = x1.y; acc[rt][6][v] = x1.z; acc[rt][7][v] = x1.w;
       }
   } else {
     const int len = A.len, p = A.p;
     const size_t rec0 = (size_t)s * p;
+    // boundary-state side data and this lane's code segments, issued first
     if (tid < D) {
       sh_a[tid] = A.row_scale[(size_t)s * D + tid];
       sh_s[tid] = A.col_scale[(size_t)s * D + tid];
-      // Gamma for row tid: product of all len decays
-      float P = 1.f;
-      for (int i = len - 1; i >= 0; --i)
-        P *= KDA ? A.buf_gate[(rec0 + i) * D + tid] : A.buf_gate[rec0 + i];
-      sh_G[tid] = P;
     }
     if (tid < r) sh_oidx[tid] = A.comp_idx[(size_t)s * r + tid];
-    __syncthreads();
-
-    // accumulator init: Gamma * (c a s + compensator rows)
-    float sv[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sv[ct] = sh_s[8 * lc + ct];
+    uint2 cw[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 32 * w + 16 * rt + 4 * lr + v;
-        const uint2 cw =
-            *reinterpret_cast<const uint2 *>(A.codes + ((size_t)s * D + row) * D + 8 * lc);
-        const float a = sh_a[row], G = sh_G[row];
-        float x[8];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          x[b] = (float)(int8_t)(cw.x >> (8 * b)) * a * sv[b];
-          x[4 + b] = (float)(int8_t)(cw.y >> (8 * b)) * a * sv[4 + b];
-        }
-        for (int c = 0; c < r; ++c) {
-          if (sh_oidx[c] == row) {
-            const float4 *wp = reinterpret_cast<const float4 *>(
-                A.comp_val + ((size_t)s * r + c) * D + 8 * lc);
-            const float4 w0 = wp[0], w1 = wp[1];
-            x[0] += w0.x; x[1] += w0.y; x[2] += w0.z; x[3] += w0.w;
-            x[4] += w1.x; x[5] += w1.y; x[6] += w1.z; x[7] += w1.w;
-          }
-        }
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[rt][ct][v] = x[ct] * G;
+        cw[rt][v] = ldu2(A.codes + ((size_t)s * D + row) * D + 8 * lc);
       }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // K_w U over the buffered records, kChunk records per LDS pass
-    for (int c0 = 0; c0 < len; c0 += kChunk) {
-      const int cnt = len - c0 < kChunk ? len - c0 : kChunk;
-      const int cnt4 = (cnt + 3) & ~3;
+    // K_w U over the records, newest chunk first
+    float P = 1.f;  // running decay product for row tid (tid < D)
+    for (int hi = len; hi > 0; hi -= kChunk) {
+      const int lo = hi > kChunk ? hi - kChunk : 0;
+      const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
       __syncthreads();
       {
-        const float4 *su = reinterpret_cast<const float4 *>(A.buf_u + (rec0 + c0) * D);
+        // kChunk * D / 4 = 512 float4 per array: two per thread, all loads
+        // of the chunk issued before the first LDS write
+        static_assert(kChunk * D / 4 == 512, "staging assumes two float4 per thread");
+        const float4 *su = reinterpret_cast<const float4 *>(A.buf_u + (rec0 + lo) * D);
+        const float4 *sk = reinterpret_cast<const float4 *>(A.buf_k + (rec0 + lo) * D);
+        const float4 *sg = reinterpret_cast<const float4 *>(A.buf_gate + (rec0 + lo) * D);
         float4 *du = reinterpret_cast<float4 *>(sh_U);
-        for (int e = tid; e < cnt4 * (D / 4); e += 256)
-          du[e] = e < cnt * (D / 4) ? su[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      if (tid < D) {
-        // rho_i for row tid, i from the newest record down
-        float P = 1.f;
-        for (int i = len - 1; i >= c0; --i) {
-          if (i < c0 + cnt) sh_K[(i - c0) * D + tid] = P * A.buf_k[(rec0 + i) * D + tid];
-          P *= KDA ? A.buf_gate[(rec0 + i) * D + tid] : A.buf_gate[rec0 + i];
+        float4 *dk = reinterpret_cast<float4 *>(sh_K);
+        float4 *dg = reinterpret_cast<float4 *>(sh_g);
+        const int nvec = cnt * (D / 4), npad = cnt4 * (D / 4);
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int e0 = tid, e1 = tid + 256;
+        float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
+        if (e0 < nvec) {
+          u0 = ld4(reinterpret_cast<const float *>(su + e0));
+          k0 = ld4(reinterpret_cast<const float *>(sk + e0));
+          if (KDA) g0 = ld4(reinterpret_cast<const float *>(sg + e0));
         }
-        for (int i = cnt; i < cnt4; ++i) sh_K[i * D + tid] = 0.f;
+        if (e1 < nvec) {
+          u1 = ld4(reinterpret_cast<const float *>(su + e1));
+          k1 = ld4(reinterpret_cast<const float *>(sk + e1));
+          if (KDA) g1 = ld4(reinterpret_cast<const float *>(sg + e1));
+        }
+        float gsc = 1.f;
+        if (!KDA && tid < cnt) gsc = A.buf_gate[rec0 + lo + tid];
+        if (e0 < npad) {
+          du[e0] = u0;
+          dk[e0] = k0;
+          if (KDA && e0 < nvec) dg[e0] = g0;
+        }
+        if (e1 < npad) {
+          du[e1] = u1;
+          dk[e1] = k1;
+          if (KDA && e1 < nvec) dg[e1] = g1;
+        }
+        if (!KDA && tid < cnt) sh_g[tid] = gsc;
+      }
+      __syncthreads();
+      if (tid < D) {
+        for (int j = cnt - 1; j >= 0; --j) {
+          sh_K[j * D + tid] *= P;
+          P *= KDA ? sh_g[j * D + tid] : sh_g[j];
+        }
       }
       __syncthreads();
       for (int ks = 0; ks < cnt4 / 4; ++ks) {
@@ -373,9 +458,43 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
         }
       }
     }
+    // a_i * Gamma_i per row (the deQ row factor) and Gamma_i itself
+    if (tid < D) {
+      sh_G[tid] = P;
+      sh_a[tid] *= P;
+    }
+    __syncthreads();
+
+    // acc += (c * (a Gamma)) * s  +  Gamma * (compensator rows)
+    float sv[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) sv[ct] = sh_s[8 * lc + ct];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 32 * w + 16 * rt + 4 * lr + v;
+        const float aG = sh_a[row];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[rt][b][v] = fmaf((float)(int8_t)(cw[rt][v].x >> (8 * b)) * aG, sv[b], acc[rt][b][v]);
+          acc[rt][4 + b][v] = fmaf((float)(int8_t)(cw[rt][v].y >> (8 * b)) * aG, sv[4 + b], acc[rt][4 + b][v]);
+        }
+        for (int c = 0; c < r; ++c) {
+          if (sh_oidx[c] == row) {
+            const float G = sh_G[row];
+            const float *wp = A.comp_val + ((size_t)s * r + c) * D + 8 * lc;
+            const float4 w0 = ld4(wp), w1 = ld4(wp + 4);
+            acc[rt][0][v] = fmaf(G, w0.x, acc[rt][0][v]); acc[rt][1][v] = fmaf(G, w0.y, acc[rt][1][v]);
+            acc[rt][2][v] = fmaf(G, w0.z, acc[rt][2][v]); acc[rt][3][v] = fmaf(G, w0.w, acc[rt][3][v]);
+            acc[rt][4][v] = fmaf(G, w1.x, acc[rt][4][v]); acc[rt][5][v] = fmaf(G, w1.y, acc[rt][5][v]);
+            acc[rt][6][v] = fmaf(G, w1.z, acc[rt][6][v]); acc[rt][7][v] = fmaf(G, w1.w, acc[rt][7][v]);
+          }
+        }
+      }
   }
 
-  // ---- a6 row L2 norms and top-r selection
+  // ---- a6 row L2 norms (squared, fp32) and top-r selection
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -386,17 +505,40 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       q = row16_sum(q);
       if (lc == 0) sh_norm[32 * w + 16 * rt + 4 * lr + v] = q;
     }
+  if (tid < D) sh_sel[tid] = -1;
   __syncthreads();
-  if (tid < D) {
-    const float ni = sh_norm[tid];
-    int rank = 0;
-    for (int j = 0; j < D; ++j) {
-      const float nj = sh_norm[j];
-      rank += (nj > ni) || (nj == ni && j < tid);
+  if (w == 0 && r > 0) {
+    // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
+    // takes the largest remaining norm, ties to the lower row index
+    float n0 = sh_norm[2 * lane], n1 = sh_norm[2 * lane + 1];
+    for (int c = 0; c < r; ++c) {
+      const bool pick1 = n1 > n0;  // equal norms keep the lower row
+      const float best = pick1 ? n1 : n0;
+      const float m = row16_max(best);
+      const float mx = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+                             fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+      const unsigned long long hit = __ballot(best == mx && best >= 0.f);
+      int wl, odd;
+      if (hit) {
+        wl = __ffsll((long long)hit) - 1;
+        odd = __builtin_amdgcn_readlane((int)pick1, wl);
+      } else {
+        // only reachable with NaN norms: take the lowest row not yet picked
+        const unsigned long long f0 = __ballot(n0 != -1.f), f1 = __ballot(n1 != -1.f);
+        wl = __ffsll((long long)(f0 | f1)) - 1;
+        odd = ((f0 >> wl) & 1ull) ? 0 : 1;
+      }
+      const int wrow = 2 * wl + odd;
+      if (lane == wl) {
+        if (odd) n1 = -1.f; else n0 = -1.f;
+      }
+      if (lane == 0) {
+        sh_sel[wrow] = c;
+        A.comp_idx[(size_t)s * r + c] = wrow;
+      }
     }
-    const int sel = rank < r ? rank : -1;
-    sh_sel[tid] = sel;
-    if (sel >= 0) A.comp_idx[(size_t)s * r + sel] = tid;
   }
   __syncthreads();
 
@@ -411,9 +553,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       const int row = 32 * w + 16 * rt + 4 * lr + v;
       const int sel = sh_sel[row];
       if (sel >= 0) {
-        float4 *wp = reinterpret_cast<float4 *>(A.comp_val + ((size_t)s * r + sel) * D + 8 * lc);
-        wp[0] = make_float4(acc[rt][0][v], acc[rt][1][v], acc[rt][2][v], acc[rt][3][v]);
-        wp[1] = make_float4(acc[rt][4][v], acc[rt][5][v], acc[rt][6][v], acc[rt][7][v]);
+        float *wp = A.comp_val + ((size_t)s * r + sel) * D + 8 * lc;
+        st4(wp, make_float4(acc[rt][0][v], acc[rt][1][v], acc[rt][2][v], acc[rt][3][v]));
+        st4(wp + 4, make_float4(acc[rt][4][v], acc[rt][5][v], acc[rt][6][v], acc[rt][7][v]));
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) acc[rt][ct][v] = 0.f;
       }
@@ -438,39 +580,65 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   }
   __syncthreads();
 
-  // ---- a8 per-row absmax and int8 codes
-  float sig[8];
+  // ---- a8 smoothed residual q = R * sigma (in place), per-row absmax
+  {
+    float sig[8];
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) sig[ct] = sh_s[8 * lc + ct];
+    for (int ct = 0; ct < 8; ++ct) sig[ct] = sh_s[8 * lc + ct];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          acc[rt][ct][v] = acc[rt][ct][v] * sig[ct];
+          m = fmaxf(m, fabsf(acc[rt][ct][v]));
+        }
+        m = row16_max(m);
+        if (lc == 0) sh_norm[32 * w + 16 * rt + 4 * lr + v] = m;
+      }
+  }
+  __syncthreads();
+  if (tid < D) {
+    // row scale and its reciprocal, once per row (correctly rounded)
+    const float m = sh_norm[tid];
+    float a = 0.f, inv = 0.f;
+    if (m > 0.f) {
+      a = m / 127.f;
+      inv = 127.f / m;
+    }
+    A.row_scale[(size_t)s * D + tid] = a;
+    sh_G[tid] = inv;
+  }
+  __syncthreads();
+  // codes: rne(q * inv).  Adding 1.5 * 2^23 rounds to the nearest integer,
+  // ties to even, and leaves that integer's two's-complement low byte in the
+  // low byte of the sum's bit pattern (|q * inv| <= 127 by construction).
+  // The product is rounded on its own: no contraction into an FMA.
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
+#pragma clang fp contract(off)
       const int row = 32 * w + 16 * rt + 4 * lr + v;
-      float qv[8];
-      float m = 0.f;
+      const float inv = sh_G[row];
+      uint32_t by[8];
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        qv[ct] = acc[rt][ct][v] * sig[ct];
-        m = fmaxf(m, fabsf(qv[ct]));
+        const float x = acc[rt][ct][v] * inv;
+        by[ct] = __float_as_uint(x + 12582912.0f);
       }
-      m = row16_max(m);
-      float a = 0.f, inv = 0.f;
-      if (m > 0.f) {
-        a = m / 127.f;
-        inv = 127.f / m;
-      }
-      uint32_t pk[2] = {0u, 0u};
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        float x = rintf(qv[ct] * inv);
-        x = fminf(fmaxf(x, -127.f), 127.f);
-        const uint32_t byte = (uint32_t)((int)x) & 0xFFu;
-        pk[ct >> 2] |= byte << (8 * (ct & 3));
-      }
-      *reinterpret_cast<uint2 *>(A.codes + ((size_t)s * D + row) * D + 8 * lc) =
-          make_uint2(pk[0], pk[1]);
-      if (lc == 0) A.row_scale[(size_t)s * D + row] = a;
+      // gather the low bytes: v_perm_b32 selector 0x0c0c0400 takes byte 0 of
+      // each source into bytes 0..1; the second perm merges two halves
+      const uint32_t lo01 = __builtin_amdgcn_perm(by[1], by[0], 0x0c0c0400u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(by[3], by[2], 0x0c0c0400u);
+      const uint32_t lo45 = __builtin_amdgcn_perm(by[5], by[4], 0x0c0c0400u);
+      const uint32_t lo67 = __builtin_amdgcn_perm(by[7], by[6], 0x0c0c0400u);
+      const uint32_t w0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      const uint32_t w1 = __builtin_amdgcn_perm(lo67, lo45, 0x05040100u);
+      __builtin_nontemporal_store(vu2{w0, w1},
+                                  reinterpret_cast<vu2 *>(A.codes + ((size_t)s * D + row) * D + 8 * lc));
     }
 }
 
