@@ -15,6 +15,9 @@ def hipcc_command(out=LIB_PATH, extra=()):
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU ops stay off: only scalar fp32 ops are emitted
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the close kernel post-processes them
+            # on the VALU, and AGPR copies would double its register footprint
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG_DIR, "csrc"),
             *extra, "-o", out, *SOURCES]
 

@@ -102,10 +102,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 // pass over the codes.
 //
 // Memory-level parallelism: every load a phase needs is issued before the
-// phase waits on any of them.  The buffered records are read in chunks of
-// kRecChunk (all k~, u and gate loads of a chunk in flight together), the
-// first compensator rows and the whole code stream are issued before the
-// first wait, so a wave pays about one memory latency per chunk.
+// phase waits on any of them.  The token inputs, the newest kRecChunk
+// records' k~ and gates, the first compensator rows and the whole code
+// stream are in flight before the first wait; the records' u rows are
+// issued after the record dots and arrive during the GEMV.  Record t's k~
+// and gate depend only on the inputs and are stored as soon as they are
+// known: stores left to the end of a wave hold it (and its registers) until
+// they drain, which measurably lowers the streaming rate.
 // ---------------------------------------------------------------------------
 constexpr int kRecChunk = 16;    // records in flight per chunk
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 
   __shared__ float2 sh_w[D];   // a_i * Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_gy[D];  // Gamma_i * (y_b, y_q)_i
-  __shared__ float2 sh_h[kRecChunk];  // record weights (h_b, h_q) of a chunk
+  __shared__ float2 sh_h[64];  // record weights (h_b, h_q)
   __shared__ __attribute__((aligned(16))) float sh_red[64 * kRedStride];
 
   const size_t vo = (size_t)s * D + 2 * lane;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   }
   int hi = t;
   int lo = hi > kRecChunk ? hi - kRecChunk : 0;
-  float2 kr[kRecChunk], ur[kRecChunk], gr[kRecChunk];
+  float2 kr[kRecChunk], gr[kRecChunk];
   float gs[kRecChunk];
   auto load_chunk = [&](int lo_, int cnt_) {
 #pragma unroll
@@ -148,7 +151,6 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
       if (j < cnt_) {
         const size_t rr = (rec0 + lo_ + j) * D + 2 * lane;
         kr[j] = ld2(A.buf_k + rr);
-        ur[j] = ld2(A.buf_u + rr);
         if (KDA) gr[j] = ld2(A.buf_gate + rr);
         else gs[j] = A.buf_gate[rec0 + lo_ + j];
       }
@@ -172,17 +174,22 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 #pragma unroll
   for (int m = 0; m < 16; ++m) cv[m] = ldu4(csrc + m * 64);
 
-  // ---- a1 token prep
+  // ---- a1 token prep; append k~_t and the gate of record t
   const float2 kt = make_float2(bt * kk.x, bt * kk.y);
   const float2 yb = make_float2(al.x * kk.x, al.y * kk.y);
   const float2 yq = make_float2(al.x * qq.x, al.y * qq.y);
+  st2(A.buf_k + (rec0 + t) * D + 2 * lane, kt);
+  if (KDA) {
+    st2(A.buf_gate + (rec0 + t) * D + 2 * lane, al);
+  } else if (lane == 0) {
+    A.buf_gate[rec0 + t] = al.x;
+  }
   const float kq = wave_sum(kt.x * qq.x + kt.y * qq.y);
 
-  // ---- a2 history, newest records first: suffix decays rho_i, record dots
-  // h_i = k~_i . (rho_i * y) for both vectors, and sum_i u_i h_i
+  // ---- a2 history, newest records first: suffix decays rho_i and record
+  // dots h_i = k~_i . (rho_i * y) for both vectors
   float Pg = 1.f;                     // GDN: rho (uniform)
   float2 Pk = make_float2(1.f, 1.f);  // KDA: rho for rows 2l, 2l+1
-  float2 zub = make_float2(0.f, 0.f), zuq = make_float2(0.f, 0.f);
   while (hi > 0) {
     const int cnt = hi - lo;
 #pragma unroll
@@ -214,24 +221,19 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         for (int m = 0; m < 32; ++m) acc += sh_red[(32 * half + m) * kRedStride + v];
       }
       acc += __shfl_xor(acc, 32);
-      if (lane < 2 * cnt) reinterpret_cast<float *>(&sh_h[lane >> 1])[lane & 1] = acc;
+      if (lane < 2 * cnt) reinterpret_cast<float *>(&sh_h[lo + (lane >> 1)])[lane & 1] = acc;
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kRecChunk; ++j) {
-      if (j < cnt) {
-        const float2 h = sh_h[j];
-        zub.x = fmaf(ur[j].x, h.x, zub.x); zub.y = fmaf(ur[j].y, h.x, zub.y);
-        zuq.x = fmaf(ur[j].x, h.y, zuq.x); zuq.y = fmaf(ur[j].y, h.y, zuq.y);
-      }
-    }
     hi = lo;
     lo = hi > kRecChunk ? hi - kRecChunk : 0;
-    if (hi > 0) {
-      __syncthreads();
-      load_chunk(lo, hi - lo);
-    }
+    if (hi > 0) load_chunk(lo, hi - lo);
   }
+  // U of the newest chunk, in flight during the GEMV
+  const int ulo = t > kRecChunk ? t - kRecChunk : 0;
+  float2 ur[kRecChunk];
+#pragma unroll
+  for (int j = 0; j < kRecChunk; ++j)
+    if (j < t - ulo) ur[j] = ld2(A.buf_u + (rec0 + ulo + j) * D + 2 * lane);
 
   // ---- GEMV weights: a_i * Gamma_i * y_i
   {
@@ -284,6 +286,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   }
 
   // ---- a4 combine: column scales, compensator rows, buffered records
+  // (sum_i u_i h_i: the newest chunk from registers, older ones streamed)
   {
     const float2 sc = ld2(A.col_scale + vo);
     zb.x *= sc.x; zb.y *= sc.y;
@@ -306,18 +309,29 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
       zq.x = fmaf(w.x, g.y, zq.x); zq.y = fmaf(w.y, g.y, zq.y);
     }
   }
-  zb.x += zub.x; zb.y += zub.y;
-  zq.x += zuq.x; zq.y += zuq.y;
+  {
+    float2 zub = make_float2(0.f, 0.f), zuq = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kRecChunk; ++j) {
+      if (j < t - ulo) {
+        const float2 h = sh_h[ulo + j];
+        zub.x = fmaf(ur[j].x, h.x, zub.x); zub.y = fmaf(ur[j].y, h.x, zub.y);
+        zuq.x = fmaf(ur[j].x, h.y, zuq.x); zuq.y = fmaf(ur[j].y, h.y, zuq.y);
+      }
+    }
+    for (int i = 0; i < ulo; ++i) {
+      const float2 u = ld2(A.buf_u + (rec0 + i) * D + 2 * lane);
+      const float2 h = sh_h[i];
+      zub.x = fmaf(u.x, h.x, zub.x); zub.y = fmaf(u.y, h.x, zub.y);
+      zuq.x = fmaf(u.x, h.y, zuq.x); zuq.y = fmaf(u.y, h.y, zuq.y);
+    }
+    zb.x += zub.x; zb.y += zub.y;
+    zq.x += zuq.x; zq.y += zuq.y;
+  }
   const float2 ut = make_float2(vv.x - zb.x, vv.y - zb.y);
   const float2 ot = make_float2(fmaf(kq, ut.x, zq.x), fmaf(kq, ut.y, zq.y));
   st2(A.o + vo, ot);
   st2(A.buf_u + (rec0 + t) * D + 2 * lane, ut);
-  st2(A.buf_k + (rec0 + t) * D + 2 * lane, kt);
-  if (KDA) {
-    st2(A.buf_gate + (rec0 + t) * D + 2 * lane, al);
-  } else if (lane == 0) {
-    A.buf_gate[rec0 + t] = al.x;
-  }
 }
 
 // ---------------------------------------------------------------------------
