@@ -51,6 +51,25 @@ def bytes_per_head_token(p, dk, dv, r, kda):
     return dec + close_bytes(p, dk, dv, r, kda) / p
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gdn_b256_4layers.txt")
+KERNEL_SRC = os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", "lq_kernels.hip")
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch (decode, close) from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or (None, None) when the counters were
+    taken on another workload or on kernel source that has changed since."""
+    import hashlib
+    if cfg.cid != 2 or not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    doc = json.load(open(TRAFFIC_FILE))
+    if doc.get("source_sha256") != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
+        return None, None
+    k = doc["kernels"]
+    return (k["decode_step_kernel<GDN>"]["traffic_bytes_per_launch"],
+            k["close_kernel<GDN, window close>"]["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +203,7 @@ def main():
     close_avg_ms = close_ms / (args.steps * windows * L)
     close_gbs = nl * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda) / (close_avg_ms * 1e-3) / 1e9
     whole_gbs = value * bpht / 1e9
+    dec_traffic, close_traffic = measured_traffic(cfg)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
@@ -196,9 +216,11 @@ def main():
                    "launch": args.mode},
         "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": round(dec_bytes),
+                     "traffic": dec_traffic, "bytes_per_launch": round(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
-        "window_close": {"avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1)},
+        "window_close": {"avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
+                         "bytes_per_launch": nl * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda),
+                         "traffic": close_traffic},
         "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
                        "bytes_per_head_token": round(bpht, 1)},
         "hbm_copy_GBs": round(copy_gbs, 1),

@@ -112,7 +112,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // ---------------------------------------------------------------------------
 constexpr int kRecChunk = 16;    // records in flight per chunk
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
-constexpr int kRedStride = 36;   // padded row of the transposed partials (16B aligned)
+constexpr int kRedStride = 33;   // odd row stride of the transposed partials: no bank conflicts
 constexpr int kGemvStride = 260; // padded row of the GEMV partials (16B aligned)
 
 template <bool KDA>
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   __shared__ __attribute__((aligned(16))) float sh_norm[D];
   __shared__ int sh_sel[D];
   __shared__ int sh_oidx[16];
-  __shared__ float sh_cm[4 * D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
 
   floatx4 acc[2][8];
 
@@ -556,7 +556,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   }
   __syncthreads();
 
-  // ---- extraction and a7 column absmax of the residual
+  // ---- extraction and a7 column absmax of the residual.  Extracted rows
+  // are not zeroed in registers: they are left out of the column maxima
+  // here and get row scale 0 (hence codes 0) below.
   float cm[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) cm[ct] = 0.f;
@@ -570,24 +572,23 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
         float *wp = A.comp_val + ((size_t)s * r + sel) * D + 8 * lc;
         st4(wp, make_float4(acc[rt][0][v], acc[rt][1][v], acc[rt][2][v], acc[rt][3][v]));
         st4(wp + 4, make_float4(acc[rt][4][v], acc[rt][5][v], acc[rt][6][v], acc[rt][7][v]));
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[rt][ct][v] = 0.f;
       }
+      const float keep = sel < 0 ? 1.f : 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) cm[ct] = fmaxf(cm[ct], fabsf(acc[rt][ct][v]));
+      for (int ct = 0; ct < 8; ++ct) cm[ct] = fmaxf(cm[ct], fabsf(acc[rt][ct][v]) * keep);
     }
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    cm[ct] = fmaxf(cm[ct], __shfl_xor(cm[ct], 16));
-    cm[ct] = fmaxf(cm[ct], __shfl_xor(cm[ct], 32));
-  }
-  if (lr == 0) {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sh_cm[w * D + 8 * lc + ct] = cm[ct];
+  // per-lane partial maxima (8 columns over 8 rows) to LDS; 16 partials per
+  // column (4 waves x 4 row groups)
+  {
+    float4 *dst = reinterpret_cast<float4 *>(sh_cmx + (4 * w + lr) * D + 8 * lc);
+    dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+    dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
   }
   __syncthreads();
   if (tid < D) {
-    const float m = fmaxf(fmaxf(sh_cm[tid], sh_cm[D + tid]), fmaxf(sh_cm[2 * D + tid], sh_cm[3 * D + tid]));
+    float m = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) m = fmaxf(m, sh_cmx[g * D + tid]);
     const float sc = (A.flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
     A.col_scale[(size_t)s * D + tid] = sc;
     sh_s[tid] = 1.f / sc;  // sigma_j, correctly rounded
@@ -618,7 +619,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
     // row scale and its reciprocal, once per row (correctly rounded)
     const float m = sh_norm[tid];
     float a = 0.f, inv = 0.f;
-    if (m > 0.f) {
+    if (m > 0.f && sh_sel[tid] < 0) {
       a = m / 127.f;
       inv = 127.f / m;
     }
