@@ -2,10 +2,11 @@
 """Decode throughput of the LeapQuant per-window int8 state path on one MI355X.
 
 Workload (default): Gated DeltaNet decode at batch 256 x 32 heads with four
-stacked layers' states resident (4 slabs of 8,192 states, dk = dv = 128),
-window p = 16, r = 4 compensator rows, 1,024 tokens.  One step is the whole
-decode of that batch: quantize the initial states, then 64 windows of
-(16 tokens x 4 layer launches + 4 window closes).  Inputs are synthetic
+stacked layers' states resident (32,768 states, 8,192 per layer, dk = dv =
+128), window p = 16, r = 4 compensator rows, 1,024 tokens.  One step is the
+whole decode of that batch: quantize the initial states, then 64 windows of
+(16 tokens x 4 per-layer decode launches + one window close over all four
+layers' states).  Inputs are synthetic
 (seeded generators) and resident in HBM before timing starts.
 
 Prints one JSON line (see the fields below).  --gpus > 1 is refused: this
@@ -56,7 +57,7 @@ KERNEL_SRC = os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", "lq_kernels
 
 
 def measured_traffic(cfg):
-    """HBM bytes per launch (decode, close) from the committed rocprofv3
+    """HBM bytes per state (decode, close) from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE summary, or (None, None) when the counters were
     taken on another workload or on kernel source that has changed since."""
     import hashlib
@@ -66,8 +67,8 @@ def measured_traffic(cfg):
     if doc.get("source_sha256") != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
         return None, None
     k = doc["kernels"]
-    return (k["decode_step_kernel<GDN>"]["traffic_bytes_per_launch"],
-            k["close_kernel<GDN, window close>"]["traffic_bytes_per_launch"])
+    return (k["decode_step_kernel<GDN>"]["traffic_bytes_per_state"],
+            k["close_kernel<GDN, window close>"]["traffic_bytes_per_state"])
 
 
 def parse():
@@ -116,16 +117,17 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] generated {n} states x {T} tokens in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
-    slabs = [lq.LeapQuantState(nl, cfg.p, cfg.r, cfg.gate, dev) for _ in range(L)]
+    # the layers' states live in one slab: decoded layer by layer through
+    # views, quantized and window-closed together in one launch each
+    slab = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, dev)
+    slabs = [slab.view(l * nl, nl) for l in range(L)]
     outs = [torch.empty((nl, cfg.dv), device=dev) for _ in range(L)]
-    S_l = [S_init[l * nl:(l + 1) * nl] for l in range(L)]
 
     def sl(x, t, l):
         return x[t, l * nl:(l + 1) * nl]
 
     def quantize_phase():
-        for l in range(L):
-            lq.leapquant_quantize_state(slabs[l], S_l[l])
+        lq.leapquant_quantize_state(slab, S_init)
 
     def decode_phase(w):
         for j in range(cfg.p):
@@ -136,8 +138,7 @@ def main():
                                          sl(tok["alpha"], t, l), outs[l])
 
     def close_phase():
-        for l in range(L):
-            lq.leapquant_window_close(slabs[l], cfg.p)
+        lq.leapquant_window_close(slab, cfg.p)
 
     if args.mode == "graph":
         stream = torch.cuda.Stream(device=dev)
@@ -200,10 +201,12 @@ def main():
     dec_avg_ms = dec_ms / n_dec
     dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(cfg.p)) / cfg.p
     dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    close_avg_ms = close_ms / (args.steps * windows * L)
-    close_gbs = nl * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda) / (close_avg_ms * 1e-3) / 1e9
+    close_avg_ms = close_ms / (args.steps * windows)
+    close_gbs = n * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda) / (close_avg_ms * 1e-3) / 1e9
     whole_gbs = value * bpht / 1e9
     dec_traffic, close_traffic = measured_traffic(cfg)
+    dec_traffic = round(dec_traffic * nl) if dec_traffic is not None else None
+    close_traffic = round(close_traffic * n) if close_traffic is not None else None
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
@@ -219,7 +222,8 @@ def main():
                      "traffic": dec_traffic, "bytes_per_launch": round(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "window_close": {"avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
-                         "bytes_per_launch": nl * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda),
+                         "bytes_per_launch": n * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda),
+                         "states_per_launch": n,
                          "traffic": close_traffic},
         "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
                        "bytes_per_head_token": round(bpht, 1)},

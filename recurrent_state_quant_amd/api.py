@@ -70,6 +70,20 @@ class LeapQuantState:
     def params(self):
         return L.LqParams(self.n, self.dk, self.dv, self.p, self.r, self.gate, self.flags)
 
+    def view(self, start, count):
+        """States start .. start+count-1 of this slab as a slab of their own
+        (views of the same memory).  Stacked layers kept in one allocation
+        can be decoded layer by layer through views and closed together in
+        one window-close call on the whole slab."""
+        if not (0 <= start and count >= 1 and start + count <= self.n):
+            raise ValueError("view out of range")
+        v = object.__new__(LeapQuantState)
+        v.n, v.p, v.r, v.dk, v.dv = int(count), self.p, self.r, self.dk, self.dv
+        v.gate, v.flags, v.device = self.gate, self.flags, self.device
+        for k in self.BOUNDARY + ("buf_gate", "buf_k", "buf_u"):
+            setattr(v, k, getattr(self, k)[start:start + count])
+        return v
+
     def ptrs(self):
         def vp(x):
             return x.data_ptr() if x.numel() else None

@@ -335,179 +335,56 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Window close / quantize: one 256-thread workgroup (4 waves) per state.
+// Window close and initial quantization: 256 threads (4 waves) per state.
 //
-// The rebuilt fp32 state lives in MFMA accumulators.  Wave w owns rows
+// The fp32 state lives in MFMA accumulator registers.  Wave w owns rows
 // 32w .. 32w+31 as two 16-row tiles; the 16 columns of tile ct map to value
 // columns 8c'+ct, so lane l holds 8 rows (32w + 16rt + 4(l>>4) + v) x 8
 // contiguous columns (8(l&15) .. +7): codes are read and written as 8-byte
 // row segments, 16 lanes covering one 128-byte row.
-//   acc  = K_w U          (v_mfma_f32_16x16x4_f32, K = records, newest
-//                          chunk first so the decays are running products)
-//   acc += Gamma * (deQ + comps)
-// with K_w[i][row] = rho_i[row] k~_i[row].  Each record chunk is staged in
-// LDS with coalesced 128-bit loads issued by all 256 threads at once.
-// Then: row L2 norms (DPP row reductions), top-r rank selection, extraction,
-// column absmax (smoothing scale), per-row absmax and int8 codes.
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 16;  // records staged in LDS per MFMA pass
 
-template <bool KDA, bool FROM_FP32>
-__global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
-  const int s = blockIdx.x;
+// Code byte B of `word` from x = q * inv (|x| <= 127): adding 1.5 * 2^23
+// rounds x to the nearest integer, ties to even, and leaves that integer's
+// two's-complement low byte in the low byte of the sum's bit pattern; the
+// SDWA form of the add writes exactly that byte into byte B of `word` and
+// keeps the other three.
+template <int B>
+__device__ __forceinline__ void pack_code(uint32_t &word, float x) {
+  static_assert(B >= 0 && B < 4, "byte index");
+  const float magic = 12582912.0f;
+  if (B == 0)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else if (B == 1)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else if (B == 2)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+}
+
+struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
+  float *norm;       // [D] row norms^2, later row absmax
+  int *sel;          // [D] compensator slot of a row or -1
+  float *cmx;        // [16 * D] column-max partials
+  float *sig;        // [D] 1 / s_j
+  float *inv;        // [D] 127 / m_i (0 for zero or extracted rows)
+};
+
+// a6-a8 on the fp32 state held in acc: row norms, top-r extraction (writes
+// comp_idx, comp_val), smoothing scales (col_scale), row scales (row_scale)
+// and int8 codes, all for state s.  Ends with every LDS array consumed.
+__device__ __forceinline__ void split_state(floatx4 (&acc)[2][8], const SplitLds &L, int8_t *codes,
+                                            float *row_scale, float *col_scale, int32_t *comp_idx,
+                                            float *comp_val, size_t s, int r, unsigned flags) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
-  const int r = A.r;
-
-  __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
-  __shared__ __attribute__((aligned(16))) float sh_U[kChunk * D];
-  __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : 64];
-  __shared__ float sh_G[D];
-  __shared__ float sh_a[D];
-  __shared__ __attribute__((aligned(16))) float sh_s[D];
-  __shared__ __attribute__((aligned(16))) float sh_norm[D];
-  __shared__ int sh_sel[D];
-  __shared__ int sh_oidx[16];
-  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
-
-  floatx4 acc[2][8];
-
-  if (FROM_FP32) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 32 * w + 16 * rt + 4 * lr + v;
-        const float *src = A.S_in + ((size_t)s * D + row) * D + 8 * lc;
-        const float4 x0 = ld4(src), x1 = ld4(src + 4);
-        acc[rt][0][v] = x0.x; acc[rt][1][v] = x0.y; acc[rt][2][v] = x0.z; acc[rt][3][v] = x0.w;
-        acc[rt][4][v] = x1.x; acc[rt][5][v] = x1.y; acc[rt][6][v] = x1.z; acc[rt][7][v] = x1.w;
-      }
-  } else {
-    const int len = A.len, p = A.p;
-    const size_t rec0 = (size_t)s * p;
-    // boundary-state side data and this lane's code segments, issued first
-    if (tid < D) {
-      sh_a[tid] = A.row_scale[(size_t)s * D + tid];
-      sh_s[tid] = A.col_scale[(size_t)s * D + tid];
-    }
-    if (tid < r) sh_oidx[tid] = A.comp_idx[(size_t)s * r + tid];
-    uint2 cw[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 32 * w + 16 * rt + 4 * lr + v;
-        cw[rt][v] = ldu2(A.codes + ((size_t)s * D + row) * D + 8 * lc);
-      }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // K_w U over the records, newest chunk first
-    float P = 1.f;  // running decay product for row tid (tid < D)
-    for (int hi = len; hi > 0; hi -= kChunk) {
-      const int lo = hi > kChunk ? hi - kChunk : 0;
-      const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
-      __syncthreads();
-      {
-        // kChunk * D / 4 = 512 float4 per array: two per thread, all loads
-        // of the chunk issued before the first LDS write
-        static_assert(kChunk * D / 4 == 512, "staging assumes two float4 per thread");
-        const float4 *su = reinterpret_cast<const float4 *>(A.buf_u + (rec0 + lo) * D);
-        const float4 *sk = reinterpret_cast<const float4 *>(A.buf_k + (rec0 + lo) * D);
-        const float4 *sg = reinterpret_cast<const float4 *>(A.buf_gate + (rec0 + lo) * D);
-        float4 *du = reinterpret_cast<float4 *>(sh_U);
-        float4 *dk = reinterpret_cast<float4 *>(sh_K);
-        float4 *dg = reinterpret_cast<float4 *>(sh_g);
-        const int nvec = cnt * (D / 4), npad = cnt4 * (D / 4);
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        const int e0 = tid, e1 = tid + 256;
-        float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
-        if (e0 < nvec) {
-          u0 = ld4(reinterpret_cast<const float *>(su + e0));
-          k0 = ld4(reinterpret_cast<const float *>(sk + e0));
-          if (KDA) g0 = ld4(reinterpret_cast<const float *>(sg + e0));
-        }
-        if (e1 < nvec) {
-          u1 = ld4(reinterpret_cast<const float *>(su + e1));
-          k1 = ld4(reinterpret_cast<const float *>(sk + e1));
-          if (KDA) g1 = ld4(reinterpret_cast<const float *>(sg + e1));
-        }
-        float gsc = 1.f;
-        if (!KDA && tid < cnt) gsc = A.buf_gate[rec0 + lo + tid];
-        if (e0 < npad) {
-          du[e0] = u0;
-          dk[e0] = k0;
-          if (KDA && e0 < nvec) dg[e0] = g0;
-        }
-        if (e1 < npad) {
-          du[e1] = u1;
-          dk[e1] = k1;
-          if (KDA && e1 < nvec) dg[e1] = g1;
-        }
-        if (!KDA && tid < cnt) sh_g[tid] = gsc;
-      }
-      __syncthreads();
-      if (tid < D) {
-        for (int j = cnt - 1; j >= 0; --j) {
-          sh_K[j * D + tid] *= P;
-          P *= KDA ? sh_g[j * D + tid] : sh_g[j];
-        }
-      }
-      __syncthreads();
-      for (int ks = 0; ks < cnt4 / 4; ++ks) {
-        const int kr = 4 * ks + lr;
-        const float a0 = sh_K[kr * D + 32 * w + lc];
-        const float a1 = sh_K[kr * D + 32 * w + 16 + lc];
-        const float4 b0 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc);
-        const float4 b1 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc + 4);
-        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bb[ct], acc[0][ct], 0, 0, 0);
-          acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bb[ct], acc[1][ct], 0, 0, 0);
-        }
-      }
-    }
-    // a_i * Gamma_i per row (the deQ row factor) and Gamma_i itself
-    if (tid < D) {
-      sh_G[tid] = P;
-      sh_a[tid] *= P;
-    }
-    __syncthreads();
-
-    // acc += (c * (a Gamma)) * s  +  Gamma * (compensator rows)
-    float sv[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sv[ct] = sh_s[8 * lc + ct];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 32 * w + 16 * rt + 4 * lr + v;
-        const float aG = sh_a[row];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          acc[rt][b][v] = fmaf((float)(int8_t)(cw[rt][v].x >> (8 * b)) * aG, sv[b], acc[rt][b][v]);
-          acc[rt][4 + b][v] = fmaf((float)(int8_t)(cw[rt][v].y >> (8 * b)) * aG, sv[4 + b], acc[rt][4 + b][v]);
-        }
-        for (int c = 0; c < r; ++c) {
-          if (sh_oidx[c] == row) {
-            const float G = sh_G[row];
-            const float *wp = A.comp_val + ((size_t)s * r + c) * D + 8 * lc;
-            const float4 w0 = ld4(wp), w1 = ld4(wp + 4);
-            acc[rt][0][v] = fmaf(G, w0.x, acc[rt][0][v]); acc[rt][1][v] = fmaf(G, w0.y, acc[rt][1][v]);
-            acc[rt][2][v] = fmaf(G, w0.z, acc[rt][2][v]); acc[rt][3][v] = fmaf(G, w0.w, acc[rt][3][v]);
-            acc[rt][4][v] = fmaf(G, w1.x, acc[rt][4][v]); acc[rt][5][v] = fmaf(G, w1.y, acc[rt][5][v]);
-            acc[rt][6][v] = fmaf(G, w1.z, acc[rt][6][v]); acc[rt][7][v] = fmaf(G, w1.w, acc[rt][7][v]);
-          }
-        }
-      }
-  }
-
   // ---- a6 row L2 norms (squared, fp32) and top-r selection
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
@@ -517,14 +394,14 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) q = fmaf(acc[rt][ct][v], acc[rt][ct][v], q);
       q = row16_sum(q);
-      if (lc == 0) sh_norm[32 * w + 16 * rt + 4 * lr + v] = q;
+      if (lc == 0) L.norm[32 * w + 16 * rt + 4 * lr + v] = q;
     }
-  if (tid < D) sh_sel[tid] = -1;
+  if (tid < D) L.sel[tid] = -1;
   __syncthreads();
   if (w == 0 && r > 0) {
     // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
     // takes the largest remaining norm, ties to the lower row index
-    float n0 = sh_norm[2 * lane], n1 = sh_norm[2 * lane + 1];
+    float n0 = L.norm[2 * lane], n1 = L.norm[2 * lane + 1];
     for (int c = 0; c < r; ++c) {
       const bool pick1 = n1 > n0;  // equal norms keep the lower row
       const float best = pick1 ? n1 : n0;
@@ -549,8 +426,8 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
         if (odd) n1 = -1.f; else n0 = -1.f;
       }
       if (lane == 0) {
-        sh_sel[wrow] = c;
-        A.comp_idx[(size_t)s * r + c] = wrow;
+        L.sel[wrow] = c;
+        comp_idx[s * r + c] = wrow;
       }
     }
   }
@@ -567,9 +444,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = 32 * w + 16 * rt + 4 * lr + v;
-      const int sel = sh_sel[row];
+      const int sel = L.sel[row];
       if (sel >= 0) {
-        float *wp = A.comp_val + ((size_t)s * r + sel) * D + 8 * lc;
+        float *wp = comp_val + (s * r + sel) * D + 8 * lc;
         st4(wp, make_float4(acc[rt][0][v], acc[rt][1][v], acc[rt][2][v], acc[rt][3][v]));
         st4(wp + 4, make_float4(acc[rt][4][v], acc[rt][5][v], acc[rt][6][v], acc[rt][7][v]));
       }
@@ -577,10 +454,8 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) cm[ct] = fmaxf(cm[ct], fabsf(acc[rt][ct][v]) * keep);
     }
-  // per-lane partial maxima (8 columns over 8 rows) to LDS; 16 partials per
-  // column (4 waves x 4 row groups)
   {
-    float4 *dst = reinterpret_cast<float4 *>(sh_cmx + (4 * w + lr) * D + 8 * lc);
+    float4 *dst = reinterpret_cast<float4 *>(L.cmx + (4 * w + lr) * D + 8 * lc);
     dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
     dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
   }
@@ -588,10 +463,10 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   if (tid < D) {
     float m = 0.f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) m = fmaxf(m, sh_cmx[g * D + tid]);
-    const float sc = (A.flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
-    A.col_scale[(size_t)s * D + tid] = sc;
-    sh_s[tid] = 1.f / sc;  // sigma_j, correctly rounded
+    for (int g = 0; g < 16; ++g) m = fmaxf(m, L.cmx[g * D + tid]);
+    const float sc = (flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
+    col_scale[s * D + tid] = sc;
+    L.sig[tid] = 1.f / sc;  // sigma_j, correctly rounded
   }
   __syncthreads();
 
@@ -599,7 +474,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   {
     float sig[8];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sig[ct] = sh_s[8 * lc + ct];
+    for (int ct = 0; ct < 8; ++ct) sig[ct] = L.sig[8 * lc + ct];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -611,50 +486,245 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
           m = fmaxf(m, fabsf(acc[rt][ct][v]));
         }
         m = row16_max(m);
-        if (lc == 0) sh_norm[32 * w + 16 * rt + 4 * lr + v] = m;
+        if (lc == 0) L.norm[32 * w + 16 * rt + 4 * lr + v] = m;
       }
   }
   __syncthreads();
   if (tid < D) {
     // row scale and its reciprocal, once per row (correctly rounded)
-    const float m = sh_norm[tid];
+    const float m = L.norm[tid];
     float a = 0.f, inv = 0.f;
-    if (m > 0.f && sh_sel[tid] < 0) {
+    if (m > 0.f && L.sel[tid] < 0) {
       a = m / 127.f;
       inv = 127.f / m;
     }
-    A.row_scale[(size_t)s * D + tid] = a;
-    sh_G[tid] = inv;
+    row_scale[s * D + tid] = a;
+    L.inv[tid] = inv;
   }
   __syncthreads();
-  // codes: rne(q * inv).  Adding 1.5 * 2^23 rounds to the nearest integer,
-  // ties to even, and leaves that integer's two's-complement low byte in the
-  // low byte of the sum's bit pattern (|q * inv| <= 127 by construction).
-  // The product is rounded on its own: no contraction into an FMA.
+  // codes: rne(q * inv), one v_add_f32 per code (see pack_code); the
+  // product is rounded on its own: no contraction into an FMA.
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
 #pragma clang fp contract(off)
       const int row = 32 * w + 16 * rt + 4 * lr + v;
-      const float inv = sh_G[row];
-      uint32_t by[8];
+      const float inv = L.inv[row];
+      uint32_t w0 = 0u, w1 = 0u;
+      pack_code<0>(w0, acc[rt][0][v] * inv);
+      pack_code<1>(w0, acc[rt][1][v] * inv);
+      pack_code<2>(w0, acc[rt][2][v] * inv);
+      pack_code<3>(w0, acc[rt][3][v] * inv);
+      pack_code<0>(w1, acc[rt][4][v] * inv);
+      pack_code<1>(w1, acc[rt][5][v] * inv);
+      pack_code<2>(w1, acc[rt][6][v] * inv);
+      pack_code<3>(w1, acc[rt][7][v] * inv);
+      __builtin_nontemporal_store(vu2{w0, w1},
+                                  reinterpret_cast<vu2 *>(codes + (s * D + row) * D + 8 * lc));
+    }
+}
+
+// ---- a9: split a caller fp32 state (one workgroup per state)
+__global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
+  const size_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  __shared__ float sh_norm[D], sh_sig[D], sh_inv[D];
+  __shared__ int sh_sel[D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
+  floatx4 acc[2][8];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 32 * w + 16 * rt + 4 * lr + v;
+      const float *src = A.S_in + (s * D + row) * D + 8 * lc;
+      const float4 x0 = ld4(src), x1 = ld4(src + 4);
+      acc[rt][0][v] = x0.x; acc[rt][1][v] = x0.y; acc[rt][2][v] = x0.z; acc[rt][3][v] = x0.w;
+      acc[rt][4][v] = x1.x; acc[rt][5][v] = x1.y; acc[rt][6][v] = x1.z; acc[rt][7][v] = x1.w;
+    }
+  const SplitLds L{sh_norm, sh_sel, sh_cmx, sh_sig, sh_inv};
+  split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, A.r, A.flags);
+}
+
+// ---- a5-a8: window close, one workgroup per state.
+//   acc  = Gamma (c (a s)) + Gamma comps   (window of <= kChunk records:
+//                                          the MFMAs accumulate onto it)
+//   acc += K_w U                           (v_mfma_f32_16x16x4_f32 over the
+//                                          records, newest chunk first: the
+//                                          decays are running products)
+// with K_w[i][row] = rho_i[row] k~_i[row].  Longer windows start from zero
+// and add the boundary term after the last chunk.  Each record chunk is
+// staged in LDS with 128-bit loads issued by all 256 threads before the
+// first LDS write.
+template <bool KDA>
+__global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
+  const size_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int r = A.r, len = A.len, p = A.p;
+  const size_t rec0 = s * p;
+
+  __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
+  __shared__ __attribute__((aligned(16))) float sh_U[kChunk * D];
+  __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : kChunk];
+  __shared__ float sh_a[D], sh_gam[D];
+  __shared__ __attribute__((aligned(16))) float sh_s[D];
+  __shared__ int sh_oidx[16];
+  __shared__ float sh_norm[D], sh_sig[D], sh_inv[D];
+  __shared__ int sh_sel[D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
+
+  // boundary-state side data and this lane's code segments, issued first
+  if (tid < D) {
+    sh_a[tid] = A.row_scale[s * D + tid];
+    sh_s[tid] = A.col_scale[s * D + tid];
+  }
+  if (tid < r) sh_oidx[tid] = A.comp_idx[s * r + tid];
+  uint2 cw[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 32 * w + 16 * rt + 4 * lr + v;
+      cw[rt][v] = ldu2(A.codes + (s * D + row) * D + 8 * lc);
+    }
+
+  floatx4 acc[2][8];
+  // acc += Gamma ((c (a Gamma)) s + compensator rows); Gamma from sh_gam
+  auto add_boundary = [&](bool first) {
+    float sv[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) sv[ct] = sh_s[8 * lc + ct];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 32 * w + 16 * rt + 4 * lr + v;
+        const float G = sh_gam[row];
+        const float aG = sh_a[row] * G;
+        float x[8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          x[b] = (float)(int8_t)(cw[rt][v].x >> (8 * b)) * (aG * sv[b]);
+          x[4 + b] = (float)(int8_t)(cw[rt][v].y >> (8 * b)) * (aG * sv[4 + b]);
+        }
+        for (int c = 0; c < r; ++c) {
+          if (sh_oidx[c] == row) {
+            const float *wp = A.comp_val + (s * r + c) * D + 8 * lc;
+            const float4 w0 = ld4(wp), w1 = ld4(wp + 4);
+            x[0] = fmaf(G, w0.x, x[0]); x[1] = fmaf(G, w0.y, x[1]);
+            x[2] = fmaf(G, w0.z, x[2]); x[3] = fmaf(G, w0.w, x[3]);
+            x[4] = fmaf(G, w1.x, x[4]); x[5] = fmaf(G, w1.y, x[5]);
+            x[6] = fmaf(G, w1.z, x[6]); x[7] = fmaf(G, w1.w, x[7]);
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[rt][ct][v] = first ? x[ct] : acc[rt][ct][v] + x[ct];
+      }
+  };
+
+  // stage records lo .. hi-1 in LDS (zero-padded to a multiple of 4) and
+  // fold the decays into K: sh_K[j] *= P, P *= gate_j, newest first
+  float P = 1.f;  // running decay product for row tid (tid < D)
+  auto stage = [&](int lo, int hi) {
+    const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
+    __syncthreads();
+    {
+      // kChunk * D / 4 = 512 float4 per array: two per thread, all loads
+      // of the chunk issued before the first LDS write
+      static_assert(kChunk * D / 4 == 512, "staging assumes two float4 per thread");
+      const float *su = A.buf_u + (rec0 + lo) * D;
+      const float *sk = A.buf_k + (rec0 + lo) * D;
+      const float *sg = A.buf_gate + (rec0 + lo) * D;
+      float4 *du = reinterpret_cast<float4 *>(sh_U);
+      float4 *dk = reinterpret_cast<float4 *>(sh_K);
+      float4 *dg = reinterpret_cast<float4 *>(sh_g);
+      const int nvec = cnt * (D / 4), npad = cnt4 * (D / 4);
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int e0 = tid, e1 = tid + 256;
+      float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
+      if (e0 < nvec) {
+        u0 = ld4(su + 4 * e0);
+        k0 = ld4(sk + 4 * e0);
+        if (KDA) g0 = ld4(sg + 4 * e0);
+      }
+      if (e1 < nvec) {
+        u1 = ld4(su + 4 * e1);
+        k1 = ld4(sk + 4 * e1);
+        if (KDA) g1 = ld4(sg + 4 * e1);
+      }
+      float gsc = 1.f;
+      if (!KDA && tid < cnt) gsc = A.buf_gate[rec0 + lo + tid];
+      if (e0 < npad) {
+        du[e0] = u0;
+        dk[e0] = k0;
+        if (KDA && e0 < nvec) dg[e0] = g0;
+      }
+      if (e1 < npad) {
+        du[e1] = u1;
+        dk[e1] = k1;
+        if (KDA && e1 < nvec) dg[e1] = g1;
+      }
+      if (!KDA && tid < cnt) sh_g[tid] = gsc;
+    }
+    __syncthreads();
+    if (tid < D) {
+      for (int j = cnt - 1; j >= 0; --j) {
+        sh_K[j * D + tid] *= P;
+        P *= KDA ? sh_g[j * D + tid] : sh_g[j];
+      }
+    }
+  };
+  // acc += K_w U over the staged records
+  auto contract = [&](int cnt) {
+    const int cnt4 = (cnt + 3) & ~3;
+    for (int ks = 0; ks < cnt4 / 4; ++ks) {
+      const int kr = 4 * ks + lr;
+      const float a0 = sh_K[kr * D + 32 * w + lc];
+      const float a1 = sh_K[kr * D + 32 * w + 16 + lc];
+      const float4 b0 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc);
+      const float4 b1 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc + 4);
+      const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const float x = acc[rt][ct][v] * inv;
-        by[ct] = __float_as_uint(x + 12582912.0f);
+        acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bb[ct], acc[0][ct], 0, 0, 0);
+        acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bb[ct], acc[1][ct], 0, 0, 0);
       }
-      // gather the low bytes: v_perm_b32 selector 0x0c0c0400 takes byte 0 of
-      // each source into bytes 0..1; the second perm merges two halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(by[1], by[0], 0x0c0c0400u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(by[3], by[2], 0x0c0c0400u);
-      const uint32_t lo45 = __builtin_amdgcn_perm(by[5], by[4], 0x0c0c0400u);
-      const uint32_t lo67 = __builtin_amdgcn_perm(by[7], by[6], 0x0c0c0400u);
-      const uint32_t w0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-      const uint32_t w1 = __builtin_amdgcn_perm(lo67, lo45, 0x05040100u);
-      __builtin_nontemporal_store(vu2{w0, w1},
-                                  reinterpret_cast<vu2 *>(A.codes + ((size_t)s * D + row) * D + 8 * lc));
     }
+  };
+
+  if (len <= kChunk) {
+    // one chunk: Gamma is known before the contraction, so the boundary
+    // term initialises the accumulators
+    stage(0, len);
+    if (tid < D) sh_gam[tid] = P;
+    __syncthreads();
+    add_boundary(true);
+    contract(len);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int hi = len; hi > 0; hi -= kChunk) {
+      const int lo = hi > kChunk ? hi - kChunk : 0;
+      stage(lo, hi);
+      __syncthreads();
+      contract(hi - lo);
+    }
+    if (tid < D) sh_gam[tid] = P;
+    __syncthreads();
+    add_boundary(false);
+  }
+  // every read of this state's compensator rows is done before the split
+  // overwrites them
+  __syncthreads();
+  const SplitLds L{sh_norm, sh_sel, sh_cmx, sh_sig, sh_inv};
+  split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, r, A.flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -699,14 +769,14 @@ hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream)
 
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream) {
   if (kda)
-    hipLaunchKernelGGL((close_kernel<true, false>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(close_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((close_kernel<false, false>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(close_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((close_kernel<false, true>), dim3(a.n), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(quantize_kernel, dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

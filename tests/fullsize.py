@@ -10,8 +10,8 @@ Two disjoint samples of states are followed:
     rounding-boundary flip makes the two trajectories part, then by a
     relative bound.
 All other states run alongside in the same launches (the benchmark's launch
-configuration: one launch per layer slab and token, one close per slab and
-window).
+configuration: one decode launch per layer and token, one window close over
+all layers' states per window).
 """
 import numpy as np
 import torch
@@ -90,10 +90,12 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
     o_f, b_f = O.run_windowed(S0s[:nf], tok_f, p, cfg.r, gate)
     o_r, b_r = O.run_windowed(S0s[nf:], tok_r, p, cfg.r, gate) if len(free) else (None, None)
 
-    slabs = [lq.LeapQuantState(nl, p, cfg.r, cfg.gate, DEV) for _ in range(L)]
+    # the benchmark's layout: one slab for all layers, decoded per layer
+    # through views, quantized and window-closed in one launch
+    slab = lq.LeapQuantState(cfg.n_states, p, cfg.r, cfg.gate, DEV)
+    slabs = [slab.view(l * nl, nl) for l in range(L)]
     outs = [torch.empty((nl, cfg.dv), device=DEV) for _ in range(L)]
-    for l in range(L):
-        lq.leapquant_quantize_state(slabs[l], S0[l * nl:(l + 1) * nl])
+    lq.leapquant_quantize_state(slab, S0)
     # boundary 0 of the forced states must already agree bit for bit
     P.compare_boundary(_gather_boundary(slabs, nl, forced), b_f[0], S0s[:nf], cfg.r,
                        f"{cfg.name} boundary 0", exact=True)
@@ -119,8 +121,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
                 dst, src = loc_t[l]
                 if len(dst):
                     rec[t].index_copy_(0, dst, outs[l].index_select(0, src))
-        for l in range(L):
-            lq.leapquant_window_close(slabs[l], p)
+        lq.leapquant_window_close(slab, p)
         ws = slice(w * p, (w + 1) * p)
         og = to_np(rec[ws])
         P.assert_close(og[:, :nf], o_f[ws], f"{cfg.name} window {w} forced outputs")
@@ -163,7 +164,8 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
         mid = keys[len(keys) // 2 - 1] if len(keys) > 1 else None
         if mid is not None:
             nxt = mid + checkpoint_every
-            res = [lq.LeapQuantState(nl, p, cfg.r, cfg.gate, DEV) for _ in range(L)]
+            rslab = lq.LeapQuantState(cfg.n_states, p, cfg.r, cfg.gate, DEV)
+            res = [rslab.view(l * nl, nl) for l in range(L)]
             for l in range(L):
                 res[l].load_boundary(snaps[mid][l])
             for w in range(mid // p, nxt // p):
@@ -173,8 +175,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
                         sl = slice(l * nl, (l + 1) * nl)
                         lq.leapquant_decode_step(res[l], j, tok["q"][t, sl], tok["k"][t, sl], tok["v"][t, sl],
                                                  tok["beta"][t, sl], tok["alpha"][t, sl], outs[l])
-                for l in range(L):
-                    lq.leapquant_window_close(res[l], p)
+                lq.leapquant_window_close(rslab, p)
             # forced states were overwritten by injection in the original run:
             # compare the states that ran untouched
             untouched = torch.ones(cfg.n_states, dtype=torch.bool)
