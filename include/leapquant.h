@@ -40,7 +40,13 @@
  *     returns without waiting.  Device faults surface at the caller's next
  *     synchronization.
  *   - Arrays are dense, row-major, in the shapes given below; n is the
- *     leading dimension of every per-state array.
+ *     leading dimension of every per-state array.  The codes of one state
+ *     are a 16 KiB block stored column-major in two 64-row halves: code
+ *     (i, j) is byte (i >> 6) * 8192 + j * 64 + slot(i & 63), where
+ *     slot(x) = (x & 0x0C) << 2 | (x & 0x30) >> 2 | (x & 3) swaps the two
+ *     2-bit fields above the lowest two bits.  Both kernels then move codes
+ *     as 16-byte column segments (the int8 MFMA operand of the decode GEMV
+ *     and the accumulator rows of one lane in the window close).
  *   - Alignment: codes and every float array whose per-state extent is a
  *     multiple of 128 floats must be 16-byte aligned; beta, a scalar alpha,
  *     comp_idx and a scalar buf_gate need 4-byte alignment.
@@ -66,7 +72,7 @@
 extern "C" {
 #endif
 
-#define LEAPQUANT_ABI_VERSION 1
+#define LEAPQUANT_ABI_VERSION 2
 
 typedef enum lq_status {
   LQ_OK = 0,
@@ -99,7 +105,7 @@ typedef struct lq_params {
  * (the prefix-cache snapshot); the last three are the window buffer.  For
  * r == 0, comp_idx and comp_val may be NULL. */
 typedef struct lq_state {
-  int8_t *codes;     /* [n][dk][dv] int8 residual codes c_ij                */
+  int8_t *codes;     /* [n][dk*dv]  int8 residual codes c_ij (layout above) */
   float *row_scale;  /* [n][dk]     a_i                                     */
   float *col_scale;  /* [n][dv]     s_j                                     */
   int32_t *comp_idx; /* [n][r]      row index of each compensator row       */

@@ -41,12 +41,51 @@ def _stream(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def code_offsets(dk=128, dv=128):
+    """Byte offset, inside one state's 16 KiB code block, of code (i, j), as
+    an int64 array [dk][dv].  Codes are stored column-major in two 64-row
+    halves: offset (i >> 6) * 8192 + j * 64 + slot(i & 63), where slot swaps
+    the two 2-bit fields above the lowest two bits of i & 63."""
+    if (dk, dv) != (128, 128):
+        raise ValueError("the code layout is defined for dk = dv = 128")
+    i = torch.arange(dk, dtype=torch.int64).view(dk, 1)
+    j = torch.arange(dv, dtype=torch.int64).view(1, dv)
+    x = i & 63
+    slot = ((x & 0x0C) << 2) | ((x & 0x30) >> 2) | (x & 3)
+    return (i >> 6) * 8192 + j * 64 + slot
+
+
+_OFFSETS = {}
+
+
+def _offsets(device):
+    key = str(device)
+    if key not in _OFFSETS:
+        _OFFSETS[key] = code_offsets().reshape(-1).to(device)
+    return _OFFSETS[key]
+
+
+def codes_to_matrix(raw):
+    """Stored codes [n][dk*dv] -> row-major int8 matrices [n][dk][dv]."""
+    n = raw.shape[0]
+    return raw.reshape(n, -1).index_select(1, _offsets(raw.device)).reshape(n, 128, 128)
+
+
+def codes_from_matrix(mat):
+    """Row-major int8 matrices [n][dk][dv] -> stored codes [n][dk*dv]."""
+    n = mat.shape[0]
+    out = torch.empty((n, 128 * 128), dtype=mat.dtype, device=mat.device)
+    out[:, _offsets(mat.device)] = mat.reshape(n, -1)
+    return out
+
+
 class LeapQuantState:
     """Device arrays of one slab of n states: boundary state + window buffer.
 
-    codes int8 [n,dk,dv]; row_scale [n,dk]; col_scale [n,dv]; comp_idx int32
-    [n,r]; comp_val [n,r,dv]; buf_gate [n,p] (gdn) or [n,p,dk] (kda);
-    buf_k [n,p,dk]; buf_u [n,p,dv].
+    codes int8 [n][dk*dv] in the stored layout (see code_offsets);
+    row_scale [n,dk]; col_scale [n,dv]; comp_idx int32 [n,r]; comp_val
+    [n,r,dv]; buf_gate [n,p] (gdn) or [n,p,dk] (kda); buf_k [n,p,dk];
+    buf_u [n,p,dv].
     """
 
     BOUNDARY = ("codes", "row_scale", "col_scale", "comp_idx", "comp_val")
@@ -57,7 +96,7 @@ class LeapQuantState:
         self.flags = int(flags)
         dev = torch.device(device)
         self.device = dev
-        self.codes = torch.zeros((n, dk, dv), dtype=_I8, device=dev)
+        self.codes = torch.zeros((n, dk * dv), dtype=_I8, device=dev)
         self.row_scale = torch.zeros((n, dk), dtype=_F32, device=dev)
         self.col_scale = torch.ones((n, dv), dtype=_F32, device=dev)
         self.comp_idx = torch.zeros((n, r), dtype=_I32, device=dev)
@@ -91,18 +130,39 @@ class LeapQuantState:
                          vp(self.comp_idx), vp(self.comp_val), vp(self.buf_gate),
                          vp(self.buf_k), vp(self.buf_u))
 
-    def boundary(self):
-        """The boundary-state tensors (views; clone for a snapshot)."""
-        return {k: getattr(self, k) for k in self.BOUNDARY}
+    def _index(self, idx):
+        if idx is None:
+            return None
+        return torch.as_tensor(idx, dtype=torch.long, device=self.device).reshape(-1)
+
+    def boundary(self, idx=None):
+        """Copy of the boundary state of all states (or of states idx), with
+        the codes as row-major int8 matrices [m][dk][dv]."""
+        ix = self._index(idx)
+        out = {}
+        for k in self.BOUNDARY:
+            x = getattr(self, k)
+            x = x.clone() if ix is None else x.index_select(0, ix)
+            out[k] = codes_to_matrix(x) if k == "codes" else x
+        return out
 
     def snapshot(self):
-        return {k: getattr(self, k).clone() for k in self.BOUNDARY}
+        """The boundary state (the prefix-cache snapshot), as boundary()."""
+        return self.boundary()
 
-    def load_boundary(self, b):
-        """Copy a boundary state (dict of tensors or arrays) into this slab."""
+    def load_boundary(self, b, idx=None):
+        """Write a boundary state (dict of tensors or arrays, codes as
+        row-major matrices [m][dk][dv]) into all states or into states idx."""
+        ix = self._index(idx)
         for k in self.BOUNDARY:
-            src = torch.as_tensor(b[k]).to(getattr(self, k).dtype)
-            getattr(self, k).copy_(src.reshape(getattr(self, k).shape), non_blocking=False)
+            dst = getattr(self, k)
+            src = torch.as_tensor(b[k]).to(device=dst.device, dtype=dst.dtype)
+            if k == "codes":
+                src = codes_from_matrix(src.reshape(-1, self.dk, self.dv))
+            if ix is None:
+                dst.copy_(src.reshape(dst.shape))
+            else:
+                dst[ix] = src.reshape((len(ix),) + tuple(dst.shape[1:]))
 
 
 def leapquant_quantize_state(state, S, stream=None):

@@ -7,10 +7,17 @@
 //        "Quantize less often, protect the outliers".
 //
 // State layout per state s (dk = dv = 128):
-//   codes     int8  [128][128] row-major (row = key channel i, col = value j)
+//   codes     int8  16 KiB, column-major in two 64-row halves: code (i, j) at
+//                   byte (i >> 6) * 8192 + j * 64 + slot(i & 63), with
+//                   slot(x) = (x & 0x0C) << 2 | (x & 0x30) >> 2 | (x & 3)
+//                   (the two 2-bit fields above the lowest two swapped)
 //   row_scale fp32  [128] a_i,  col_scale fp32 [128] s_j
 //   comp_idx  int32 [r],        comp_val  fp32 [r][128]
 //   buffer    buf_gate [p] or [p][128], buf_k [p][128], buf_u [p][128]
+// The code layout serves both kernels with 16-byte accesses: in the decode
+// GEMV one lane's 16 bytes are the 16 rows of one column that an int8 MFMA
+// lane consumes, and in the window close they are the 16 rows of one column
+// that one lane holds in its MFMA accumulators.
 //
 // Windowed form used by the decode step (exact algebra of the recurrence of
 // [EL] Table 4 started from the boundary state B and replayed through the
@@ -64,10 +71,15 @@ __device__ __forceinline__ void st4(float *p, float4 v) {
 }
 
 // DPP lane permutes (gfx9 encodings): quad_perm, row_half_mirror, row_mirror.
+// Every pattern used reads a lane that exists, so bound_ctrl is irrelevant;
+// setting it lets the compiler fold the move into the consuming operation.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
 // Sum / max over the 16 lanes of a DPP row; every lane of the row gets it.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -84,6 +96,17 @@ __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp<0x140>(x));
   return x;
 }
+// Max of non-negative floats (or +NaN) over a DPP row: for such values the
+// IEEE order is the order of the bit patterns as integers, and an integer
+// max folds into one DPP instruction per step.
+__device__ __forceinline__ float row16_max_nn(float x) {
+  int v = __float_as_int(x);
+  v = max(v, dppi<0xB1>(v));
+  v = max(v, dppi<0x4E>(v));
+  v = max(v, dppi<0x141>(v));
+  v = max(v, dppi<0x140>(v));
+  return __int_as_float(v);
+}
 __device__ __forceinline__ float wave_sum(float x) {
   x = row16_sum(x);
   x += __shfl_xor(x, 16);
@@ -94,12 +117,22 @@ __device__ __forceinline__ float wave_sum(float x) {
 // ---------------------------------------------------------------------------
 // Decode step: one wave per state.
 //
-// Lane l owns key rows / value columns 2l and 2l+1 for the vector work.  For
-// the int8 GEMV it owns the 16-byte column chunk cc = l & 7 of rows
-// rg + 8m (rg = l >> 3, m = 0..15): each of the 16 loads of the wave reads 8
-// full rows (1 KiB, fully coalesced 128-bit loads) and both vectors
-// (Gamma*alpha*k and Gamma*alpha*q, scaled by a_i) are accumulated from one
-// pass over the codes.
+// Lane l owns key rows / value columns 2l and 2l+1 for the vector work.
+//
+// The int8 GEMV z = c^T W for the two weight vectors W = a * Gamma * y
+// (y = alpha*k and alpha*q) runs on v_mfma_i32_16x16x64_i8 and is exact in
+// integers: each weight vector is scaled by a power of two 2^e so that
+// |W 2^e| < 2^30, rounded to an integer x_i (an error of at most 2^-31 of
+// the vector's largest entry, below fp32 rounding of that entry), and x_i is
+// split into four signed base-256 digits d0..d3 (x = d0 + 2^8 d1 + 2^16 d2 +
+// 2^24 d3, each in [-128, 127]).  The MFMA's A operand holds the 8 digit
+// rows (2 vectors x 4 digits; rows 8..15 are zero), its B operand the
+// codes: lane (g = l >> 4, n = l & 15) loads, for row half kb and column
+// tile nt, the 16 bytes of column 16nt + n at slots 16g .. 16g+15, which is
+// exactly the B layout of the instruction (one 128-bit load per operand,
+// 1 KiB contiguous per wave load).  The A lane holds the digits of the same
+// 16 slots, written to LDS by slot.  Integer sums per digit are bounded by
+// 128 * 128 * 127 < 2^21, combined in fp32 and scaled back by 2^-e.
 //
 // Memory-level parallelism: every load a phase needs is issued before the
 // phase waits on any of them.  The token inputs, the newest kRecChunk
@@ -113,7 +146,33 @@ __device__ __forceinline__ float wave_sum(float x) {
 constexpr int kRecChunk = 16;    // records in flight per chunk
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
 constexpr int kRedStride = 33;   // odd row stride of the transposed partials: no bank conflicts
-constexpr int kGemvStride = 260; // padded row of the GEMV partials (16B aligned)
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// slot of row i & 63 inside its column segment (see the state layout)
+__device__ __forceinline__ int code_slot(int x) {
+  return ((x & 0x0C) << 2) | ((x & 0x30) >> 2) | (x & 3);
+}
+
+// max over the wave of non-negative floats
+__device__ __forceinline__ float wave_max_nn(float x) {
+  int v = __float_as_int(row16_max_nn(x));
+  v = max(v, __shfl_xor(v, 16));
+  v = max(v, __shfl_xor(v, 32));
+  return __int_as_float(v);
+}
+
+// Signed base-256 digits of x (|x| < 2^30): byte k of the result is the
+// low byte of x_k, where x_0 = x and x_{k+1} = (x_k + 128) >> 8, so that
+// x = sum_k 2^(8k) * sext(byte k).
+__device__ __forceinline__ uint32_t digits4(int x0) {
+  const int x1 = (x0 + 128) >> 8;
+  const int x2 = (x1 + 128) >> 8;
+  const int x3 = (x2 + 128) >> 8;
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)x1, (uint32_t)x0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)x3, (uint32_t)x2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
 
 template <bool KDA>
 __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
@@ -121,9 +180,10 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   const int lane = threadIdx.x;
   const int t = A.t, p = A.p, r = A.r;
 
-  __shared__ float2 sh_w[D];   // a_i * Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_gy[D];  // Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_h[64];  // record weights (h_b, h_q)
+  __shared__ float2 sh_z[D];   // GEMV result (z_b, z_q) per column
+  __shared__ __attribute__((aligned(16))) uint8_t sh_dig[8 * 2 * 64];  // [vector*4+digit][half][slot]
   __shared__ __attribute__((aligned(16))) float sh_red[64 * kRedStride];
 
   const size_t vo = (size_t)s * D + 2 * lane;
@@ -166,13 +226,19 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
       cw[c] = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
     }
   }
-  // ---- issue: the 16 KiB of int8 codes of this state
-  const int cc = lane & 7, rg = lane >> 3;
-  const uint4 *csrc =
-      reinterpret_cast<const uint4 *>(A.codes + (size_t)s * D * D) + rg * 8 + cc;
-  uint4 cv[16];
+  const float2 ar = ld2(A.row_scale + vo);
+  // ---- issue: the 16 KiB of int8 codes, as the MFMA B operands
+  const int n16 = lane & 15, g = lane >> 4;
+  const uint8_t *cbase =
+      reinterpret_cast<const uint8_t *>(A.codes) + (size_t)s * D * D + n16 * 64 + 16 * g;
+  v4i cv[2][8];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) cv[m] = ldu4(csrc + m * 64);
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const uint4 x = ldu4(cbase + kb * 8192 + nt * 1024);
+      cv[kb][nt] = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    }
 
   // ---- a1 token prep; append k~_t and the gate of record t
   const float2 kt = make_float2(bt * kk.x, bt * kk.y);
@@ -235,54 +301,66 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   for (int j = 0; j < kRecChunk; ++j)
     if (j < t - ulo) ur[j] = ld2(A.buf_u + (rec0 + ulo + j) * D + 2 * lane);
 
-  // ---- GEMV weights: a_i * Gamma_i * y_i
+  // ---- GEMV weights W = a_i Gamma_i y_i as integers with a power-of-two
+  // scale per vector, split into digits and written to LDS by slot
+  int eb, eq;  // W * 2^eb, W * 2^eq are below 2^30 in magnitude
   {
-    const float2 ar = ld2(A.row_scale + vo);
     const float2 G = KDA ? Pk : make_float2(Pg, Pg);
     const float2 gb = make_float2(G.x * yb.x, G.y * yb.y);
     const float2 gq = make_float2(G.x * yq.x, G.y * yq.y);
     sh_gy[2 * lane] = make_float2(gb.x, gq.x);
     sh_gy[2 * lane + 1] = make_float2(gb.y, gq.y);
-    sh_w[2 * lane] = make_float2(ar.x * gb.x, ar.x * gq.x);
-    sh_w[2 * lane + 1] = make_float2(ar.y * gb.y, ar.y * gq.y);
+    const float wb0 = ar.x * gb.x, wb1 = ar.y * gb.y;
+    const float wq0 = ar.x * gq.x, wq1 = ar.y * gq.y;
+    const float mb = wave_max_nn(fmaxf(fabsf(wb0), fabsf(wb1)));
+    const float mq = wave_max_nn(fmaxf(fabsf(wq0), fabsf(wq1)));
+    // max < 2^frexp_exp(max), so W * 2^(30 - exp) < 2^30 (exact scaling)
+    eb = 30 - __builtin_amdgcn_frexp_expf(mb);
+    eq = 30 - __builtin_amdgcn_frexp_expf(mq);
+    const uint32_t db0 = digits4(__float2int_rn(ldexpf(wb0, eb)));
+    const uint32_t db1 = digits4(__float2int_rn(ldexpf(wb1, eb)));
+    const uint32_t dq0 = digits4(__float2int_rn(ldexpf(wq0, eq)));
+    const uint32_t dq1 = digits4(__float2int_rn(ldexpf(wq1, eq)));
+    // rows 2l and 2l+1 sit in adjacent slots of the same half
+    const int kb = lane >> 5, sl = code_slot((2 * lane) & 63);
+    uint16_t *dst = reinterpret_cast<uint16_t *>(sh_dig + kb * 64 + sl);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t sel = 0x0c0c0400u + 0x00000101u * d;  // byte d of each
+      dst[(d * 2) * 32] = (uint16_t)__builtin_amdgcn_perm(db1, db0, sel);
+      dst[((4 + d) * 2) * 32] = (uint16_t)__builtin_amdgcn_perm(dq1, dq0, sel);
+    }
   }
   __syncthreads();
 
-  // ---- a3 int8 GEMV: both vectors from one pass over the codes
-  float accb[16], accq[16];
+  // ---- a3 int8 GEMV on MFMA: both vectors, all four digits
+  {
+    const int m = lane & 15;
+    v4i da[2];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) accb[j] = accq[j] = 0.f;
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint4 x = *reinterpret_cast<const uint4 *>(sh_dig + ((m & 7) * 2 + kb) * 64 + 16 * g);
+      da[kb] = m < 8 ? v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w} : v4i{0, 0, 0, 0};
+    }
+    const int e = g == 0 ? eb : eq;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const float2 w = sh_w[rg + 8 * m];
-    const uint32_t wd[4] = {cv[m].x, cv[m].y, cv[m].z, cv[m].w};
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float c = (float)(int8_t)(wd[q4] >> (8 * b));
-        accb[4 * q4 + b] = fmaf(c, w.x, accb[4 * q4 + b]);
-        accq[4 * q4 + b] = fmaf(c, w.y, accq[4 * q4 + b]);
+    for (int nt = 0; nt < 8; ++nt) {
+      v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[0], cv[0][nt], v4i{0, 0, 0, 0}, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(da[1], cv[1][nt], acc, 0, 0, 0);
+      // lane (g, n16) holds digits 0..3 of vector g for column 16nt + n16
+      if (g < 2) {
+        const float zs = fmaf((float)acc.w, 16777216.f,
+                              fmaf((float)acc.z, 65536.f, fmaf((float)acc.y, 256.f, (float)acc.x)));
+        reinterpret_cast<float *>(&sh_z[16 * nt + n16])[g] = ldexpf(zs, -e);
       }
     }
   }
-  // reduce over the 8 row groups through LDS
-  {
-    float4 *dst = reinterpret_cast<float4 *>(sh_red + rg * kGemvStride + 16 * cc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dst[j] = make_float4(accb[4 * j], accb[4 * j + 1], accb[4 * j + 2], accb[4 * j + 3]);
-      dst[32 + j] = make_float4(accq[4 * j], accq[4 * j + 1], accq[4 * j + 2], accq[4 * j + 3]);
-    }
-  }
   __syncthreads();
-  float2 zb = make_float2(0.f, 0.f), zq = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const float2 pb = *reinterpret_cast<const float2 *>(sh_red + g * kGemvStride + 2 * lane);
-    const float2 pq = *reinterpret_cast<const float2 *>(sh_red + g * kGemvStride + 128 + 2 * lane);
-    zb.x += pb.x; zb.y += pb.y;
-    zq.x += pq.x; zq.y += pq.y;
+  float2 zb, zq;
+  {
+    const float2 z0 = sh_z[2 * lane], z1 = sh_z[2 * lane + 1];
+    zb = make_float2(z0.x, z1.x);
+    zq = make_float2(z0.y, z1.y);
   }
 
   // ---- a4 combine: column scales, compensator rows, buffered records
@@ -295,18 +373,18 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 #pragma unroll
   for (int c = 0; c < kCompEarly; ++c) {
     if (c < r && (unsigned)cidx[c] < (unsigned)D) {
-      const float2 g = sh_gy[cidx[c]];
-      zb.x = fmaf(cw[c].x, g.x, zb.x); zb.y = fmaf(cw[c].y, g.x, zb.y);
-      zq.x = fmaf(cw[c].x, g.y, zq.x); zq.y = fmaf(cw[c].y, g.y, zq.y);
+      const float2 gg = sh_gy[cidx[c]];
+      zb.x = fmaf(cw[c].x, gg.x, zb.x); zb.y = fmaf(cw[c].y, gg.x, zb.y);
+      zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
     }
   }
   for (int c = kCompEarly; c < r; ++c) {
     const int idx = A.comp_idx[(size_t)s * r + c];
     if ((unsigned)idx < (unsigned)D) {
-      const float2 g = sh_gy[idx];
+      const float2 gg = sh_gy[idx];
       const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
-      zb.x = fmaf(w.x, g.x, zb.x); zb.y = fmaf(w.y, g.x, zb.y);
-      zq.x = fmaf(w.x, g.y, zq.x); zq.y = fmaf(w.y, g.y, zq.y);
+      zb.x = fmaf(w.x, gg.x, zb.x); zb.y = fmaf(w.y, gg.x, zb.y);
+      zq.x = fmaf(w.x, gg.y, zq.x); zq.y = fmaf(w.y, gg.y, zq.y);
     }
   }
   {
@@ -337,11 +415,27 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 // ---------------------------------------------------------------------------
 // Window close and initial quantization: 256 threads (4 waves) per state.
 //
-// The fp32 state lives in MFMA accumulator registers.  Wave w owns rows
-// 32w .. 32w+31 as two 16-row tiles; the 16 columns of tile ct map to value
-// columns 8c'+ct, so lane l holds 8 rows (32w + 16rt + 4(l>>4) + v) x 8
-// contiguous columns (8(l&15) .. +7): codes are read and written as 8-byte
-// row segments, 16 lanes covering one 128-byte row.
+// The rebuilt fp32 state lives in MFMA accumulators.  Wave w owns the rows
+// of half h = w & 1 (64h .. 64h+63) and the columns of half ch = w >> 1
+// (64ch .. 64ch+63) as 4 x 4 tiles of 16 x 16 (tile ct holds columns
+// 64ch + 16ct .. +15).  Lane l (lr = l >> 4, lc = l & 15) holds, for each of
+// its 4 columns 64ch + 16ct + lc, the 16 rows 64h + 16rt + 4lr + v (rt, v =
+// 0..3), which are slots 16lr .. 16lr+15 of that column's segment in the
+// code layout: codes are read and written as one 16-byte access per column,
+// and one wave instruction covers 16 adjacent column segments (1 KiB of
+// whole cache lines).
+//   acc  = Gamma (deQ + comps)    (window of <= kChunk records: the MFMAs
+//                                  accumulate onto it)
+//   acc += K_w U                  (v_mfma_f32_16x16x4_f32 over the records,
+//                                  newest chunk first: the decays are
+//                                  running products)
+// with K_w[i][row] = rho_i[row] k~_i[row].  Longer windows start from zero
+// and add the boundary term after the last chunk.  Each record chunk is
+// staged in LDS with 128-bit loads issued by all 256 threads before the
+// first LDS write.
+// Then (split_state): row norms, top-r rank selection, extraction, column
+// absmax (smoothing scale), per-row absmax and int8 codes.  Row reductions
+// combine the two column-half waves through LDS.
 // ---------------------------------------------------------------------------
 constexpr int kChunk = 16;  // records staged in LDS per MFMA pass
 
@@ -368,10 +462,17 @@ __device__ __forceinline__ void pack_code(uint32_t &word, float x) {
                  : "+v"(word) : "v"(x), "v"(magic));
 }
 
+__device__ __forceinline__ float f4get(const float4 &x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+__device__ __forceinline__ uint32_t u4get(const uint4 &x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
 struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
-  float *norm;       // [D] row norms^2, later row absmax
+  float *part;       // [2][D] per column half: row norms^2, later row absmax
   int *sel;          // [D] compensator slot of a row or -1
-  float *cmx;        // [16 * D] column-max partials
+  float *cmx;        // [8][D] column-max partials
   float *sig;        // [D] 1 / s_j
   float *inv;        // [D] 127 / m_i (0 for zero or extracted rows)
 };
@@ -379,29 +480,33 @@ struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
 // a6-a8 on the fp32 state held in acc: row norms, top-r extraction (writes
 // comp_idx, comp_val), smoothing scales (col_scale), row scales (row_scale)
 // and int8 codes, all for state s.  Ends with every LDS array consumed.
-__device__ __forceinline__ void split_state(floatx4 (&acc)[2][8], const SplitLds &L, int8_t *codes,
+__device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds &L, int8_t *codes,
                                             float *row_scale, float *col_scale, int32_t *comp_idx,
                                             float *comp_val, size_t s, int r, unsigned flags) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
-  // ---- a6 row L2 norms (squared, fp32) and top-r selection
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;  // row of (rt, v) = rbase + 16 rt + v
+  const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
+  // ---- a6 row L2 norms (squared, fp32; two column-half partials)
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float q = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) q = fmaf(acc[rt][ct][v], acc[rt][ct][v], q);
+      for (int ct = 0; ct < 4; ++ct) q = fmaf(acc[rt][ct][v], acc[rt][ct][v], q);
       q = row16_sum(q);
-      if (lc == 0) L.norm[32 * w + 16 * rt + 4 * lr + v] = q;
+      if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = q;
     }
   if (tid < D) L.sel[tid] = -1;
   __syncthreads();
   if (w == 0 && r > 0) {
     // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
     // takes the largest remaining norm, ties to the lower row index
-    float n0 = L.norm[2 * lane], n1 = L.norm[2 * lane + 1];
+    float n0 = L.part[2 * lane] + L.part[D + 2 * lane];
+    float n1 = L.part[2 * lane + 1] + L.part[D + 2 * lane + 1];
     for (int c = 0; c < r; ++c) {
       const bool pick1 = n1 > n0;  // equal norms keep the lower row
       const float best = pick1 ? n1 : n0;
@@ -434,36 +539,40 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[2][8], const SplitLds
   __syncthreads();
 
   // ---- extraction and a7 column absmax of the residual.  Extracted rows
-  // are not zeroed in registers: they are left out of the column maxima
-  // here and get row scale 0 (hence codes 0) below.
-  float cm[8];
+  // are written out and zeroed in the lanes that hold them (a branch that
+  // most waves skip), so they drop out of the column maxima and get row
+  // scale 0 (hence codes 0) below.
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) cm[ct] = 0.f;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 4; ++rt) {
+    const int4 sl4 = *reinterpret_cast<const int4 *>(L.sel + rbase + 16 * rt);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int row = 32 * w + 16 * rt + 4 * lr + v;
-      const int sel = L.sel[row];
+      const int sel = v == 0 ? sl4.x : v == 1 ? sl4.y : v == 2 ? sl4.z : sl4.w;
       if (sel >= 0) {
-        float *wp = comp_val + (s * r + sel) * D + 8 * lc;
-        st4(wp, make_float4(acc[rt][0][v], acc[rt][1][v], acc[rt][2][v], acc[rt][3][v]));
-        st4(wp + 4, make_float4(acc[rt][4][v], acc[rt][5][v], acc[rt][6][v], acc[rt][7][v]));
-      }
-      const float keep = sel < 0 ? 1.f : 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) cm[ct] = fmaxf(cm[ct], fabsf(acc[rt][ct][v]) * keep);
+        for (int ct = 0; ct < 4; ++ct) comp_val[(s * r + sel) * D + col0 + 16 * ct] = acc[rt][ct][v];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = 0.f;
+      }
     }
-  {
-    float4 *dst = reinterpret_cast<float4 *>(L.cmx + (4 * w + lr) * D + 8 * lc);
-    dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
-    dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
   }
+  float cm[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    float m = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(acc[rt][ct][v]));
+    cm[ct] = m;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) L.cmx[(4 * h + lr) * D + col0 + 16 * ct] = cm[ct];
   __syncthreads();
   if (tid < D) {
     float m = 0.f;
 #pragma unroll
-    for (int g = 0; g < 16; ++g) m = fmaxf(m, L.cmx[g * D + tid]);
+    for (int g = 0; g < 8; ++g) m = fmaxf(m, L.cmx[g * D + tid]);
     const float sc = (flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
     col_scale[s * D + tid] = sc;
     L.sig[tid] = 1.f / sc;  // sigma_j, correctly rounded
@@ -472,27 +581,27 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[2][8], const SplitLds
 
   // ---- a8 smoothed residual q = R * sigma (in place), per-row absmax
   {
-    float sig[8];
+    float sig[4];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sig[ct] = L.sig[8 * lc + ct];
+    for (int ct = 0; ct < 4; ++ct) sig[ct] = L.sig[col0 + 16 * ct];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float m = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
+        for (int ct = 0; ct < 4; ++ct) {
           acc[rt][ct][v] = acc[rt][ct][v] * sig[ct];
           m = fmaxf(m, fabsf(acc[rt][ct][v]));
         }
-        m = row16_max(m);
-        if (lc == 0) L.norm[32 * w + 16 * rt + 4 * lr + v] = m;
+        m = row16_max_nn(m);
+        if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = m;
       }
   }
   __syncthreads();
   if (tid < D) {
     // row scale and its reciprocal, once per row (correctly rounded)
-    const float m = L.norm[tid];
+    const float m = fmaxf(L.part[tid], L.part[D + tid]);
     float a = 0.f, inv = 0.f;
     if (m > 0.f && L.sel[tid] < 0) {
       a = m / 127.f;
@@ -504,25 +613,27 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[2][8], const SplitLds
   __syncthreads();
   // codes: rne(q * inv), one v_add_f32 per code (see pack_code); the
   // product is rounded on its own: no contraction into an FMA.
+  {
+    float4 iv[4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt) iv[rt] = *reinterpret_cast<const float4 *>(L.inv + rbase + 16 * rt);
+    int8_t *cdst = codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;  // + 1024 ct
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int ct = 0; ct < 4; ++ct) {
 #pragma clang fp contract(off)
-      const int row = 32 * w + 16 * rt + 4 * lr + v;
-      const float inv = L.inv[row];
-      uint32_t w0 = 0u, w1 = 0u;
-      pack_code<0>(w0, acc[rt][0][v] * inv);
-      pack_code<1>(w0, acc[rt][1][v] * inv);
-      pack_code<2>(w0, acc[rt][2][v] * inv);
-      pack_code<3>(w0, acc[rt][3][v] * inv);
-      pack_code<0>(w1, acc[rt][4][v] * inv);
-      pack_code<1>(w1, acc[rt][5][v] * inv);
-      pack_code<2>(w1, acc[rt][6][v] * inv);
-      pack_code<3>(w1, acc[rt][7][v] * inv);
-      __builtin_nontemporal_store(vu2{w0, w1},
-                                  reinterpret_cast<vu2 *>(codes + (s * D + row) * D + 8 * lc));
+      uint32_t wd[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        wd[rt] = 0u;
+        pack_code<0>(wd[rt], acc[rt][ct][0] * iv[rt].x);
+        pack_code<1>(wd[rt], acc[rt][ct][1] * iv[rt].y);
+        pack_code<2>(wd[rt], acc[rt][ct][2] * iv[rt].z);
+        pack_code<3>(wd[rt], acc[rt][ct][3] * iv[rt].w);
+      }
+      __builtin_nontemporal_store(vu4{wd[0], wd[1], wd[2], wd[3]},
+                                  reinterpret_cast<vu4 *>(cdst + ct * 1024));
     }
+  }
 }
 
 // ---- a9: split a caller fp32 state (one workgroup per state)
@@ -531,106 +642,104 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
-  __shared__ float sh_norm[D], sh_sig[D], sh_inv[D];
-  __shared__ int sh_sel[D];
-  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
-  floatx4 acc[2][8];
+  const int h = w & 1, ch = w >> 1;
+  __shared__ float sh_part[2 * D], sh_sig[D];
+  __shared__ __attribute__((aligned(16))) float sh_inv[D];
+  __shared__ __attribute__((aligned(16))) int sh_sel[D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[8 * D];
+  floatx4 acc[4][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int row = 32 * w + 16 * rt + 4 * lr + v;
-      const float *src = A.S_in + (s * D + row) * D + 8 * lc;
-      const float4 x0 = ld4(src), x1 = ld4(src + 4);
-      acc[rt][0][v] = x0.x; acc[rt][1][v] = x0.y; acc[rt][2][v] = x0.z; acc[rt][3][v] = x0.w;
-      acc[rt][4][v] = x1.x; acc[rt][5][v] = x1.y; acc[rt][6][v] = x1.z; acc[rt][7][v] = x1.w;
+      const int row = 64 * h + 16 * rt + 4 * lr + v;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        acc[rt][ct][v] = __builtin_nontemporal_load(A.S_in + (s * D + row) * D + 64 * ch + 16 * ct + lc);
     }
-  const SplitLds L{sh_norm, sh_sel, sh_cmx, sh_sig, sh_inv};
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv};
   split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, A.r, A.flags);
 }
 
 // ---- a5-a8: window close, one workgroup per state.
-//   acc  = Gamma (c (a s)) + Gamma comps   (window of <= kChunk records:
-//                                          the MFMAs accumulate onto it)
-//   acc += K_w U                           (v_mfma_f32_16x16x4_f32 over the
-//                                          records, newest chunk first: the
-//                                          decays are running products)
-// with K_w[i][row] = rho_i[row] k~_i[row].  Longer windows start from zero
-// and add the boundary term after the last chunk.  Each record chunk is
-// staged in LDS with 128-bit loads issued by all 256 threads before the
-// first LDS write.
 template <bool KDA>
 __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   const size_t s = blockIdx.x;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;
+  const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
   const int r = A.r, len = A.len, p = A.p;
   const size_t rec0 = s * p;
 
   __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
   __shared__ __attribute__((aligned(16))) float sh_U[kChunk * D];
   __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : kChunk];
-  __shared__ float sh_a[D], sh_gam[D];
+  __shared__ __attribute__((aligned(16))) float sh_a[D];
+  __shared__ __attribute__((aligned(16))) float sh_ag[D];  // a_i * Gamma_i
+  __shared__ float sh_gam[D];
   __shared__ __attribute__((aligned(16))) float sh_s[D];
-  __shared__ int sh_oidx[16];
-  __shared__ float sh_norm[D], sh_sig[D], sh_inv[D];
-  __shared__ int sh_sel[D];
-  __shared__ __attribute__((aligned(16))) float sh_cmx[16 * D];
+  __shared__ __attribute__((aligned(16))) int sh_cslot[D];  // compensator slot of a row or -1
+  __shared__ __attribute__((aligned(16))) float sh_comp[16 * D];  // compensator rows w_c
+  __shared__ float sh_part[2 * D], sh_sig[D];
+  __shared__ __attribute__((aligned(16))) float sh_inv[D];
+  __shared__ __attribute__((aligned(16))) int sh_sel[D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[8 * D];
 
   // boundary-state side data and this lane's code segments, issued first
   if (tid < D) {
     sh_a[tid] = A.row_scale[s * D + tid];
     sh_s[tid] = A.col_scale[s * D + tid];
   }
-  if (tid < r) sh_oidx[tid] = A.comp_idx[s * r + tid];
-  uint2 cw[2][4];
+  if (tid < D) sh_cslot[tid] = -1;
+  const int8_t *csrc = A.codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;
+  uint4 cw[4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 32 * w + 16 * rt + 4 * lr + v;
-      cw[rt][v] = ldu2(A.codes + (s * D + row) * D + 8 * lc);
-    }
+  for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
 
-  floatx4 acc[2][8];
-  // acc += Gamma ((c (a Gamma)) s + compensator rows); Gamma from sh_gam
+  floatx4 acc[4][4];
+  // acc (+)= Gamma ((c (a Gamma)) s + compensator rows); Gamma from sh_gam
   auto add_boundary = [&](bool first) {
-    float sv[8];
+    float sv[4];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) sv[ct] = sh_s[8 * lc + ct];
+    for (int ct = 0; ct < 4; ++ct) sv[ct] = sh_s[col0 + 16 * ct];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 ag4 = *reinterpret_cast<const float4 *>(sh_ag + rbase + 16 * rt);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = 32 * w + 16 * rt + 4 * lr + v;
-        const float G = sh_gam[row];
-        const float aG = sh_a[row] * G;
-        float x[8];
+        const float ag = f4get(ag4, v);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          x[b] = (float)(int8_t)(cw[rt][v].x >> (8 * b)) * (aG * sv[b]);
-          x[4 + b] = (float)(int8_t)(cw[rt][v].y >> (8 * b)) * (aG * sv[4 + b]);
+        for (int ct = 0; ct < 4; ++ct) {
+          const float x = (float)(int8_t)(u4get(cw[ct], rt) >> (8 * v)) * (ag * sv[ct]);
+          acc[rt][ct][v] = first ? x : acc[rt][ct][v] + x;
         }
-        for (int c = 0; c < r; ++c) {
-          if (sh_oidx[c] == row) {
-            const float *wp = A.comp_val + (s * r + c) * D + 8 * lc;
-            const float4 w0 = ld4(wp), w1 = ld4(wp + 4);
-            x[0] = fmaf(G, w0.x, x[0]); x[1] = fmaf(G, w0.y, x[1]);
-            x[2] = fmaf(G, w0.z, x[2]); x[3] = fmaf(G, w0.w, x[3]);
-            x[4] = fmaf(G, w1.x, x[4]); x[5] = fmaf(G, w1.y, x[5]);
-            x[6] = fmaf(G, w1.z, x[6]); x[7] = fmaf(G, w1.w, x[7]);
-          }
-        }
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[rt][ct][v] = first ? x[ct] : acc[rt][ct][v] + x[ct];
       }
+    }
+    // compensator rows: the lanes holding row idx_c add Gamma_idx * w_c
+    // (sh_cslot maps a row to its compensator slot or -1)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int4 cs4 = *reinterpret_cast<const int4 *>(sh_cslot + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = v == 0 ? cs4.x : v == 1 ? cs4.y : v == 2 ? cs4.z : cs4.w;
+        if (c >= 0) {
+          const float G = sh_gam[rbase + 16 * rt + v];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            acc[rt][ct][v] = fmaf(G, sh_comp[c * D + col0 + 16 * ct], acc[rt][ct][v]);
+        }
+      }
+    }
   };
 
   // stage records lo .. hi-1 in LDS (zero-padded to a multiple of 4) and
   // fold the decays into K: sh_K[j] *= P, P *= gate_j, newest first
   float P = 1.f;  // running decay product for row tid (tid < D)
-  auto stage = [&](int lo, int hi) {
+  auto stage = [&](int lo, int hi, bool first) {
     const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
     __syncthreads();
     {
@@ -646,6 +755,11 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       const int nvec = cnt * (D / 4), npad = cnt4 * (D / 4);
       const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
       const int e0 = tid, e1 = tid + 256;
+      // the compensator rows (r * 32 float4) come with the first chunk;
+      // rows 8 .. r-1 (r > 8 only) follow it
+      const int ncv = first ? r * (D / 4) : 0;
+      float4 c0 = z4;
+      if (e0 < ncv) c0 = ld4(A.comp_val + s * r * D + 4 * e0);
       float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
       if (e0 < nvec) {
         u0 = ld4(su + 4 * e0);
@@ -670,6 +784,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
         if (KDA && e1 < nvec) dg[e1] = g1;
       }
       if (!KDA && tid < cnt) sh_g[tid] = gsc;
+      float4 *dc = reinterpret_cast<float4 *>(sh_comp);
+      if (e0 < ncv) dc[e0] = c0;
+      if (e1 < ncv) dc[e1] = ld4(A.comp_val + s * r * D + 4 * e1);
     }
     __syncthreads();
     if (tid < D) {
@@ -684,75 +801,87 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
     const int cnt4 = (cnt + 3) & ~3;
     for (int ks = 0; ks < cnt4 / 4; ++ks) {
       const int kr = 4 * ks + lr;
-      const float a0 = sh_K[kr * D + 32 * w + lc];
-      const float a1 = sh_K[kr * D + 32 * w + 16 + lc];
-      const float4 b0 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc);
-      const float4 b1 = *reinterpret_cast<const float4 *>(sh_U + kr * D + 8 * lc + 4);
-      const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float a[4];
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bb[ct], acc[0][ct], 0, 0, 0);
-        acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bb[ct], acc[1][ct], 0, 0, 0);
-      }
+      for (int rt = 0; rt < 4; ++rt) a[rt] = sh_K[kr * D + 64 * h + 16 * rt + lc];
+      float bb[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bb[ct] = sh_U[kr * D + col0 + 16 * ct];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt], bb[ct], acc[rt][ct], 0, 0, 0);
     }
+  };
+  auto set_gamma = [&]() {
+    if (tid < D) {
+      sh_gam[tid] = P;
+      sh_ag[tid] = sh_a[tid] * P;
+    }
+    if (tid < r) {
+      // comp_idx entries outside [0, dk) are ignored
+      const int idx = A.comp_idx[s * r + tid];
+      if ((unsigned)idx < (unsigned)D) sh_cslot[idx] = tid;
+    }
+    __syncthreads();
   };
 
   if (len <= kChunk) {
     // one chunk: Gamma is known before the contraction, so the boundary
     // term initialises the accumulators
-    stage(0, len);
-    if (tid < D) sh_gam[tid] = P;
-    __syncthreads();
+    stage(0, len, true);
+    set_gamma();
     add_boundary(true);
     contract(len);
   } else {
+    // newest chunk first; the accumulators start at zero after its staging
+    stage(len - kChunk, len, true);
+    __syncthreads();
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int hi = len; hi > 0; hi -= kChunk) {
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    contract(kChunk);
+    for (int hi = len - kChunk; hi > 0; hi -= kChunk) {
       const int lo = hi > kChunk ? hi - kChunk : 0;
-      stage(lo, hi);
+      stage(lo, hi, false);
       __syncthreads();
       contract(hi - lo);
     }
-    if (tid < D) sh_gam[tid] = P;
-    __syncthreads();
+    set_gamma();
     add_boundary(false);
   }
   // every read of this state's compensator rows is done before the split
   // overwrites them
   __syncthreads();
-  const SplitLds L{sh_norm, sh_sel, sh_cmx, sh_sig, sh_inv};
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv};
   split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, r, A.flags);
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: S_out = deQ(codes, a, s) + compensator rows (fp32)
+// Dequantize: S_out = deQ(codes, a, s) + compensator rows (fp32).  Thread
+// (half hh, column j) reads the 64 code bytes of its column segment and
+// writes column j of rows 64hh .. 64hh+63.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
-  const int s = blockIdx.x;
-  const int row = threadIdx.x >> 1, h = threadIdx.x & 1;
-  const float a = A.row_scale[(size_t)s * D + row];
-  const int8_t *cr = A.codes + ((size_t)s * D + row) * D + 64 * h;
-  const float *sc = A.col_scale + (size_t)s * D + 64 * h;
-  float *out = A.S_out + ((size_t)s * D + row) * D + 64 * h;
-  for (int j4 = 0; j4 < 16; ++j4) {
-    const uint32_t cw = *reinterpret_cast<const uint32_t *>(cr + 4 * j4);
-    const float4 s4 = *reinterpret_cast<const float4 *>(sc + 4 * j4);
-    float4 x;
-    x.x = (float)(int8_t)(cw) * a * s4.x;
-    x.y = (float)(int8_t)(cw >> 8) * a * s4.y;
-    x.z = (float)(int8_t)(cw >> 16) * a * s4.z;
-    x.w = (float)(int8_t)(cw >> 24) * a * s4.w;
-    for (int c = 0; c < A.r; ++c) {
-      if (A.comp_idx[(size_t)s * A.r + c] == row) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(
-            A.comp_val + ((size_t)s * A.r + c) * D + 64 * h + 4 * j4);
-        x.x += w4.x; x.y += w4.y; x.z += w4.z; x.w += w4.w;
-      }
+  const size_t s = blockIdx.x;
+  const int j = threadIdx.x & (D - 1), hh = threadIdx.x >> 7;
+  const int r = A.r;
+  const float sj = A.col_scale[s * D + j];
+  const uint4 *src = reinterpret_cast<const uint4 *>(A.codes + s * D * D + hh * 8192 + j * 64);
+  for (int q = 0; q < 4; ++q) {
+    const uint4 cq = src[q];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int slot = 16 * q + e;
+      const int row = 64 * hh + code_slot(slot);  // the slot map is its own inverse
+      const uint32_t wd = u4get(cq, e >> 2);
+      float x = (float)(int8_t)(wd >> (8 * (e & 3))) * A.row_scale[s * D + row] * sj;
+      for (int c = 0; c < r; ++c)
+        if (A.comp_idx[s * r + c] == row) x += A.comp_val[(s * r + c) * D + j];
+      A.S_out[(s * D + row) * D + j] = x;
     }
-    *reinterpret_cast<float4 *>(out + 4 * j4) = x;
   }
 }
 

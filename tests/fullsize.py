@@ -45,21 +45,12 @@ def pick_states(cfg, n_forced, n_free, seed=1234):
     return forced, free
 
 
-def _gather_boundary(slabs, nl, idx):
-    out = {k: [] for k in lq.LeapQuantState.BOUNDARY}
-    for g in idx:
-        l, i = divmod(int(g), nl)
-        for k in out:
-            out[k].append(getattr(slabs[l], k)[i])
-    return {k: torch.stack(v).cpu().numpy() for k, v in out.items()}
+def _gather_boundary(slab, idx):
+    return {k: v.cpu().numpy() for k, v in slab.boundary(idx).items()}
 
 
-def _inject(slabs, nl, idx, b):
-    for j, g in enumerate(idx):
-        l, i = divmod(int(g), nl)
-        for k in lq.LeapQuantState.BOUNDARY:
-            dst = getattr(slabs[l], k)
-            dst[i] = torch.as_tensor(np.ascontiguousarray(b[k][j])).to(device=dst.device, dtype=dst.dtype)
+def _inject(slab, idx, b):
+    slab.load_boundary({k: np.ascontiguousarray(b[k]) for k in lq.LeapQuantState.BOUNDARY}, idx)
 
 
 def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_every=0):
@@ -97,7 +88,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
     outs = [torch.empty((nl, cfg.dv), device=DEV) for _ in range(L)]
     lq.leapquant_quantize_state(slab, S0)
     # boundary 0 of the forced states must already agree bit for bit
-    P.compare_boundary(_gather_boundary(slabs, nl, forced), b_f[0], S0s[:nf], cfg.r,
+    P.compare_boundary(_gather_boundary(slab, forced), b_f[0], S0s[:nf], cfg.r,
                        f"{cfg.name} boundary 0", exact=True)
     rec = torch.empty((T, len(both), cfg.dv), device=DEV)
     loc = [[(j, int(gi) - l * nl) for j, gi in enumerate(both) if int(gi) // nl == l] for l in range(L)]
@@ -111,7 +102,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
         _, _, exact = O.sequential_exact(S0s[nf:], tok_r, gate, keep_every=checkpoint_every)
         deq = torch.empty((nl, cfg.dk, cfg.dv), device=DEV)
     for w in range(T // p):
-        _inject(slabs, nl, forced, b_f[w])
+        _inject(slab, forced, b_f[w])
         for j in range(p):
             t = w * p + j
             for l in range(L):
@@ -126,7 +117,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
         og = to_np(rec[ws])
         P.assert_close(og[:, :nf], o_f[ws], f"{cfg.name} window {w} forced outputs")
         _, _, S_end, _ = O.window(b_f[w], tok_f, w * p, p, gate, cfg.r)
-        s = P.compare_boundary(_gather_boundary(slabs, nl, forced), b_f[w + 1],
+        s = P.compare_boundary(_gather_boundary(slab, forced), b_f[w + 1],
                                S_end.astype(np.float32), cfg.r, f"{cfg.name} boundary {w + 1}")
         for k in ("flips", "codes", "ties"):
             stats[k] += s[k]
@@ -139,7 +130,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
                 rel = np.linalg.norm(ofr[:, diverged] - orr[:, diverged]) / np.linalg.norm(orr[:, diverged])
                 stats["worst_free_rel"] = max(stats["worst_free_rel"], float(rel))
                 assert rel < 2e-2, f"{cfg.name} window {w}: diverged free states differ by {rel}"
-            gb = _gather_boundary(slabs, nl, free)
+            gb = _gather_boundary(slab, free)
             same = np.all(gb["codes"] == b_r[w + 1]["codes"], axis=(1, 2))
             if cfg.r:
                 same &= np.all(gb["comp_idx"] == b_r[w + 1]["comp_idx"], axis=1)
@@ -182,8 +173,9 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
             untouched[torch.as_tensor(forced)] = False
             for l in range(L):
                 keep = untouched[l * nl:(l + 1) * nl].to(DEV)
+                cur = res[l].boundary()
                 for k in lq.LeapQuantState.BOUNDARY:
-                    a_, b_ = getattr(res[l], k)[keep], snaps[nxt][l][k][keep]
+                    a_, b_ = cur[k][keep], snaps[nxt][l][k][keep]
                     assert torch.equal(a_, b_), f"resume from token {mid}: {k} differs at token {nxt}"
             stats["resume"] = (mid, nxt)
     stats["free_diverged"] = int(diverged.sum())

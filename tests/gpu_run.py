@@ -10,21 +10,15 @@ def to_np(x):
 
 
 def boundary_np(state, idx=None):
-    b = {k: to_np(v) for k, v in state.boundary().items()}
-    if idx is not None:
-        b = {k: v[idx] for k, v in b.items()}
-    return b
+    """Boundary state of the slab (or of states idx) as numpy arrays, codes
+    as row-major matrices."""
+    return {k: to_np(v) for k, v in state.boundary(idx).items()}
 
 
 def upload_boundary(state, b, idx=None):
-    """Write boundary arrays (numpy) into the slab, optionally for states idx."""
-    for k in lq.LeapQuantState.BOUNDARY:
-        dst = getattr(state, k)
-        src = torch.as_tensor(np.ascontiguousarray(b[k])).to(device=dst.device, dtype=dst.dtype)
-        if idx is None:
-            dst.copy_(src.reshape(dst.shape))
-        else:
-            dst[torch.as_tensor(idx, device=dst.device)] = src
+    """Write boundary arrays (numpy, codes as row-major matrices) into the
+    slab, optionally for states idx."""
+    state.load_boundary({k: np.ascontiguousarray(b[k]) for k in lq.LeapQuantState.BOUNDARY}, idx)
 
 
 def tokens_np(tok, idx=None, t0=0, t1=None):

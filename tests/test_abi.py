@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.leapquant_abi_version() == 1
+    assert lib.leapquant_abi_version() == 2
     for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
                  L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
         assert lib.leapquant_status_string(code)
