@@ -5,9 +5,11 @@ Workload (default): Gated DeltaNet decode at batch 256 x 32 heads with four
 stacked layers' states resident (32,768 states, 8,192 per layer, dk = dv =
 128), window p = 16, r = 4 compensator rows, 1,024 tokens.  One step is the
 whole decode of that batch: quantize the initial states, then 64 windows of
-(16 tokens x 4 per-layer decode launches + one window close over all four
-layers' states).  Inputs are synthetic
-(seeded generators) and resident in HBM before timing starts.
+16 tokens x 4 per-layer launches.  With --close fused (default) the last
+token of a window is decoded and the layer's window closed in one launch
+(leapquant_decode_close); with --close separate all 16 tokens are decode
+steps and one window close covers all four layers' states.  Inputs are
+synthetic (seeded generators) and resident in HBM before timing starts.
 
 Prints one JSON line (see the fields below).  --gpus > 1 is refused: this
 path runs on one GPU.
@@ -47,7 +49,23 @@ def close_bytes(p, dk, dv, r, kda):
     return 2 * boundary + 4 * p * R
 
 
-def bytes_per_head_token(p, dk, dv, r, kda):
+def fused_bytes(t, dk, dv, r, kda):
+    """Algorithmic HBM bytes of one fused last-token decode and window close
+    for one state: read and write the boundary state, read the t buffered
+    records and the token's inputs, write its output."""
+    G = dk if kda else 1
+    R = G + dk + dv
+    boundary = dk * dv + 4 * (dk + dv) + r * (4 * dv + 4)
+    return 2 * boundary + 4 * t * R + 4 * (2 * dk + dv + 1 + G) + 4 * dv
+
+
+def bytes_per_head_token(p, dk, dv, r, kda, fused=False):
+    """Algorithmic bytes per state and token, the window's work spread over
+    its p tokens: p decode steps and a window close, or p - 1 decode steps
+    and the fused last-token decode and close."""
+    if fused:
+        dec = sum(step_bytes(t, dk, dv, r, kda) for t in range(p - 1))
+        return (dec + fused_bytes(p - 1, dk, dv, r, kda)) / p
     dec = sum(step_bytes(t, dk, dv, r, kda) for t in range(p)) / p
     return dec + close_bytes(p, dk, dv, r, kda) / p
 
@@ -57,18 +75,20 @@ KERNEL_SRC = os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", "lq_kernels
 
 
 def measured_traffic(cfg):
-    """HBM bytes per state (decode, close) from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or (None, None) when the counters were
+    """HBM bytes per state {decode, close, fused} from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary; empty when the counters were
     taken on another workload or on kernel source that has changed since."""
     import hashlib
     if cfg.cid != 2 or not os.path.exists(TRAFFIC_FILE):
-        return None, None
+        return {}
     doc = json.load(open(TRAFFIC_FILE))
     if doc.get("source_sha256") != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
-        return None, None
-    k = doc["kernels"]
-    return (k["decode_step_kernel<GDN>"]["traffic_bytes_per_state"],
-            k["close_kernel<GDN, window close>"]["traffic_bytes_per_state"])
+        return {}
+    names = {"decode_fused": "decode_step_kernel<GDN> (fused schedule)",
+             "decode_separate": "decode_step_kernel<GDN> (separate schedule)",
+             "close": "close_kernel<GDN, window close>", "fused": "close_kernel<GDN, fused decode_close>"}
+    return {key: doc["kernels"][nm]["traffic_bytes_per_state"]
+            for key, nm in names.items() if nm in doc["kernels"]}
 
 
 def parse():
@@ -79,6 +99,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id (default: the batch-256 4-layer workload)")
     ap.add_argument("--tokens", type=int, default=0, help="tokens per step (default: the workload's)")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--close", choices=("fused", "separate"), default="fused",
+                    help="fused: last token decoded and window closed per layer in one launch; "
+                         "separate: p decode steps, then one window close over all layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-states", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -129,37 +152,50 @@ def main():
     def quantize_phase():
         lq.leapquant_quantize_state(slab, S_init)
 
+    fused = args.close == "fused"
+    n_steps = cfg.p - 1 if fused else cfg.p  # decode-step launches per layer and window
+
+    def token_args(t, l):
+        return (sl(tok["q"], t, l), sl(tok["k"], t, l), sl(tok["v"], t, l), sl(tok["beta"], t, l),
+                sl(tok["alpha"], t, l), outs[l])
+
     def decode_phase(w):
-        for j in range(cfg.p):
+        for j in range(n_steps):
             t = w * cfg.p + j
             for l in range(L):
-                lq.leapquant_decode_step(slabs[l], j, sl(tok["q"], t, l), sl(tok["k"], t, l),
-                                         sl(tok["v"], t, l), sl(tok["beta"], t, l),
-                                         sl(tok["alpha"], t, l), outs[l])
+                lq.leapquant_decode_step(slabs[l], j, *token_args(t, l))
 
-    def close_phase():
-        lq.leapquant_window_close(slab, cfg.p)
+    def close_phase(w):
+        if fused:
+            t = w * cfg.p + cfg.p - 1
+            for l in range(L):
+                lq.leapquant_decode_close(slabs[l], cfg.p - 1, *token_args(t, l))
+        else:
+            lq.leapquant_window_close(slab, cfg.p)
 
     if args.mode == "graph":
         stream = torch.cuda.Stream(device=dev)
         # one warm eager pass on the capture stream before capturing
         with torch.cuda.stream(stream):
-            quantize_phase(); decode_phase(0); close_phase()
+            quantize_phase(); decode_phase(0); close_phase(0)
         torch.cuda.synchronize()
         gq = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gq, stream=stream):
             quantize_phase()
-        gd = []
+        gd, gc = [], []
         for w in range(windows):
             gw = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gw, stream=stream):
                 decode_phase(w)
             gd.append(gw)
-        gc = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gc, stream=stream):
-            close_phase()
+            if fused or w == 0:
+                gw = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gw, stream=stream):
+                    close_phase(w)
+                gc.append(gw)
         torch.cuda.synchronize()
-        run_q, run_d, run_c = gq.replay, (lambda w: gd[w].replay()), gc.replay
+        run_q, run_d = gq.replay, (lambda w: gd[w].replay())
+        run_c = (lambda w: gc[w].replay()) if fused else (lambda w: gc[0].replay())
     else:
         stream = torch.cuda.current_stream(dev)
         run_q, run_d, run_c = quantize_phase, decode_phase, close_phase
@@ -175,7 +211,7 @@ def main():
             run_d(w)
             if record:
                 ev[w][1].record(stream)
-            run_c()
+            run_c(w)
             if record:
                 ev[w][2].record(stream)
 
@@ -196,17 +232,24 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     head_tokens = n * T
     value = head_tokens / (wall / args.steps)
-    bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda)
-    n_dec = args.steps * windows * cfg.p * L
+    bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, fused)
+    bpht_unfused = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda)
+    n_dec = args.steps * windows * n_steps * L
     dec_avg_ms = dec_ms / n_dec
-    dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(cfg.p)) / cfg.p
+    dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(n_steps)) / n_steps
     dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    close_avg_ms = close_ms / (args.steps * windows)
-    close_gbs = n * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda) / (close_avg_ms * 1e-3) / 1e9
+    close_launches = L if fused else 1          # per window
+    close_states = nl if fused else n           # per launch
+    close_state_bytes = (fused_bytes(cfg.p - 1, cfg.dk, cfg.dv, cfg.r, kda) if fused
+                         else close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda))
+    close_avg_ms = close_ms / (args.steps * windows * close_launches)
+    close_gbs = close_states * close_state_bytes / (close_avg_ms * 1e-3) / 1e9
     whole_gbs = value * bpht / 1e9
-    dec_traffic, close_traffic = measured_traffic(cfg)
-    dec_traffic = round(dec_traffic * nl) if dec_traffic is not None else None
-    close_traffic = round(close_traffic * n) if close_traffic is not None else None
+    traffic = measured_traffic(cfg)
+    dkey = "decode_fused" if fused else "decode_separate"
+    dec_traffic = round(traffic[dkey] * nl) if dkey in traffic else None
+    ckey = "fused" if fused else "close"
+    close_traffic = round(traffic[ckey] * close_states) if ckey in traffic else None
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
@@ -216,17 +259,20 @@ def main():
         "config": {"workload": cfg.name, "gate": cfg.gate, "batch": cfg.batch, "heads": cfg.heads,
                    "layers": L, "states": n, "dk": cfg.dk, "dv": cfg.dv, "p": cfg.p, "r": cfg.r,
                    "tokens": T, "state_storage": "int8 codes + fp32 scales, fp32 compensators",
-                   "launch": args.mode},
+                   "launch": args.mode, "close": args.close},
         "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": dec_traffic, "bytes_per_launch": round(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
-        "window_close": {"avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
-                         "bytes_per_launch": n * close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda),
-                         "states_per_launch": n,
+        "window_close": {"kernel": "decode_close (fused)" if fused else "window_close",
+                         "avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
+                         "bytes_per_launch": close_states * close_state_bytes,
+                         "states_per_launch": close_states, "launches_per_window": close_launches,
                          "traffic": close_traffic},
         "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
-                       "bytes_per_head_token": round(bpht, 1)},
+                       "bytes_per_head_token": round(bpht, 1),
+                       "unfused_bytes_per_head_token": round(bpht_unfused, 1),
+                       "frac_of_unfused_model": round(value * bpht_unfused / 1e9 / HBM_PEAK_GBS, 4)},
         "hbm_copy_GBs": round(copy_gbs, 1),
     }
 

@@ -150,6 +150,24 @@ int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t,
 int leapquant_window_close(const lq_params *prm, const lq_state *st,
                            int32_t len, hipStream_t stream);
 
+/* Decode token t and close the window in one pass (the fused form of
+ * leapquant_decode_step(t) followed by leapquant_window_close(len = t + 1);
+ * [EL] Figure 2: the state is quantized once per window, at its last
+ * token).  Reads the boundary state and the records 0..t-1, rebuilds
+ * D_t S_{t-1} in fp32, writes o[n][dv] = S_t^T q_t with
+ *   u_t = v_t - S_{t-1}^T b_t,  S_t = D_t S_{t-1} + k~_t u_t^T,
+ * then splits S_t into the new boundary state, overwriting it in place.
+ * Record t is not written to the buffer (the window is closed).  Arguments,
+ * layouts, alignment and aliasing rules are those of leapquant_decode_step;
+ * t is normally p - 1 (t < p - 1 closes a final partial window).  Results
+ * agree with the two-call form to fp32 rounding, not bit for bit: the
+ * fused form reads S_{t-1} from the rebuilt state instead of the windowed
+ * sums. */
+int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t,
+                           const float *q, const float *k, const float *v,
+                           const float *beta, const float *alpha, float *o,
+                           hipStream_t stream);
+
 /* Write the boundary state B = deQ(codes, a, s) + compensator rows as fp32
  * S_out [n][dk][dv] (the state the next window starts from; used for state
  * error tracking and prefix-cache reads).  S_out must not overlap `st`. */

@@ -8,14 +8,14 @@ torch device tensors and streams into the C calls and runs nothing itself.
 """
 from ._lib import (LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_SMOOTH, LeapQuantError, LIB_PATH, load)
 from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matrix,
-                  leapquant_abi_version, leapquant_decode_step,
+                  leapquant_abi_version, leapquant_decode_close, leapquant_decode_step,
                   leapquant_dequantize_state, leapquant_quantize_state,
                   leapquant_status_string, leapquant_window_close)
 
 __all__ = [
     "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_SMOOTH", "LeapQuantError", "LIB_PATH", "load",
     "LeapQuantState", "code_offsets", "codes_from_matrix", "codes_to_matrix",
-    "leapquant_abi_version", "leapquant_decode_step",
+    "leapquant_abi_version", "leapquant_decode_close", "leapquant_decode_step",
     "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",
     "leapquant_window_close",
 ]

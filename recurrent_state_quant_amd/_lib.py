@@ -24,6 +24,7 @@ EXPORTED = (
     "leapquant_quantize_state",
     "leapquant_decode_step",
     "leapquant_window_close",
+    "leapquant_decode_close",
     "leapquant_dequantize_state",
     "leapquant_status_string",
     "leapquant_abi_version",
@@ -65,9 +66,10 @@ def load():
     lib.leapquant_quantize_state.argtypes = [P, vp, S, vp]
     lib.leapquant_decode_step.argtypes = [P, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_window_close.argtypes = [P, S, i32, vp]
+    lib.leapquant_decode_close.argtypes = [P, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
-              "leapquant_dequantize_state"):
+              "leapquant_decode_close", "leapquant_dequantize_state"):
         getattr(lib, f).restype = ctypes.c_int
     lib.leapquant_status_string.argtypes = [ctypes.c_int]
     lib.leapquant_status_string.restype = ctypes.c_char_p

@@ -174,14 +174,25 @@ def leapquant_quantize_state(state, S, stream=None):
 
 
 def leapquant_decode_step(state, t, q, k, v, beta, alpha, o, stream=None):
-    n, dk, dv = state.n, state.dk, state.dv
-    ashape = (n,) if state.gate == L.LQ_GATE_GDN else (n, dk)
-    args = [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
-            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
-            _ptr(o, _F32, (n, dv), "o")]
+    args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
     L.check(L.load().leapquant_decode_step(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
                                            _stream(stream, state.device)))
+
+
+def _token_args(state, q, k, v, beta, alpha, o):
+    n, dk, dv = state.n, state.dk, state.dv
+    ashape = (n,) if state.gate == L.LQ_GATE_GDN else (n, dk)
+    return [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
+            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
+            _ptr(o, _F32, (n, dv), "o")]
+
+
+def leapquant_decode_close(state, t, q, k, v, beta, alpha, o, stream=None):
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_decode_close(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
+                                            _stream(stream, state.device)))
 
 
 def leapquant_window_close(state, length, stream=None):

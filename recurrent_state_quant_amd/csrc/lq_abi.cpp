@@ -101,9 +101,15 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
   return hip_status(lq::launch_quantize_state(a, stream));
 }
 
-int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
-                          const float *k, const float *v, const float *beta, const float *alpha,
-                          float *o, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two token entry points: parameters, state, t, the
+// token inputs, and that o overlaps no input or state array.
+int check_token_call(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
+                     const float *k, const float *v, const float *beta, const float *alpha,
+                     const float *o) {
   int rc = check_params(prm);
   if (rc) return rc;
   if ((rc = check_boundary(prm, st))) return rc;
@@ -129,6 +135,19 @@ int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, c
       (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
                       overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
     return LQ_ERR_ALIAS;
+  return LQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
+                          const float *k, const float *v, const float *beta, const float *alpha,
+                          float *o, hipStream_t stream) {
+  const int rc = check_token_call(prm, st, t, q, k, v, beta, alpha, o);
+  if (rc) return rc;
+  const bool kda = prm->gate == LQ_GATE_KDA;
   lq::DecodeArgs a{};
   a.codes = st->codes;
   a.row_scale = st->row_scale;
@@ -174,6 +193,35 @@ int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len
   a.len = len;
   a.flags = prm->flags;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
+}
+
+int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
+                           const float *k, const float *v, const float *beta, const float *alpha,
+                           float *o, hipStream_t stream) {
+  const int rc = check_token_call(prm, st, t, q, k, v, beta, alpha, o);
+  if (rc) return rc;
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.S_in = nullptr;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.len = t;
+  a.flags = prm->flags;
+  return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st, float *S_out,

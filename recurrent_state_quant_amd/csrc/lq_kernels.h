@@ -34,7 +34,10 @@ struct CloseArgs {
   const float *buf_k;
   const float *buf_u;
   const float *S_in;  // quantize_state source; nullptr for a window close
-  int n, p, r, len;
+  // decode_close only: the last token's inputs and output
+  const float *q, *k, *v, *beta, *alpha;
+  float *o;
+  int n, p, r, len;  // len: buffered records the rebuild replays
   unsigned flags;
 };
 
@@ -50,6 +53,7 @@ struct DequantArgs {
 
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t stream);
 

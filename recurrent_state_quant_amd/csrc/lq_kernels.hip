@@ -661,8 +661,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
   split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, A.r, A.flags);
 }
 
-// ---- a5-a8: window close, one workgroup per state.
-template <bool KDA>
+// ---- a5-a8: window close, one workgroup per state.  With FUSED the
+// workgroup first decodes the window's last token t from the rebuilt fp32
+// state: the decay chain starts at alpha_t, so the accumulators hold
+// D_t S_{t-1}; then z = (D_t S_{t-1})^T k_t = S_{t-1}^T b_t and
+// (D_t S_{t-1})^T q_t = S_{t-1}^T (alpha_t q_t), u_t = v_t - z_b,
+// o_t = z_q + (k~_t . q_t) u_t, and S_t = D_t S_{t-1} + k~_t u_t^T is split.
+template <bool KDA, bool FUSED>
 __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   const size_t s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -683,6 +688,10 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   __shared__ __attribute__((aligned(16))) float sh_s[D];
   __shared__ __attribute__((aligned(16))) int sh_cslot[D];  // compensator slot of a row or -1
   __shared__ __attribute__((aligned(16))) float sh_comp[16 * D];  // compensator rows w_c
+  // FUSED: the last token's k, q, k~ per row, u per column, k~ . q per wave
+  __shared__ __attribute__((aligned(16))) float sh_tk[FUSED ? D : 4], sh_tq[FUSED ? D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_tkt[FUSED ? D : 4], sh_tu[FUSED ? D : 4];
+  __shared__ float sh_kq[2];
   __shared__ float sh_part[2 * D], sh_sig[D];
   __shared__ __attribute__((aligned(16))) float sh_inv[D];
   __shared__ __attribute__((aligned(16))) int sh_sel[D];
@@ -737,7 +746,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   };
 
   // stage records lo .. hi-1 in LDS (zero-padded to a multiple of 4) and
-  // fold the decays into K: sh_K[j] *= P, P *= gate_j, newest first
+  // fold the decays into K: sh_K[j] *= P, P *= gate_j, newest first.
+  // FUSED: the first call also stages the last token's k, q, k~ (rows) and
+  // v (columns), and starts the decay chain at alpha_t.
   float P = 1.f;  // running decay product for row tid (tid < D)
   auto stage = [&](int lo, int hi, bool first) {
     const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
@@ -760,6 +771,14 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       const int ncv = first ? r * (D / 4) : 0;
       float4 c0 = z4;
       if (e0 < ncv) c0 = ld4(A.comp_val + s * r * D + 4 * e0);
+      float tk = 0.f, tq = 0.f, tv = 0.f, tb = 0.f;
+      if (FUSED && first && tid < D) {
+        tk = A.k[s * D + tid];
+        tq = A.q[s * D + tid];
+        tv = A.v[s * D + tid];
+        tb = A.beta[s];
+        P = KDA ? A.alpha[s * D + tid] : A.alpha[s];
+      }
       float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
       if (e0 < nvec) {
         u0 = ld4(su + 4 * e0);
@@ -787,6 +806,12 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       float4 *dc = reinterpret_cast<float4 *>(sh_comp);
       if (e0 < ncv) dc[e0] = c0;
       if (e1 < ncv) dc[e1] = ld4(A.comp_val + s * r * D + 4 * e1);
+      if (FUSED && first && tid < D) {
+        sh_tk[tid] = tk;
+        sh_tq[tid] = tq;
+        sh_tkt[tid] = tb * tk;
+        sh_tu[tid] = tv;  // v_t; replaced by u_t after the decode
+      }
     }
     __syncthreads();
     if (tid < D) {
@@ -824,6 +849,10 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       const int idx = A.comp_idx[s * r + tid];
       if ((unsigned)idx < (unsigned)D) sh_cslot[idx] = tid;
     }
+    if (FUSED && tid < D) {
+      const float kq = wave_sum(sh_tkt[tid] * sh_tq[tid]);  // waves 0 and 1, all lanes active
+      if (lane == 0) sh_kq[w] = kq;
+    }
     __syncthreads();
   };
 
@@ -851,6 +880,53 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
     }
     set_gamma();
     add_boundary(false);
+  }
+  if (FUSED) {
+    // z = acc^T k_t and acc^T q_t: each lane sums its 16 rows for its 4
+    // columns; the 8 (row half, lane group) partials meet in LDS
+    float zb[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(sh_tk + rbase + 16 * rt);
+      const float4 q4 = *reinterpret_cast<const float4 *>(sh_tq + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          zb[ct] = fmaf(acc[rt][ct][v], f4get(k4, v), zb[ct]);
+          zq[ct] = fmaf(acc[rt][ct][v], f4get(q4, v), zq[ct]);
+        }
+    }
+    __syncthreads();  // every wave is done with sh_K
+    float2 *zp = reinterpret_cast<float2 *>(sh_K);  // [8][D]
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) zp[(4 * h + lr) * D + col0 + 16 * ct] = make_float2(zb[ct], zq[ct]);
+    __syncthreads();
+    if (tid < D) {
+      float b = 0.f, q = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float2 x = zp[g * D + tid];
+        b += x.x;
+        q += x.y;
+      }
+      const float u = sh_tu[tid] - b;
+      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + tid);
+      sh_tu[tid] = u;
+    }
+    __syncthreads();
+    // S_t = D_t S_{t-1} + k~_t u_t^T
+    float uu[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) uu[ct] = sh_tu[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 kt4 = *reinterpret_cast<const float4 *>(sh_tkt + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(f4get(kt4, v), uu[ct], acc[rt][ct][v]);
+    }
   }
   // every read of this state's compensator rows is done before the split
   // overwrites them
@@ -898,9 +974,17 @@ hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream)
 
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream) {
   if (kda)
-    hipLaunchKernelGGL(close_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<true, false>), dim3(a.n), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(close_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<false, false>), dim3(a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  if (kda)
+    hipLaunchKernelGGL((close_kernel<true, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((close_kernel<false, true>), dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

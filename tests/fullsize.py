@@ -10,8 +10,10 @@ Two disjoint samples of states are followed:
     rounding-boundary flip makes the two trajectories part, then by a
     relative bound.
 All other states run alongside in the same launches (the benchmark's launch
-configuration: one decode launch per layer and token, one window close over
-all layers' states per window).
+configuration: one decode launch per layer and token; either one window
+close over all layers' states per window, or, with fused=True, the last
+token of each window decoded and the window closed per layer in one
+leapquant_decode_close launch).
 """
 import numpy as np
 import torch
@@ -53,7 +55,26 @@ def _inject(slab, idx, b):
     slab.load_boundary({k: np.ascontiguousarray(b[k]) for k in lq.LeapQuantState.BOUNDARY}, idx)
 
 
-def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_every=0):
+def _decode_window(slab, slabs, tok, w, p, nl, L, outs, fused, after_token=None):
+    """One window of every layer: p - 1 decode steps and a fused last token
+    per layer, or p decode steps and one close over the whole slab."""
+    for j in range(p):
+        t = w * p + j
+        for l in range(L):
+            sl = slice(l * nl, (l + 1) * nl)
+            args = (tok["q"][t, sl], tok["k"][t, sl], tok["v"][t, sl], tok["beta"][t, sl],
+                    tok["alpha"][t, sl], outs[l])
+            if fused and j == p - 1:
+                lq.leapquant_decode_close(slabs[l], j, *args)
+            else:
+                lq.leapquant_decode_step(slabs[l], j, *args)
+            if after_token is not None:
+                after_token(t, l)
+    if not fused:
+        lq.leapquant_window_close(slab, p)
+
+
+def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_every=0, fused=False):
     """Run the workload and compare.  With checkpoint_every > 0 (a multiple
     of p) the whole boundary state is snapshotted at every checkpoint (the
     prefix-cache shape), the state MSE of the free states against the exact
@@ -77,7 +98,8 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
     nf = len(forced)
     tok_f = {k: v[:, :nf] for k, v in toks.items()}
     tok_r = {k: v[:, nf:] for k, v in toks.items()}
-    log(f"[fullsize {cfg.name}] oracle: {nf} forced + {len(free)} free states x {T} tokens")
+    log(f"[fullsize {cfg.name}] oracle: {nf} forced + {len(free)} free states x {T} tokens"
+        f" ({'fused last token' if fused else 'separate close'})")
     o_f, b_f = O.run_windowed(S0s[:nf], tok_f, p, cfg.r, gate)
     o_r, b_r = O.run_windowed(S0s[nf:], tok_r, p, cfg.r, gate) if len(free) else (None, None)
 
@@ -101,18 +123,14 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
         assert checkpoint_every % p == 0 and len(free)
         _, _, exact = O.sequential_exact(S0s[nf:], tok_r, gate, keep_every=checkpoint_every)
         deq = torch.empty((nl, cfg.dk, cfg.dv), device=DEV)
+    def gather_outputs(t, l):
+        dst, src = loc_t[l]
+        if len(dst):
+            rec[t].index_copy_(0, dst, outs[l].index_select(0, src))
+
     for w in range(T // p):
         _inject(slab, forced, b_f[w])
-        for j in range(p):
-            t = w * p + j
-            for l in range(L):
-                sl = slice(l * nl, (l + 1) * nl)
-                lq.leapquant_decode_step(slabs[l], j, tok["q"][t, sl], tok["k"][t, sl], tok["v"][t, sl],
-                                         tok["beta"][t, sl], tok["alpha"][t, sl], outs[l])
-                dst, src = loc_t[l]
-                if len(dst):
-                    rec[t].index_copy_(0, dst, outs[l].index_select(0, src))
-        lq.leapquant_window_close(slab, p)
+        _decode_window(slab, slabs, tok, w, p, nl, L, outs, fused, gather_outputs)
         ws = slice(w * p, (w + 1) * p)
         og = to_np(rec[ws])
         P.assert_close(og[:, :nf], o_f[ws], f"{cfg.name} window {w} forced outputs")
@@ -160,13 +178,7 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
             for l in range(L):
                 res[l].load_boundary(snaps[mid][l])
             for w in range(mid // p, nxt // p):
-                for j in range(p):
-                    t = w * p + j
-                    for l in range(L):
-                        sl = slice(l * nl, (l + 1) * nl)
-                        lq.leapquant_decode_step(res[l], j, tok["q"][t, sl], tok["k"][t, sl], tok["v"][t, sl],
-                                                 tok["beta"][t, sl], tok["alpha"][t, sl], outs[l])
-                lq.leapquant_window_close(rslab, p)
+                _decode_window(rslab, res, tok, w, p, nl, L, outs, fused)
             # forced states were overwritten by injection in the original run:
             # compare the states that ran untouched
             untouched = torch.ones(cfg.n_states, dtype=torch.bool)

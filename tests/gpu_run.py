@@ -32,14 +32,20 @@ def tokens_np(tok, idx=None, t0=0, t1=None):
     return out
 
 
-def run_window(state, tok, t0, length, out, close=True, lo=0, hi=None):
+def run_window(state, tok, t0, length, out, close=True, lo=0, hi=None, fused=False):
     """Decode tokens t0 .. t0+length-1 of `tok` (device tensors [T, n_total,
     ...]) for the slab's states lo .. hi-1 of the token arrays, writing o into
-    out[t] [n_total, dv] (same state range), then close the window."""
+    out[t] [n_total, dv] (same state range), then close the window; with
+    fused=True the last token is decoded and the window closed in one call
+    (leapquant_decode_close)."""
     hi = lo + state.n if hi is None else hi
     for j in range(length):
         t = t0 + j
-        lq.leapquant_decode_step(state, j, tok["q"][t, lo:hi], tok["k"][t, lo:hi], tok["v"][t, lo:hi],
-                                 tok["beta"][t, lo:hi], tok["alpha"][t, lo:hi], out[t, lo:hi])
+        args = (tok["q"][t, lo:hi], tok["k"][t, lo:hi], tok["v"][t, lo:hi],
+                tok["beta"][t, lo:hi], tok["alpha"][t, lo:hi], out[t, lo:hi])
+        if fused and close and j == length - 1:
+            lq.leapquant_decode_close(state, j, *args)
+            return
+        lq.leapquant_decode_step(state, j, *args)
     if close:
         lq.leapquant_window_close(state, length)

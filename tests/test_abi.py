@@ -61,15 +61,27 @@ def _state(**kw):
     return L.LqState(*[addrs[f] for f, _ in L.LqState._fields_]), base
 
 
+# both token entry points validate the same way
+TOKEN_ENTRIES = ("leapquant_decode_step", "leapquant_decode_close")
+_ENTRY = {"name": TOKEN_ENTRIES[0]}
+
+
+@pytest.fixture(params=TOKEN_ENTRIES)
+def entry(request):
+    _ENTRY["name"] = request.param
+    yield request.param
+    _ENTRY["name"] = TOKEN_ENTRIES[0]
+
+
 def _decode(lib, prm, st, t=0, **kw):
     _, base = _state()
     vec = 4 * 512
     a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
              o=base + 4 * vec)
     a.update(kw)
-    return lib.leapquant_decode_step(ctypes.byref(prm) if prm is not None else None,
-                                     ctypes.byref(st) if st is not None else None, t,
-                                     a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["o"], None)
+    return getattr(lib, _ENTRY["name"])(ctypes.byref(prm) if prm is not None else None,
+                                        ctypes.byref(st) if st is not None else None, t,
+                                        a["q"], a["k"], a["v"], a["beta"], a["alpha"], a["o"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -78,7 +90,7 @@ def _decode(lib, prm, st, t=0, **kw):
     (dict(r=-1), L.LQ_ERR_SHAPE), (dict(r=17), L.LQ_ERR_SHAPE), (dict(gate=2), L.LQ_ERR_SHAPE),
     (dict(flags=2), L.LQ_ERR_SHAPE),
 ])
-def test_bad_params(lib, kw, code):
+def test_bad_params(lib, entry, kw, code):
     st, _ = _state()
     prm = _params(**kw)
     assert _decode(lib, prm, st) == code
@@ -87,7 +99,7 @@ def test_bad_params(lib, kw, code):
     assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), FAKE + (1 << 36), None) == code
 
 
-def test_null_pointers(lib):
+def test_null_pointers(lib, entry):
     st, _ = _state()
     prm = _params()
     assert _decode(lib, None, st) == L.LQ_ERR_NULL
@@ -104,7 +116,7 @@ def test_null_pointers(lib):
     assert lib.leapquant_window_close(ctypes.byref(_params(r=0)), ctypes.byref(nobuf), 16, None) == L.LQ_ERR_NULL
 
 
-def test_misaligned(lib):
+def test_misaligned(lib, entry):
     prm = _params()
     for f in ("codes", "row_scale", "col_scale", "comp_val", "buf_k", "buf_u"):
         st, _ = _state()
@@ -125,7 +137,7 @@ def test_misaligned(lib):
     assert lib.leapquant_quantize_state(ctypes.byref(prm), FAKE + (1 << 36) + 8, ctypes.byref(_state()[0]), None) == L.LQ_ERR_ALIGN
 
 
-def test_window_position_ranges(lib):
+def test_window_position_ranges(lib, entry):
     st, _ = _state()
     prm = _params()
     assert _decode(lib, prm, st, t=-1) == L.LQ_ERR_SHAPE
@@ -134,7 +146,7 @@ def test_window_position_ranges(lib):
     assert lib.leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), 17, None) == L.LQ_ERR_SHAPE
 
 
-def test_aliasing_rejected(lib):
+def test_aliasing_rejected(lib, entry):
     st, base = _state()
     prm = _params()
     assert _decode(lib, prm, st, o=base) == L.LQ_ERR_ALIAS            # o == q

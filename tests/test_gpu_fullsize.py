@@ -20,7 +20,15 @@ def _free_memory():
 
 def test_fullsize_b256_4layers():
     """Batch 256 x 32 heads x 4 layers (32,768 states), 1,024 tokens: the
-    benchmarked workload."""
+    benchmarked workload, in the benchmark's default schedule (last token of
+    each window fused with the close)."""
+    s = fullsize.run(CONFIGS[2], n_forced=12, n_free=8, fused=True)
+    assert s["flips"] <= 1e-3 * s["codes"]
+
+
+def test_fullsize_b256_4layers_separate_close():
+    """The benchmarked workload with p decode steps and one window close
+    over all layers per window (bench.py --close separate)."""
     s = fullsize.run(CONFIGS[2], n_forced=12, n_free=8)
     assert s["flips"] <= 1e-3 * s["codes"]
 
@@ -31,7 +39,7 @@ def test_fullsize_gdn_layer_b64():
 
 
 def test_fullsize_kda_b128():
-    s = fullsize.run(CONFIGS[3], n_forced=8, n_free=8)
+    s = fullsize.run(CONFIGS[3], n_forced=8, n_free=8, fused=True)
     assert s["flips"] <= 1e-3 * s["codes"]
 
 

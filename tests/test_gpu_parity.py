@@ -182,6 +182,36 @@ def test_window_close_entry(gate, p, length, r, flags):
 
 
 # ---------------------------------------------------------------------------
+# a1-a8 fused: decode the window's last token and close the window
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("p,t", [(1, 0), (16, 0), (16, 7), (16, 15), (32, 31), (64, 40), (64, 63)])
+@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (16, 0), (4, lq.LQ_NO_SMOOTH)])
+def test_decode_close_entry(gate, p, t, r, flags):
+    rng = np.random.default_rng(5000 + 100 * p + t + 7 * r + flags + (gate == "kda"))
+    n = 19
+    b, recs = _random_window_inputs(rng, n, p, t, gate, r)
+    st = lq.LeapQuantState(n, p, r, gate, DEV, flags)
+    upload_boundary(st, b)
+    _upload_records(st, recs, gate)
+    tok = _token(rng, n, gate)
+    o = torch.empty((n, 128), device=DEV)
+    lq.leapquant_decode_close(st, t, _dev(tok["q"]), _dev(tok["k"]), _dev(tok["v"]), _dev(tok["beta"]),
+                              _dev(tok["alpha"]), o)
+    torch.cuda.synchronize()
+    S_prev = O.replay(O.dequantize(b), _oracle_records(recs, gate))
+    t64 = {k: v.astype(np.float64) for k, v in tok.items()}
+    o_ref, S_t, _ = O.step(S_prev, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate))
+    P.assert_close(to_np(o), o_ref, "o_t")
+    ref = O.quantize(S_t, r, flags)
+    P.compare_boundary(boundary_np(st), ref, S_t.astype(np.float32), r, "decode_close")
+    # the buffer is read, never written
+    for i, (a, ktr, ur) in enumerate(recs):
+        np.testing.assert_array_equal(to_np(st.buf_u[:, i]), ur)
+    assert not to_np(st.buf_u[:, t]).any() and not to_np(st.buf_k[:, t]).any()
+
+
+# ---------------------------------------------------------------------------
 # Whole windows: the GPU starts each window from the oracle's boundary
 # ---------------------------------------------------------------------------
 def _workload(cid, n, steps, device="cpu", seed=None):
@@ -192,8 +222,9 @@ def _workload(cid, n, steps, device="cpu", seed=None):
     return cfg, S0, tok
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 24, 128), (3, 24, 128)])
-def test_oracle_forced_windows(cid, n, steps):
+def test_oracle_forced_windows(cid, n, steps, fused):
     cfg, S0, tok = _workload(cid, n, steps)
     S0n = S0.numpy()
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
@@ -204,7 +235,7 @@ def test_oracle_forced_windows(cid, n, steps):
     total = {"flips": 0, "codes": 0, "ties": 0}
     for w in range(steps // cfg.p):
         upload_boundary(st, bounds[w])
-        run_window(st, tokd, w * cfg.p, cfg.p, out)
+        run_window(st, tokd, w * cfg.p, cfg.p, out, fused=fused)
         torch.cuda.synchronize()
         sl = slice(w * cfg.p, (w + 1) * cfg.p)
         P.assert_close(to_np(out[sl]), o_ref[sl], f"cfg{cid} window {w} outputs")
@@ -219,8 +250,9 @@ def test_oracle_forced_windows(cid, n, steps):
 # ---------------------------------------------------------------------------
 # Free-running: strict until the first legitimate rounding-boundary flip
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 16, 256), (3, 16, 256)])
-def test_free_running(cid, n, steps):
+def test_free_running(cid, n, steps, fused):
     cfg, S0, tok = _workload(cid, n, steps)
     S0n = S0.numpy()
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
@@ -232,7 +264,7 @@ def test_free_running(cid, n, steps):
     diverged = np.zeros(n, bool)
     worst_rel = 0.0
     for w in range(steps // cfg.p):
-        run_window(st, tokd, w * cfg.p, cfg.p, out)
+        run_window(st, tokd, w * cfg.p, cfg.p, out, fused=fused)
         torch.cuda.synchronize()
         sl = slice(w * cfg.p, (w + 1) * cfg.p)
         og, orf = to_np(out[sl]), o_ref[sl]
