@@ -102,6 +102,11 @@ def parse():
     ap.add_argument("--close", choices=("fused", "separate"), default="fused",
                     help="fused: last token decoded and window closed per layer in one launch; "
                          "separate: p decode steps, then one window close over all layers")
+    ap.add_argument("--ablations", action="store_true",
+                    help="instead of the headline line, print one line with the kernel-throughput "
+                         "analogues of the pages' Table 2 (per-step fp32 / bf16 / int8 baselines, "
+                         "per-window, compensators) and Table 3 (window length p) on this workload")
+    ap.add_argument("--ablation-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-states", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -125,6 +130,9 @@ def main():
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.ablations:
+        print(json.dumps(ablations(args, cfg, dev)), flush=True)
+        return
     kda = cfg.gate == "kda"
     T = args.tokens or cfg.steps
     assert T % cfg.p == 0
@@ -279,6 +287,107 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, S_init, tok)
     print(json.dumps(result), flush=True)
+
+
+def dense_bytes(dk, dv, kda, elem):
+    """Algorithmic bytes of one dense-state token for one state: read and
+    write the state, read the token's inputs, write its output."""
+    G = dk if kda else 1
+    return 2 * elem * dk * dv + 4 * (2 * dk + dv + 1 + G) + 4 * dv
+
+
+def ablations(args, cfg, dev, reps=3):
+    """Kernel-level analogues of the pages' Table 2 and Table 3 on this
+    workload's shape: head-tokens/s of each variant (all layers' states
+    resident, one launch per layer and token, launches replayed from one
+    graph per variant), and the ratio to the fp32 per-step baseline."""
+    import torch
+    import recurrent_state_quant_amd as lq
+    from workloads import generators as G
+    T = args.ablation_tokens
+    L, nl, n = cfg.layers, cfg.states_per_layer, cfg.n_states
+    kda = cfg.gate == "kda"
+    g = G.make_generator(cfg.seed, dev)
+    S_init = G.initial_state(cfg, n, g, dev)
+    tok = G.token_inputs(cfg, n, T, g, dev)
+    outs = [torch.empty((nl, cfg.dv), device=dev) for _ in range(L)]
+
+    def targs(t, l):
+        sl = slice(l * nl, (l + 1) * nl)
+        return (tok["q"][t, sl], tok["k"][t, sl], tok["v"][t, sl], tok["beta"][t, sl],
+                tok["alpha"][t, sl], outs[l])
+
+    def timed(run):
+        stream = torch.cuda.Stream(device=dev)
+        with torch.cuda.stream(stream):
+            run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        return n * T * reps / (time.perf_counter() - t0)
+
+    def dense(dtype):
+        S = S_init.clone() if dtype == torch.float32 else S_init.to(dtype)
+        views = [S[l * nl:(l + 1) * nl] for l in range(L)]
+
+        def run():
+            for t in range(T):
+                for l in range(L):
+                    lq.leapquant_dense_step(views[l], cfg.gate, *targs(t, l))
+        value = timed(run)
+        del S, views
+        return value, dense_bytes(cfg.dk, cfg.dv, kda, 4 if dtype == torch.float32 else 2)
+
+    def windowed(p, r, flags):
+        slab = lq.LeapQuantState(n, p, r, cfg.gate, dev, flags)
+        lq.leapquant_quantize_state(slab, S_init)
+        views = [slab.view(l * nl, nl) for l in range(L)]
+
+        def run():
+            for t in range(T):
+                j = t % p
+                for l in range(L):
+                    if j == p - 1:
+                        lq.leapquant_decode_close(views[l], j, *targs(t, l))
+                    else:
+                        lq.leapquant_decode_step(views[l], j, *targs(t, l))
+        value = timed(run)
+        del slab, views
+        return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
+
+    rows2 = [("FP32 per-step", lambda: dense(torch.float32)),
+             ("BF16 per-step", lambda: dense(torch.bfloat16)),
+             ("INT8 per-step", lambda: windowed(1, 0, 1)),
+             ("+ Per-window (p = 16)", lambda: windowed(16, 0, 1)),
+             ("+ Comp. Tokens (r = 4) and smoothing", lambda: windowed(16, cfg.r, 0))]
+    rows3 = [(f"p = {p}", (lambda p=p: windowed(p, cfg.r, 0))) for p in (4, 8, 16, 32)]
+
+    def table(rows, ref):
+        out = []
+        for name, fn in rows:
+            value, bpht = fn()
+            out.append({"row": name, "head_tokens_per_s": round(value, 1),
+                        "kernel_speedup": round(value / ref, 3) if ref else 1.0,
+                        "bytes_per_head_token": round(bpht, 1),
+                        "hbm_frac": round(value * bpht / 1e9 / HBM_PEAK_GBS, 4)})
+            if ref is None:
+                ref = value
+        return out, ref
+
+    t2, ref = table(rows2, None)
+    t3, _ = table(rows3, ref)
+    return {"metric": "kernel throughput ablations (head-tokens/s; speedup over fp32 per-step)",
+            "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph",
+            "schedule": "one launch per layer and token; last token of each window fused with its close",
+            "table2": t2, "table3_r": cfg.r, "table3": t3}
 
 
 def copy_calibration(dev, nbytes=1 << 31, reps=5):

@@ -174,6 +174,28 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t,
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st,
                                float *S_out, hipStream_t stream);
 
+/* ---- Uncompressed baselines ([EL] Table 2, rows "FP32 per-step" and
+ * "BF16 per-step"): the same token update on a dense state that is read
+ * and written in full every token.  Provided to measure the quantized path
+ * against in the same harness; not part of the quantized decode. */
+typedef enum lq_dense_dtype {
+  LQ_DENSE_FP32 = 0, /* S is float [n][dk][dv]                            */
+  LQ_DENSE_BF16 = 1  /* S is bfloat16 (uint16 bit patterns) [n][dk][dv];
+                        computed in fp32, stored rounded to nearest even   */
+} lq_dense_dtype;
+
+/* One token for n dense states, in place: u_t = v_t - S^T b_t,
+ * S <- D_t S + k~_t u_t^T, o[n][dv] = S^T q_t (the recurrence of [EL]
+ * Table 4 with no quantization).  prm supplies n, dk, dv and gate (p, r
+ * and flags must be valid but are not used).  S is row-major (row = key
+ * channel), 16-byte aligned (fp32) or 8-byte aligned (bf16); the token
+ * inputs follow leapquant_decode_step.  S and o must not overlap each other
+ * or any input. */
+int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype,
+                         const float *q, const float *k, const float *v,
+                         const float *beta, const float *alpha, float *o,
+                         hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *leapquant_status_string(int status);
 

@@ -291,6 +291,26 @@ def run_per_token(S_init, tokens, r, gate, flags=0):
     return np.stack(outs), b
 
 
+def round_bf16(x):
+    """Round to bfloat16 (8 significant bits), to nearest with ties to even,
+    through the fp32 value: the storage of the dense "BF16 per-step" state of
+    [EL] Table 2.  Returns fp64 arrays holding bf16-representable values."""
+    f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32))
+    bits = f.view(np.uint32).astype(np.uint64)
+    upper, lower = bits >> 16, bits & 0xFFFF
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    out = ((upper + up) << 16).astype(np.uint32).view(np.float32)
+    return out.astype(np.float64)
+
+
+def step_dense_bf16(S, q, k, v, beta, alpha, gate):
+    """One token of the "BF16 per-step" baseline of [EL] Table 2: the exact
+    update of a bf16 state, the new state rounded to bf16.  Returns (o, S_new)
+    with o read from the updated state before rounding."""
+    o, S_new, _ = step(S, q, k, v, beta, alpha, gate)
+    return o, round_bf16(S_new)
+
+
 def state_mse(boundary, S_exact):
     """mean((B - S_exact)^2) per state, B the dequantized boundary state."""
     B = dequantize(boundary)

@@ -6,16 +6,20 @@ smoothing, as hand-written HIP kernels behind the C ABI of
 include/leapquant.h.  This package is the thin Python binding: it marshals
 torch device tensors and streams into the C calls and runs nothing itself.
 """
-from ._lib import (LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_SMOOTH, LeapQuantError, LIB_PATH, load)
+from ._lib import (LQ_DENSE_BF16, LQ_DENSE_FP32, LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_SMOOTH,
+                   LeapQuantError, LIB_PATH, load)
 from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matrix,
                   leapquant_abi_version, leapquant_decode_close, leapquant_decode_step,
+                  leapquant_dense_step,
                   leapquant_dequantize_state, leapquant_quantize_state,
                   leapquant_status_string, leapquant_window_close)
 
 __all__ = [
-    "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_SMOOTH", "LeapQuantError", "LIB_PATH", "load",
+    "LQ_DENSE_BF16", "LQ_DENSE_FP32", "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_SMOOTH",
+    "LeapQuantError", "LIB_PATH", "load",
     "LeapQuantState", "code_offsets", "codes_from_matrix", "codes_to_matrix",
     "leapquant_abi_version", "leapquant_decode_close", "leapquant_decode_step",
+    "leapquant_dense_step",
     "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",
     "leapquant_window_close",
 ]

@@ -19,12 +19,15 @@ LQ_ERR_HIP = -6
 LQ_GATE_GDN = 0
 LQ_GATE_KDA = 1
 LQ_NO_SMOOTH = 1
+LQ_DENSE_FP32 = 0
+LQ_DENSE_BF16 = 1
 
 EXPORTED = (
     "leapquant_quantize_state",
     "leapquant_decode_step",
     "leapquant_window_close",
     "leapquant_decode_close",
+    "leapquant_dense_step",
     "leapquant_dequantize_state",
     "leapquant_status_string",
     "leapquant_abi_version",
@@ -67,9 +70,10 @@ def load():
     lib.leapquant_decode_step.argtypes = [P, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_window_close.argtypes = [P, S, i32, vp]
     lib.leapquant_decode_close.argtypes = [P, S, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_dense_step.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
-              "leapquant_decode_close", "leapquant_dequantize_state"):
+              "leapquant_decode_close", "leapquant_dense_step", "leapquant_dequantize_state"):
         getattr(lib, f).restype = ctypes.c_int
     lib.leapquant_status_string.argtypes = [ctypes.c_int]
     lib.leapquant_status_string.restype = ctypes.c_char_p

@@ -195,6 +195,28 @@ def leapquant_decode_close(state, t, q, k, v, beta, alpha, o, stream=None):
                                             _stream(stream, state.device)))
 
 
+def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None):
+    """One token for dense states S [n][dk][dv] (float32, or bfloat16), in
+    place; the uncompressed baseline of the quantized path."""
+    if not isinstance(S, torch.Tensor) or S.dim() != 3:
+        raise ValueError("S must be a [n, dk, dv] tensor")
+    if S.dtype == torch.float32:
+        dtype = L.LQ_DENSE_FP32
+    elif S.dtype == torch.bfloat16:
+        dtype = L.LQ_DENSE_BF16
+    else:
+        raise ValueError(f"S must be float32 or bfloat16, got {S.dtype}")
+    n, dk, dv = S.shape
+    sp = _ptr(S, S.dtype, (n, dk, dv), "S")
+    g = _gate_id(gate)
+    ashape = (n,) if g == L.LQ_GATE_GDN else (n, dk)
+    args = [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
+            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
+            _ptr(o, _F32, (n, dv), "o")]
+    prm = L.LqParams(n, dk, dv, 1, 0, g, 0)
+    L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
+
+
 def leapquant_window_close(state, length, stream=None):
     prm, st = state.params(), state.ptrs()
     L.check(L.load().leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), int(length),

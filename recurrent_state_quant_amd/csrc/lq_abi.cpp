@@ -224,6 +224,38 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t, 
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
+int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const float *q,
+                         const float *k, const float *v, const float *beta, const float *alpha,
+                         float *o, hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if (dtype != LQ_DENSE_FP32 && dtype != LQ_DENSE_BF16) return LQ_ERR_SHAPE;
+  if (!S || !q || !k || !v || !beta || !alpha || !o) return LQ_ERR_NULL;
+  const bool kda = prm->gate == LQ_GATE_KDA, bf16 = dtype == LQ_DENSE_BF16;
+  if (!aligned(S, bf16 ? 8 : 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(o, 16) || !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4))
+    return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const size_t vec = n * kDim * sizeof(float);
+  const Range state = span(S, n * kDim * kDim * (bf16 ? 2 : 4));
+  const Range out = span(o, vec);
+  const Range in[5] = {span(q, vec), span(k, vec), span(v, vec), span(beta, n * sizeof(float)),
+                       span(alpha, kda ? vec : n * sizeof(float))};
+  if (overlap(state, out)) return LQ_ERR_ALIAS;
+  for (const Range &x : in)
+    if (overlap(state, x) || overlap(out, x)) return LQ_ERR_ALIAS;
+  lq::DenseArgs a{};
+  a.S = S;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.n = prm->n;
+  return hip_status(lq::launch_dense_step(a, kda, bf16, stream));
+}
+
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st, float *S_out,
                                hipStream_t stream) {
   int rc = check_params(prm);

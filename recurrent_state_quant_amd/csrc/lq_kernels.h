@@ -51,7 +51,17 @@ struct DequantArgs {
   int n, r;
 };
 
+// Dense-state per-token decode (the uncompressed baselines): S is fp32 or
+// bf16 [n][dk][dv], updated in place.
+struct DenseArgs {
+  void *S;
+  const float *q, *k, *v, *beta, *alpha;
+  float *o;
+  int n;
+};
+
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_dense_step(const DenseArgs &a, bool kda, bool bf16, hipStream_t stream);
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream);

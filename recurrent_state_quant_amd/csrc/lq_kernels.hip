@@ -962,8 +962,137 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense-state per-token decode: the uncompressed baselines the quantized path
+// is compared with (an fp32 or bf16 state read and written every token).
+// One 256-thread workgroup per state, one pass over the state: thread
+// (rg = tid >> 5, cg = tid & 31) holds rows rg + 8m (m = 0..15) x columns
+// 4cg .. 4cg+3 in registers (each wave load reads two full rows); partial
+// column sums of S^T b and S^T (D q) meet in LDS, then u_t and o_t =
+// S_{t-1}^T (D q) + (k~ . q) u_t, and the registers are updated to
+// S_t = D S_{t-1} + k~ u^T and written back.  bf16 states are widened to
+// fp32 on load and rounded to nearest even on store.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (u >> 16) | ((u & 0xffffu) ? 0x40u : 0u);  // inf / NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;  // round to nearest, ties to even
+}
+
+template <bool KDA, bool BF16>
+__global__ __launch_bounds__(256) void dense_step_kernel(const DenseArgs A) {
+  const size_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int rg = tid >> 5, cg = tid & 31;
+  __shared__ __attribute__((aligned(16))) float sh_b[D], sh_dq[D], sh_kt[D], sh_al[D];
+  __shared__ __attribute__((aligned(16))) float sh_u[D];
+  __shared__ __attribute__((aligned(16))) float2 sh_part[8 * D];
+  __shared__ float sh_kq[2];
+
+  // the state rows of this thread, issued first
+  float x[16][4];
+  if (BF16) {
+    const uint16_t *S = reinterpret_cast<const uint16_t *>(A.S) + s * D * D;
+    uint2 raw[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) raw[m] = ldu2(S + (rg + 8 * m) * D + 4 * cg);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      x[m][0] = bf16_to_f32(raw[m].x & 0xffffu);
+      x[m][1] = bf16_to_f32(raw[m].x >> 16);
+      x[m][2] = bf16_to_f32(raw[m].y & 0xffffu);
+      x[m][3] = bf16_to_f32(raw[m].y >> 16);
+    }
+  } else {
+    const float *S = reinterpret_cast<const float *>(A.S) + s * D * D;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float4 f = ld4(S + (rg + 8 * m) * D + 4 * cg);
+      x[m][0] = f.x; x[m][1] = f.y; x[m][2] = f.z; x[m][3] = f.w;
+    }
+  }
+  float vv = 0.f;
+  if (tid < D) {
+    const float k = A.k[s * D + tid], q = A.q[s * D + tid];
+    const float al = KDA ? A.alpha[s * D + tid] : A.alpha[s];
+    const float kt = A.beta[s] * k;
+    vv = A.v[s * D + tid];
+    sh_b[tid] = al * k;
+    sh_dq[tid] = al * q;
+    sh_kt[tid] = kt;
+    sh_al[tid] = al;
+    const float kq = wave_sum(kt * q);  // waves 0 and 1, all lanes active
+    if (lane == 0) sh_kq[w] = kq;
+  }
+  __syncthreads();
+  // partial column sums over this thread's 16 rows
+  float pb[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float b = sh_b[rg + 8 * m], dq = sh_dq[rg + 8 * m];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pb[c] = fmaf(x[m][c], b, pb[c]);
+      pq[c] = fmaf(x[m][c], dq, pq[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) sh_part[rg * D + 4 * cg + c] = make_float2(pb[c], pq[c]);
+  __syncthreads();
+  if (tid < D) {
+    float zb = 0.f, zq = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const float2 t = sh_part[g * D + tid];
+      zb += t.x;
+      zq += t.y;
+    }
+    const float u = vv - zb;
+    __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, zq), A.o + s * D + tid);
+    sh_u[tid] = u;
+  }
+  __syncthreads();
+  // S_t = D S_{t-1} + k~ u^T, written back in place
+  const float4 u4 = *reinterpret_cast<const float4 *>(sh_u + 4 * cg);
+  const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float al = sh_al[rg + 8 * m], kt = sh_kt[rg + 8 * m];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[m][c] = fmaf(al, x[m][c], kt * uu[c]);
+  }
+  if (BF16) {
+    uint16_t *S = reinterpret_cast<uint16_t *>(A.S) + s * D * D;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const uint32_t lo = f32_to_bf16(x[m][0]) | (f32_to_bf16(x[m][1]) << 16);
+      const uint32_t hi = f32_to_bf16(x[m][2]) | (f32_to_bf16(x[m][3]) << 16);
+      __builtin_nontemporal_store(vu2{lo, hi}, reinterpret_cast<vu2 *>(S + (rg + 8 * m) * D + 4 * cg));
+    }
+  } else {
+    float *S = reinterpret_cast<float *>(A.S) + s * D * D;
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+      st4(S + (rg + 8 * m) * D + 4 * cg, make_float4(x[m][0], x[m][1], x[m][2], x[m][3]));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_dense_step(const DenseArgs &a, bool kda, bool bf16, hipStream_t stream) {
+  if (kda && bf16)
+    hipLaunchKernelGGL((dense_step_kernel<true, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (kda)
+    hipLaunchKernelGGL((dense_step_kernel<true, false>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (bf16)
+    hipLaunchKernelGGL((dense_step_kernel<false, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dense_step_kernel<false, false>), dim3(a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream) {
   if (kda)
     hipLaunchKernelGGL(decode_step_kernel<true>, dim3(a.n), dim3(64), 0, stream, a);

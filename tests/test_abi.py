@@ -153,3 +153,26 @@ def test_aliasing_rejected(lib, entry):
     assert _decode(lib, prm, st, o=st.buf_u + 512) == L.LQ_ERR_ALIAS  # o inside the buffer
     assert lib.leapquant_quantize_state(ctypes.byref(prm), st.codes, ctypes.byref(st), None) == L.LQ_ERR_ALIAS
     assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), st.row_scale, None) == L.LQ_ERR_ALIAS
+
+
+def test_dense_step_validation(lib):
+    prm = _params()
+    _, base = _state()
+    vec = 4 * 512
+    S = base + (1 << 30)
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+
+    def call(S_=S, dtype=L.LQ_DENSE_FP32, prm_=prm, **kw):
+        x = dict(a, **kw)
+        return lib.leapquant_dense_step(ctypes.byref(prm_), S_, dtype, x["q"], x["k"], x["v"],
+                                        x["beta"], x["alpha"], x["o"], None)
+
+    assert call(S_=None) == L.LQ_ERR_NULL
+    assert call(o=0) == L.LQ_ERR_NULL
+    assert call(dtype=7) == L.LQ_ERR_SHAPE
+    assert call(prm_=_params(dk=64)) == L.LQ_ERR_UNSUPPORTED
+    assert call(S_=S + 8) == L.LQ_ERR_ALIGN                       # fp32 state: 16 bytes
+    assert call(S_=S + 4, dtype=L.LQ_DENSE_BF16) == L.LQ_ERR_ALIGN  # bf16 state: 8 bytes
+    assert call(S_=base) == L.LQ_ERR_ALIAS                         # S over q
+    assert call(o=S + 4096) == L.LQ_ERR_ALIAS                      # o inside S

@@ -313,3 +313,60 @@ def test_determinism_and_resume():
     assert torch.equal(out3[48:], out1[48:])
     for k in lq.LeapQuantState.BOUNDARY:
         assert torch.equal(getattr(st3, k), getattr(st1, k)), k
+
+
+# ---------------------------------------------------------------------------
+# Dense-state baselines ([EL] Table 2, FP32 and BF16 per-step)
+# ---------------------------------------------------------------------------
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_dense_fp32_steps(gate):
+    rng = np.random.default_rng(800 + (gate == "kda"))
+    n, T = 23, 12
+    S0 = _states_with_outliers(rng, n)
+    toks = [_token(rng, n, gate) for _ in range(T)]
+    S = _dev(S0)
+    o = torch.empty((n, 128), device=DEV)
+    S_ref = S0.astype(np.float64)
+    for t in range(T):
+        tok = toks[t]
+        lq.leapquant_dense_step(S, gate, *(_dev(tok[x]) for x in ("q", "k", "v", "beta", "alpha")), o)
+        t64 = {x: y.astype(np.float64) for x, y in tok.items()}
+        o_ref, S_ref, _ = O.step(S_ref, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate))
+        torch.cuda.synchronize()
+        P.assert_close(to_np(o), o_ref, f"dense fp32 o_{t}")
+    P.assert_close(to_np(S), S_ref, "dense fp32 state")
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_dense_bf16_step(gate):
+    rng = np.random.default_rng(900 + (gate == "kda"))
+    n = 23
+    S0 = O.round_bf16(_states_with_outliers(rng, n))
+    tok = _token(rng, n, gate)
+    S = torch.as_tensor(S0).to(torch.float32).to(torch.bfloat16).to(DEV)
+    assert torch.equal(S.double().cpu(), torch.as_tensor(S0))   # exact upload
+    o = torch.empty((n, 128), device=DEV)
+    lq.leapquant_dense_step(S, gate, *(_dev(tok[x]) for x in ("q", "k", "v", "beta", "alpha")), o)
+    torch.cuda.synchronize()
+    t64 = {x: y.astype(np.float64) for x, y in tok.items()}
+    o_ref, S_ref = O.step_dense_bf16(S0, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate))
+    P.assert_close(to_np(o), o_ref, "dense bf16 o")
+    Sg = S.double().cpu().numpy()
+    # the rounding to bf16 is decided from the fp32 update on the GPU and from
+    # the fp64 one in the oracle: they may differ by one bf16 step where the
+    # update sits at a rounding tie, plus the fp32 error of the update's two
+    # terms D S and k~ u, which dominates where they cancel
+    d_, kt_, _ = O.transition(_gate(gate), t64["k"], t64["beta"], t64["alpha"], 128)
+    _, _, (_, _, u_) = O.step(S0, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate))
+    terms = np.abs(d_[:, :, None] * S0) + np.abs(kt_[:, :, None] * u_[:, None, :])
+    d = np.abs(Sg - S_ref)
+    bound = _bf16_ulp(S_ref) * 1.0001 + 64 * 2.0 ** -24 * terms
+    worst = np.unravel_index(np.argmax(d - bound), d.shape)
+    assert np.all(d <= bound), (worst, float(Sg[worst]), float(S_ref[worst]), float(bound[worst]))
+    assert (d > 0).mean() <= 1e-3, float((d > 0).mean())

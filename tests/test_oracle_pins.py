@@ -314,3 +314,43 @@ def test_generators_match_recipe():
     tok2 = G.token_inputs(cfg, 5, 4, g2, "cpu")
     for k in tok:
         assert torch.equal(tok[k], tok2[k])
+
+
+# ---------------------------------------------------------------------------
+# Dense "BF16 per-step" baseline ([EL] Table 2): bf16 rounding of the state
+# ---------------------------------------------------------------------------
+def test_round_bf16_fixed_points_and_ties():
+    # representable values are kept; halfway cases go to the even significand
+    assert O.round_bf16(np.array([1.0, -2.5, 0.0, 3.0 * 2.0 ** -20])).tolist() == [1.0, -2.5, 0.0, 3.0 * 2.0 ** -20]
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                       # tie, 1.0 is even
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6       # tie, 1 + 2^-6 is even
+    assert O.round_bf16(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert O.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -20)) == -(1.0 + 2.0 ** -7)
+
+
+def test_round_bf16_matches_torch_and_nearest():
+    """Against torch's float32 -> bfloat16 conversion (round to nearest
+    even), and by brute force: no bf16 neighbour of x is closer."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    r = O.round_bf16(x)
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(r, t)
+    # neighbours: truncation and the next value up in magnitude
+    bits = x.view(np.uint32) & np.uint32(0xFFFF0000)
+    lo = bits.view(np.float32).astype(np.float64)
+    hi = (bits + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+    xd = x.astype(np.float64)
+    assert np.all(np.abs(r - xd) <= np.minimum(np.abs(lo - xd), np.abs(hi - xd)))
+
+
+def test_dense_bf16_step_is_rounded_exact_step():
+    rng = np.random.default_rng(12)
+    S = O.round_bf16(0.1 * rng.standard_normal((3, 8, 8)))
+    q, k, v = (rng.standard_normal((3, 8)) for _ in range(3))
+    beta, alpha = rng.uniform(0.1, 1, 3), rng.uniform(0.1, 1, 3)
+    o, S_new = O.step_dense_bf16(S, q, k, v, beta, alpha, O.GATE_GDN)
+    o2, S2, _ = O.step(S, q, k, v, beta, alpha, O.GATE_GDN)
+    np.testing.assert_array_equal(o, o2)
+    assert np.all(np.abs(S_new - S2) <= 2.0 ** -8 * np.abs(S2) + 1e-300)
+    np.testing.assert_array_equal(O.round_bf16(S_new), S_new)
