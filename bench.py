@@ -363,6 +363,30 @@ def ablations(args, cfg, dev, reps=3):
         del slab, views
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
 
+    def slots(p, r):
+        # continuous batching: every slot has its own window phase (seeded,
+        # uniform), so about 1/p of the slots close at every token; the
+        # positions live on the device.  (Phases strided by a multiple of 8
+        # in slot order would put every closing workgroup on one XCD: the
+        # dispatcher deals workgroups to the 8 XCDs round-robin.)
+        slab = lq.LeapQuantState(n, p, r, cfg.gate, dev)
+        lq.leapquant_quantize_state(slab, S_init)
+        views = [slab.view(l * nl, nl) for l in range(L)]
+        gp = torch.Generator(device=dev).manual_seed(cfg.seed + 1)
+        phase = torch.randint(0, p, (nl,), generator=gp, device=dev, dtype=torch.int32)
+        pos = [(phase + t) % p for t in range(T)]
+        step_pos = [torch.where(x == p - 1, -1, x).to(torch.int32) for x in pos]
+        close_pos = [torch.where(x == p - 1, x, -1).to(torch.int32) for x in pos]
+
+        def run():
+            for t in range(T):
+                for l in range(L):
+                    lq.leapquant_decode_step_slots(views[l], step_pos[t], *targs(t, l))
+                    lq.leapquant_decode_close_slots(views[l], close_pos[t], *targs(t, l))
+        value = timed(run)
+        del slab, views
+        return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
+
     rows2 = [("FP32 per-step", lambda: dense(torch.float32)),
              ("BF16 per-step", lambda: dense(torch.bfloat16)),
              ("INT8 per-step", lambda: windowed(1, 0, 1)),
@@ -382,12 +406,15 @@ def ablations(args, cfg, dev, reps=3):
                 ref = value
         return out, ref
 
+    rows_cb = [("lockstep windows (all slots at the same position)", lambda: windowed(cfg.p, cfg.r, 0)),
+               ("continuous batching (slot phases spread over the window)", lambda: slots(cfg.p, cfg.r))]
     t2, ref = table(rows2, None)
     t3, _ = table(rows3, ref)
+    tcb, _ = table(rows_cb, ref)
     return {"metric": "kernel throughput ablations (head-tokens/s; speedup over fp32 per-step)",
             "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph",
             "schedule": "one launch per layer and token; last token of each window fused with its close",
-            "table2": t2, "table3_r": cfg.r, "table3": t3}
+            "table2": t2, "table3_r": cfg.r, "table3": t3, "continuous_batching": tcb}
 
 
 def copy_calibration(dev, nbytes=1 << 31, reps=5):

@@ -174,6 +174,35 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t,
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st,
                                float *S_out, hipStream_t stream);
 
+/* ---- Continuous batching.  The slots of a slab hold sequences at
+ * different positions of their own windows (requests join and finish
+ * independently).  pos[n] and len[n] are int32 arrays in DEVICE memory,
+ * read by the kernels (4-byte aligned, read-only, overlapping no state
+ * array or output); the host keeps them up to date, typically with one
+ * small device operation per token.
+ *
+ * leapquant_decode_step_slots: slot s decodes its token at window position
+ * pos[s] exactly as leapquant_decode_step would with t = pos[s]; a slot with
+ * pos[s] outside [0, p) is idle (its o row and state are left as they are).
+ * leapquant_decode_close_slots: the same for the fused last-token decode
+ * and close of leapquant_decode_close (slot s closes with pos[s] + 1
+ * records); idle slots as above.
+ * leapquant_window_close_slots: slot s is closed with len[s] records when
+ * 1 <= len[s] <= p (len[s] < p closes a partial window at the end of a
+ * sequence); other slots are left as they are.
+ * The other arguments and the error codes are those of the uniform calls;
+ * values in pos and len cannot be checked on the host. */
+int leapquant_decode_step_slots(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                const float *q, const float *k, const float *v,
+                                const float *beta, const float *alpha, float *o,
+                                hipStream_t stream);
+int leapquant_decode_close_slots(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                 const float *q, const float *k, const float *v,
+                                 const float *beta, const float *alpha, float *o,
+                                 hipStream_t stream);
+int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const int32_t *len,
+                                 hipStream_t stream);
+
 /* ---- Uncompressed baselines ([EL] Table 2, rows "FP32 per-step" and
  * "BF16 per-step"): the same token update on a dense state that is read
  * and written in full every token.  Provided to measure the quantized path

@@ -28,6 +28,9 @@ EXPORTED = (
     "leapquant_window_close",
     "leapquant_decode_close",
     "leapquant_dense_step",
+    "leapquant_decode_step_slots",
+    "leapquant_decode_close_slots",
+    "leapquant_window_close_slots",
     "leapquant_dequantize_state",
     "leapquant_status_string",
     "leapquant_abi_version",
@@ -71,9 +74,14 @@ def load():
     lib.leapquant_window_close.argtypes = [P, S, i32, vp]
     lib.leapquant_decode_close.argtypes = [P, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_dense_step.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_decode_step_slots.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_decode_close_slots.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_window_close_slots.argtypes = [P, S, vp, vp]
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
-              "leapquant_decode_close", "leapquant_dense_step", "leapquant_dequantize_state"):
+              "leapquant_decode_close", "leapquant_dense_step", "leapquant_decode_step_slots",
+              "leapquant_decode_close_slots", "leapquant_window_close_slots",
+              "leapquant_dequantize_state"):
         getattr(lib, f).restype = ctypes.c_int
     lib.leapquant_status_string.argtypes = [ctypes.c_int]
     lib.leapquant_status_string.restype = ctypes.c_char_p

@@ -195,6 +195,37 @@ def leapquant_decode_close(state, t, q, k, v, beta, alpha, o, stream=None):
                                             _stream(stream, state.device)))
 
 
+def _slots_ptr(x, n, name):
+    return _ptr(x, _I32, (n,), name)
+
+
+def leapquant_decode_step_slots(state, pos, q, k, v, beta, alpha, o, stream=None):
+    """Per-slot window positions pos (int32 [n] on the device); slots with
+    pos outside [0, p) are idle."""
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_decode_step_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                 _slots_ptr(pos, state.n, "pos"), *args,
+                                                 _stream(stream, state.device)))
+
+
+def leapquant_decode_close_slots(state, pos, q, k, v, beta, alpha, o, stream=None):
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_decode_close_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                  _slots_ptr(pos, state.n, "pos"), *args,
+                                                  _stream(stream, state.device)))
+
+
+def leapquant_window_close_slots(state, lengths, stream=None):
+    """Close slot s with lengths[s] records (int32 [n] on the device) when
+    1 <= lengths[s] <= p; other slots are left as they are."""
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_window_close_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                  _slots_ptr(lengths, state.n, "lengths"),
+                                                  _stream(stream, state.device)))
+
+
 def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None):
     """One token for dense states S [n][dk][dv] (float32, or bfloat16), in
     place; the uncompressed baseline of the quantized path."""

@@ -21,6 +21,7 @@ struct DecodeArgs {
   const float *beta;
   const float *alpha;
   float *o;
+  const int32_t *pos;  // per-state window position (nullptr: t for all)
   int n, p, r, t;
 };
 
@@ -37,6 +38,9 @@ struct CloseArgs {
   // decode_close only: the last token's inputs and output
   const float *q, *k, *v, *beta, *alpha;
   float *o;
+  // per-state record counts (nullptr: len for all); for decode_close the
+  // last token's window position
+  const int32_t *lens;
   int n, p, r, len;  // len: buffered records the rebuild replays
   unsigned flags;
 };

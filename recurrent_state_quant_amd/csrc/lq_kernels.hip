@@ -178,7 +178,10 @@ template <bool KDA>
 __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   const int lane = threadIdx.x;
-  const int t = A.t, p = A.p, r = A.r;
+  const int p = A.p, r = A.r;
+  // per-slot positions (continuous batching): out-of-range slots are idle
+  const int t = A.pos ? A.pos[s] : A.t;
+  if (t < 0 || t >= p) return;
 
   __shared__ float2 sh_gy[D];  // Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_h[64];  // record weights (h_b, h_q)
@@ -676,7 +679,11 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   const int h = w & 1, ch = w >> 1;
   const int rbase = 64 * h + 4 * lr;
   const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
-  const int r = A.r, len = A.len, p = A.p;
+  const int r = A.r, p = A.p;
+  // per-slot record counts (continuous batching); a slot outside the valid
+  // range is left untouched.  FUSED: len is the last token's position t.
+  const int len = A.lens ? A.lens[s] : A.len;
+  if (FUSED ? (len < 0 || len >= p) : (len < 1 || len > p)) return;
   const size_t rec0 = s * p;
 
   __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];

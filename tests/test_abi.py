@@ -176,3 +176,29 @@ def test_dense_step_validation(lib):
     assert call(S_=S + 4, dtype=L.LQ_DENSE_BF16) == L.LQ_ERR_ALIGN  # bf16 state: 8 bytes
     assert call(S_=base) == L.LQ_ERR_ALIAS                         # S over q
     assert call(o=S + 4096) == L.LQ_ERR_ALIAS                      # o inside S
+
+
+def test_slot_entry_points_validation(lib):
+    st, base = _state()
+    prm = _params()
+    vec = 4 * 512
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+    pos = base + 5 * vec
+    for name in ("leapquant_decode_step_slots", "leapquant_decode_close_slots"):
+        f = getattr(lib, name)
+
+        def call(p_=pos, prm_=prm, **kw):
+            x = dict(a, **kw)
+            return f(ctypes.byref(prm_), ctypes.byref(st), p_, x["q"], x["k"], x["v"], x["beta"],
+                     x["alpha"], x["o"], None)
+        assert call(p_=None) == L.LQ_ERR_NULL, name
+        assert call(p_=pos + 2) == L.LQ_ERR_ALIGN, name
+        assert call(p_=st.buf_u + 64) == L.LQ_ERR_ALIAS, name       # positions inside the buffer
+        assert call(p_=a["o"]) == L.LQ_ERR_ALIAS, name              # positions over the output
+        assert call(prm_=_params(p=0)) == L.LQ_ERR_SHAPE, name
+        assert call(o=0) == L.LQ_ERR_NULL, name
+    f = lib.leapquant_window_close_slots
+    assert f(ctypes.byref(prm), ctypes.byref(st), None, None) == L.LQ_ERR_NULL
+    assert f(ctypes.byref(prm), ctypes.byref(st), pos + 1, None) == L.LQ_ERR_ALIGN
+    assert f(ctypes.byref(prm), ctypes.byref(st), st.codes + 128, None) == L.LQ_ERR_ALIAS

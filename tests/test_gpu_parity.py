@@ -370,3 +370,63 @@ def test_dense_bf16_step(gate):
     worst = np.unravel_index(np.argmax(d - bound), d.shape)
     assert np.all(d <= bound), (worst, float(Sg[worst]), float(S_ref[worst]), float(bound[worst]))
     assert (d > 0).mean() <= 1e-3, float((d > 0).mean())
+
+
+# ---------------------------------------------------------------------------
+# Continuous batching: slots join and finish at different steps, each with
+# its own window phase; partial windows are closed at sequence end
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cid", [1, 3])
+def test_continuous_batching_slots(cid):
+    cfg = CONFIGS[cid]
+    n, T, p = 12, 64, cfg.p
+    rng = np.random.default_rng(70 + cid)
+    join = rng.integers(0, 24, n)
+    end = np.minimum(T, join + rng.integers(8, 60, n))
+    end[0], join[0] = T, 0                          # one slot runs the whole time
+    cfgw, S0, tok = _workload(cid, n, T)
+    tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    gate = _gate(cfg.gate)
+    ref_o, ref_b, ref_tok = [], [], []
+    for s in range(n):
+        ts = {k: v[join[s]:end[s], s:s + 1] for k, v in tokn.items()}
+        o_s, b_s = O.run_windowed(S0.numpy()[s:s + 1], ts, p, cfg.r, gate)
+        ref_o.append(o_s[:, 0])
+        ref_b.append(b_s)
+        ref_tok.append(ts)
+    st = lq.LeapQuantState(n, p, cfg.r, cfg.gate, DEV)
+    for s in range(n):
+        upload_boundary(st, ref_b[s][0], [s])
+    window = np.zeros(n, int)
+    out = torch.zeros((n, 128), device=DEV)
+    flips = 0
+    for t in range(T):
+        active = (join <= t) & (t < end)
+        pos = np.where(active, (t - join) % p, -1)
+        closing = active & (pos == p - 1)
+        ending = active & (t == end - 1) & ~closing
+        step_pos = torch.as_tensor(np.where(closing, -1, pos), dtype=torch.int32, device=DEV)
+        close_pos = torch.as_tensor(np.where(closing, pos, -1), dtype=torch.int32, device=DEV)
+        args = [tokd[x][t] for x in ("q", "k", "v", "beta", "alpha")] + [out]
+        lq.leapquant_decode_step_slots(st, step_pos, *args)
+        lq.leapquant_decode_close_slots(st, close_pos, *args)
+        if ending.any():
+            lens = torch.as_tensor(np.where(ending, pos + 1, 0), dtype=torch.int32, device=DEV)
+            lq.leapquant_window_close_slots(st, lens)
+        torch.cuda.synchronize()
+        og = to_np(out)
+        for s in np.nonzero(active)[0]:
+            P.assert_close(og[s:s + 1], ref_o[s][t - join[s]][None], f"slot {s} step {t}")
+        for s in np.nonzero(closing | ending)[0]:
+            window[s] += 1
+            gb = boundary_np(st, [s])
+            w0 = (window[s] - 1) * p          # the window's first token, in slot s's own count
+            _, _, S_end, _ = O.window(ref_b[s][window[s] - 1], ref_tok[s], w0, t - join[s] + 1 - w0,
+                                      gate, cfg.r)
+            stats = P.compare_boundary(gb, ref_b[s][window[s]], S_end.astype(np.float32), cfg.r,
+                                       f"slot {s} boundary {window[s]}")
+            flips += stats["flips"]
+            upload_boundary(st, ref_b[s][window[s]], [s])   # next window starts from the oracle's state
+    assert window.sum() == sum(int(np.ceil((end[s] - join[s]) / p)) for s in range(n))
+    print(f"cfg{cid}: {window.sum()} slot windows, {flips} flipped codes")
