@@ -19,6 +19,7 @@
  *                b_t = alpha_t k_t (alpha_t one scalar per state).
  *   LQ_GATE_KDA (Kimi Delta Attention): D_t = Diag(alpha_t), k~_t = beta_t k_t,
  *                b_t = alpha_t * k_t (alpha_t one value per key channel).
+ *   With the LQ_NO_DELTA flag, b_t = 0 (the other rows of Table 4).
  * Between window boundaries the state is kept as ([EL] Figure 2, Figure 4)
  *   B  = deQ(codes, a, s) + sum_c e_{idx_c} w_c^T      (fixed, low-bit)
  *   records (d_i, k~_i, u_i), i < t                    (fp32 buffer)
@@ -89,7 +90,15 @@ typedef enum lq_gate {
   LQ_GATE_KDA = 1  /* per-key-channel decay (Kimi Delta Attention)       */
 } lq_gate;
 
-enum { LQ_NO_SMOOTH = 1u /* ablation: s_j = 1 for every column */ };
+enum {
+  LQ_NO_SMOOTH = 1u, /* ablation: s_j = 1 for every column                     */
+  LQ_NO_DELTA = 2u   /* b_t = 0, so u_t = v_t: the rows of [EL] Appendix Table 4
+                        without the delta correction.  With LQ_GATE_GDN: linear
+                        attention (alpha = 1, beta = 1), RetNet (alpha = gamma,
+                        beta = 1), Mamba2 (beta = 1); with LQ_GATE_KDA: GLA /
+                        RWKV6 / HGRN2 (beta = 1).  DeltaNet is LQ_GATE_GDN with
+                        alpha = 1 and the flag clear.                          */
+};
 
 typedef struct lq_params {
   int32_t n;      /* number of independent states in the slab (>= 1)     */
@@ -98,7 +107,7 @@ typedef struct lq_params {
   int32_t p;      /* window length in tokens, 1..64                       */
   int32_t r;      /* compensator rows per state, 0..16                    */
   int32_t gate;   /* lq_gate                                              */
-  uint32_t flags; /* 0 or LQ_NO_SMOOTH                                    */
+  uint32_t flags; /* LQ_NO_SMOOTH | LQ_NO_DELTA, or 0                      */
 } lq_params;
 
 /* One slab of n states.  The first five arrays are the boundary state

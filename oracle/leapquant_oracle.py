@@ -62,6 +62,8 @@ import numpy as np
 GATE_GDN = 0   # D_t = alpha_t I           (Gated DeltaNet row of Table 4)
 GATE_KDA = 1   # D_t = Diag(alpha_t)       (Kimi Delta Attention reading)
 NO_SMOOTH = 1  # flag: s_j = 1 (ablation of residual smoothing)
+NO_DELTA = 2   # flag: b_t = 0, so u_t = v_t (the rows of Table 4 without the
+               # delta correction: linear attention, RetNet, Mamba2, GLA family)
 
 _F32 = np.float32
 
@@ -69,11 +71,15 @@ _F32 = np.float32
 # --------------------------------------------------------------------------
 # Recurrence ([EL] Appendix Table 4)
 # --------------------------------------------------------------------------
-def transition(gate, k, beta, alpha, dk):
+def transition(gate, k, beta, alpha, dk, flags=0):
     """Return (d, k~, b) for a batch of states.
 
     d is the diagonal of D_t as an [n, dk] array.  Shapes: k [n, dk],
-    beta [n], alpha [n] (GDN) or [n, dk] (KDA).
+    beta [n], alpha [n] (GDN) or [n, dk] (KDA).  With NO_DELTA, b = 0.  The
+    rows of [EL] Appendix Table 4 are: linear attention (alpha = 1, beta = 1,
+    NO_DELTA), RetNet (alpha = gamma, beta = 1, NO_DELTA), Mamba2 (scalar
+    alpha_t, beta = 1, NO_DELTA), GLA / RWKV6 / HGRN2 (per-channel alpha_t,
+    beta = 1, NO_DELTA), DeltaNet (alpha = 1), Gated DeltaNet.
     """
     k = np.asarray(k, np.float64)
     beta = np.asarray(beta, np.float64)
@@ -86,18 +92,18 @@ def transition(gate, k, beta, alpha, dk):
     else:
         raise ValueError("unknown gate")
     kt = beta.reshape(n, 1) * k
-    b = d * k
+    b = np.zeros_like(k) if flags & NO_DELTA else d * k
     return d, kt, b
 
 
-def step(S, q, k, v, beta, alpha, gate):
+def step(S, q, k, v, beta, alpha, gate, flags=0):
     """One exact token update on dense fp64 states S [n, dk, dv].
 
     Returns (o [n, dv], S_new [n, dk, dv], record) where record = (d, k~, u),
     the buffered update of [EL] Table 4's last column.
     """
     n, dk, dv = S.shape
-    d, kt, b = transition(gate, k, beta, alpha, dk)
+    d, kt, b = transition(gate, k, beta, alpha, dk, flags)
     u = np.asarray(v, np.float64) - np.einsum("nij,ni->nj", S, b)
     S_new = d[:, :, None] * S + kt[:, :, None] * u[:, None, :]
     o = np.einsum("nij,ni->nj", S_new, np.asarray(q, np.float64))
@@ -112,7 +118,7 @@ def replay(B, records):
     return S
 
 
-def sequential_exact(S0, tokens, gate, keep_every=0):
+def sequential_exact(S0, tokens, gate, keep_every=0, flags=0):
     """Unquantized recurrence over all tokens (fp64).
 
     tokens: dict of arrays q [T,n,dk], k, v [T,n,dv], beta [T,n], alpha.
@@ -125,7 +131,7 @@ def sequential_exact(S0, tokens, gate, keep_every=0):
     kept = {}
     for t in range(T):
         o, S, _ = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
-                       tokens["beta"][t], tokens["alpha"][t], gate)
+                       tokens["beta"][t], tokens["alpha"][t], gate, flags)
         outs[t] = o
         if keep_every and (t + 1) % keep_every == 0:
             kept[t + 1] = S.copy()
@@ -239,7 +245,7 @@ def window(boundary, tokens, t0, length, gate, r, flags=0, quantizer=True):
     records = []
     for t in range(t0, t0 + length):
         o, S, rec = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
-                         tokens["beta"][t], tokens["alpha"][t], gate)
+                         tokens["beta"][t], tokens["alpha"][t], gate, flags)
         outs.append(o)
         records.append(rec)
     nxt = quantize(S, r, flags) if quantizer else S
@@ -285,7 +291,7 @@ def run_per_token(S_init, tokens, r, gate, flags=0):
     for t in range(T):
         S = dequantize(b)
         o, S, _ = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
-                       tokens["beta"][t], tokens["alpha"][t], gate)
+                       tokens["beta"][t], tokens["alpha"][t], gate, flags)
         outs.append(o)
         b = quantize(S, r, flags)
     return np.stack(outs), b
@@ -303,11 +309,11 @@ def round_bf16(x):
     return out.astype(np.float64)
 
 
-def step_dense_bf16(S, q, k, v, beta, alpha, gate):
+def step_dense_bf16(S, q, k, v, beta, alpha, gate, flags=0):
     """One token of the "BF16 per-step" baseline of [EL] Table 2: the exact
     update of a bf16 state, the new state rounded to bf16.  Returns (o, S_new)
     with o read from the updated state before rounding."""
-    o, S_new, _ = step(S, q, k, v, beta, alpha, gate)
+    o, S_new, _ = step(S, q, k, v, beta, alpha, gate, flags)
     return o, round_bf16(S_new)
 
 

@@ -19,6 +19,7 @@ LQ_ERR_HIP = -6
 LQ_GATE_GDN = 0
 LQ_GATE_KDA = 1
 LQ_NO_SMOOTH = 1
+LQ_NO_DELTA = 2
 LQ_DENSE_FP32 = 0
 LQ_DENSE_BF16 = 1
 

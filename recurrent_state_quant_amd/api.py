@@ -226,9 +226,10 @@ def leapquant_window_close_slots(state, lengths, stream=None):
                                                   _stream(stream, state.device)))
 
 
-def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None):
+def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0):
     """One token for dense states S [n][dk][dv] (float32, or bfloat16), in
-    place; the uncompressed baseline of the quantized path."""
+    place; the uncompressed baseline of the quantized path.  flags may hold
+    LQ_NO_DELTA."""
     if not isinstance(S, torch.Tensor) or S.dim() != 3:
         raise ValueError("S must be a [n, dk, dv] tensor")
     if S.dtype == torch.float32:
@@ -244,7 +245,7 @@ def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None):
     args = [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
             _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
             _ptr(o, _F32, (n, dv), "o")]
-    prm = L.LqParams(n, dk, dv, 1, 0, g, 0)
+    prm = L.LqParams(n, dk, dv, 1, 0, g, int(flags))
     L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
 
 

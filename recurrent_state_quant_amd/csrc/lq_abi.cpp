@@ -27,7 +27,7 @@ int check_params(const lq_params *prm) {
   if (prm->dk != kDim || prm->dv != kDim) return LQ_ERR_UNSUPPORTED;
   if (prm->n < 1 || prm->p < 1 || prm->p > kMaxP || prm->r < 0 || prm->r > kMaxR) return LQ_ERR_SHAPE;
   if (prm->gate != LQ_GATE_GDN && prm->gate != LQ_GATE_KDA) return LQ_ERR_SHAPE;
-  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_SMOOTH)) return LQ_ERR_SHAPE;
+  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_SMOOTH | LQ_NO_DELTA)) return LQ_ERR_SHAPE;
   return LQ_OK;
 }
 
@@ -167,6 +167,7 @@ int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, c
   a.p = prm->p;
   a.r = prm->r;
   a.t = t;
+  a.flags = prm->flags;
   return hip_status(lq::launch_decode_step(a, kda, stream));
 }
 
@@ -270,6 +271,7 @@ int leapquant_decode_step_slots(const lq_params *prm, const lq_state *st, const 
   a.p = prm->p;
   a.r = prm->r;
   a.t = 0;
+  a.flags = prm->flags;
   return hip_status(lq::launch_decode_step(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -357,6 +359,7 @@ int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const flo
   a.alpha = alpha;
   a.o = o;
   a.n = prm->n;
+  a.flags = prm->flags;
   return hip_status(lq::launch_dense_step(a, kda, bf16, stream));
 }
 

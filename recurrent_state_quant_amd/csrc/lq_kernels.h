@@ -23,6 +23,7 @@ struct DecodeArgs {
   float *o;
   const int32_t *pos;  // per-state window position (nullptr: t for all)
   int n, p, r, t;
+  unsigned flags;      // bit 1: b_t = 0 (no delta correction)
 };
 
 struct CloseArgs {
@@ -62,6 +63,7 @@ struct DenseArgs {
   const float *q, *k, *v, *beta, *alpha;
   float *o;
   int n;
+  unsigned flags;  // bit 1: b_t = 0 (no delta correction)
 };
 
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream);

@@ -245,7 +245,9 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 
   // ---- a1 token prep; append k~_t and the gate of record t
   const float2 kt = make_float2(bt * kk.x, bt * kk.y);
-  const float2 yb = make_float2(al.x * kk.x, al.y * kk.y);
+  // b_t = alpha_t * k_t, or 0 for the recurrences without the delta
+  // correction (flag bit 1)
+  const float2 yb = (A.flags & 2u) ? make_float2(0.f, 0.f) : make_float2(al.x * kk.x, al.y * kk.y);
   const float2 yq = make_float2(al.x * qq.x, al.y * qq.y);
   st2(A.buf_k + (rec0 + t) * D + 2 * lane, kt);
   if (KDA) {
@@ -814,7 +816,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       if (e0 < ncv) dc[e0] = c0;
       if (e1 < ncv) dc[e1] = ld4(A.comp_val + s * r * D + 4 * e1);
       if (FUSED && first && tid < D) {
-        sh_tk[tid] = tk;
+        sh_tk[tid] = (A.flags & 2u) ? 0.f : tk;  // b_t = 0 without the delta correction
         sh_tq[tid] = tq;
         sh_tkt[tid] = tb * tk;
         sh_tu[tid] = tv;  // v_t; replaced by u_t after the decode
@@ -1025,7 +1027,7 @@ __global__ __launch_bounds__(256) void dense_step_kernel(const DenseArgs A) {
     const float al = KDA ? A.alpha[s * D + tid] : A.alpha[s];
     const float kt = A.beta[s] * k;
     vv = A.v[s * D + tid];
-    sh_b[tid] = al * k;
+    sh_b[tid] = (A.flags & 2u) ? 0.f : al * k;  // b_t = 0 without the delta correction
     sh_dq[tid] = al * q;
     sh_kt[tid] = kt;
     sh_al[tid] = al;

@@ -88,7 +88,7 @@ def _decode(lib, prm, st, t=0, **kw):
     (dict(dk=64), L.LQ_ERR_UNSUPPORTED), (dict(dv=256), L.LQ_ERR_UNSUPPORTED),
     (dict(n=0), L.LQ_ERR_SHAPE), (dict(p=0), L.LQ_ERR_SHAPE), (dict(p=65), L.LQ_ERR_SHAPE),
     (dict(r=-1), L.LQ_ERR_SHAPE), (dict(r=17), L.LQ_ERR_SHAPE), (dict(gate=2), L.LQ_ERR_SHAPE),
-    (dict(flags=2), L.LQ_ERR_SHAPE),
+    (dict(flags=4), L.LQ_ERR_SHAPE),
 ])
 def test_bad_params(lib, entry, kw, code):
     st, _ = _state()

@@ -430,3 +430,73 @@ def test_continuous_batching_slots(cid):
             upload_boundary(st, ref_b[s][window[s]], [s])   # next window starts from the oracle's state
     assert window.sum() == sum(int(np.ceil((end[s] - join[s]) / p)) for s in range(n))
     print(f"cfg{cid}: {window.sum()} slot windows, {flips} flipped codes")
+
+
+# ---------------------------------------------------------------------------
+# The other rows of [EL] Appendix Table 4 (LQ_NO_DELTA: b_t = 0)
+# ---------------------------------------------------------------------------
+_TABLE4 = {  # row: (gate, alpha rule, beta = 1?, no delta?)
+    "linear_attention": ("gdn", "one", True, True),
+    "retnet": ("gdn", "const", True, True),
+    "mamba2": ("gdn", "token", True, True),
+    "gla_rwkv6_hgrn2": ("kda", "token", True, True),
+    "deltanet": ("gdn", "one", False, False),
+}
+
+
+def _table4_tokens(row, n, T, seed):
+    gate, arule, beta1, _ = _TABLE4[row]
+    cfg = CONFIGS[3 if gate == "kda" else 1]
+    g = G.make_generator(seed, "cpu")
+    S0 = G.initial_state(cfg, n, g, "cpu")
+    tok = G.token_inputs(cfg, n, T, g, "cpu")
+    if arule == "one":
+        tok["alpha"] = torch.ones_like(tok["alpha"])
+    elif arule == "const":
+        tok["alpha"] = torch.full_like(tok["alpha"], 0.9)
+    if beta1:
+        tok["beta"] = torch.ones_like(tok["beta"])
+    return cfg, S0, tok
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("row", list(_TABLE4))
+def test_table4_rows_forced_windows(row, fused):
+    gate, _, _, nodelta = _TABLE4[row]
+    n, T, p, r = 12, 48, 16, 4
+    flags = lq.LQ_NO_DELTA if nodelta else 0
+    cfg, S0, tok = _table4_tokens(row, n, T, 31)
+    tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
+    oflags = O.NO_DELTA if nodelta else 0
+    o_ref, bounds = O.run_windowed(S0.numpy(), tokn, p, r, _gate(gate), flags=oflags)
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    st = lq.LeapQuantState(n, p, r, gate, DEV, flags)
+    out = torch.empty((T, n, 128), device=DEV)
+    for w in range(T // p):
+        upload_boundary(st, bounds[w])
+        run_window(st, tokd, w * p, p, out, fused=fused)
+        torch.cuda.synchronize()
+        sl = slice(w * p, (w + 1) * p)
+        P.assert_close(to_np(out[sl]), o_ref[sl], f"{row} window {w} outputs")
+        _, _, S_end, _ = O.window(bounds[w], tokn, w * p, p, _gate(gate), r, oflags)
+        P.compare_boundary(boundary_np(st), bounds[w + 1], S_end.astype(np.float32), r,
+                           f"{row} boundary {w + 1}")
+
+
+@pytest.mark.parametrize("row", ["mamba2", "gla_rwkv6_hgrn2"])
+def test_table4_rows_dense_baseline(row):
+    gate, _, _, nodelta = _TABLE4[row]
+    n, T = 10, 6
+    cfg, S0, tok = _table4_tokens(row, n, T, 32)
+    S = S0.to(DEV).contiguous()
+    S_ref = S0.numpy().astype(np.float64)
+    o = torch.empty((n, 128), device=DEV)
+    for t in range(T):
+        lq.leapquant_dense_step(S, gate, *(tok[x][t].to(DEV) for x in ("q", "k", "v", "beta", "alpha")), o,
+                                flags=lq.LQ_NO_DELTA)
+        t64 = {x: tok[x][t].numpy().astype(np.float64) for x in tok}
+        o_ref, S_ref, _ = O.step(S_ref, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"], _gate(gate),
+                                 O.NO_DELTA)
+        torch.cuda.synchronize()
+        P.assert_close(to_np(o), o_ref, f"{row} dense o_{t}")
+    P.assert_close(to_np(S), S_ref, f"{row} dense state")

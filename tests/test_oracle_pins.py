@@ -354,3 +354,71 @@ def test_dense_bf16_step_is_rounded_exact_step():
     np.testing.assert_array_equal(o, o2)
     assert np.all(np.abs(S_new - S2) <= 2.0 ** -8 * np.abs(S2) + 1e-300)
     np.testing.assert_array_equal(O.round_bf16(S_new), S_new)
+
+
+# ---------------------------------------------------------------------------
+# Other rows of [EL] Appendix Table 4 (b_t = 0: NO_DELTA), closed forms
+# ---------------------------------------------------------------------------
+def _rows_tokens(rng, T, n, dk, dv, kda):
+    q = rng.standard_normal((T, n, dk))
+    k = rng.standard_normal((T, n, dk))
+    v = rng.standard_normal((T, n, dv))
+    beta = np.ones((T, n))
+    alpha = rng.uniform(0.3, 1.0, (T, n, dk) if kda else (T, n))
+    return dict(q=q, k=k, v=v, beta=beta, alpha=alpha)
+
+
+@pytest.mark.parametrize("row", ["linear", "retnet", "mamba2", "gla"])
+def test_table4_rows_without_delta_closed_form(row):
+    """S_T = (prod_t D_t) S_0 + sum_t (prod_{s>t} D_s) k_t v_t^T, written with
+    cumulative products instead of the step loop; outputs o_t = S_t^T q_t."""
+    rng = np.random.default_rng(40)
+    T, n, dk, dv = 7, 3, 5, 4
+    kda = row == "gla"
+    tok = _rows_tokens(rng, T, n, dk, dv, kda)
+    if row == "linear":
+        tok["alpha"] = np.ones((T, n))
+    elif row == "retnet":
+        tok["alpha"] = np.full((T, n), 0.8)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    S0 = rng.standard_normal((n, dk, dv))
+    outs, S_T, _ = O.sequential_exact(S0, tok, gate, flags=O.NO_DELTA)
+    a = tok["alpha"] if kda else np.repeat(tok["alpha"][:, :, None], dk, axis=2)   # [T, n, dk]
+    for t_end in range(1, T + 1):
+        tail = lambda t: np.prod(a[t + 1:t_end], axis=0) if t + 1 < t_end else np.ones((n, dk))
+        S = np.prod(a[:t_end], axis=0)[:, :, None] * S0
+        for t in range(t_end):
+            S = S + (tail(t) * tok["k"][t])[:, :, None] * tok["v"][t][:, None, :]
+        np.testing.assert_allclose(np.einsum("nij,ni->nj", S, tok["q"][t_end - 1]), outs[t_end - 1],
+                                   rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S_T, rtol=1e-12, atol=1e-12)
+
+
+def test_delta_rule_writes_value_under_its_key():
+    """DeltaNet row (alpha = 1, beta = 1, unit key): after the update the
+    state maps the key exactly to the value, S_t^T k_t = v_t."""
+    rng = np.random.default_rng(41)
+    n, dk, dv = 4, 6, 5
+    S = rng.standard_normal((n, dk, dv))
+    k = rng.standard_normal((n, dk)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((n, dv))
+    _, S1, _ = O.step(S, k, k, v, np.ones(n), np.ones(n), O.GATE_GDN)
+    np.testing.assert_allclose(np.einsum("nij,ni->nj", S1, k), v, rtol=1e-12, atol=1e-12)
+    # without the delta correction the same update only adds k v^T
+    _, S2, _ = O.step(S, k, k, v, np.ones(n), np.ones(n), O.GATE_GDN, O.NO_DELTA)
+    np.testing.assert_allclose(S2, S + k[:, :, None] * v[:, None, :], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_windowing_is_exact_without_delta(kda):
+    """P1 for the NO_DELTA rows: with the quantizer off, windows reproduce the
+    plain recurrence."""
+    rng = np.random.default_rng(42)
+    T, n, dk, dv = 11, 2, 6, 5
+    tok = _rows_tokens(rng, T, n, dk, dv, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    S0 = rng.standard_normal((n, dk, dv))
+    o_ref, S_ref, _ = O.sequential_exact(S0, tok, gate, flags=O.NO_DELTA)
+    o_w, b = O.run_windowed(S0, tok, 4, 0, gate, flags=O.NO_DELTA, quantizer=False)
+    np.testing.assert_allclose(o_w, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b[max(b)], S_ref, rtol=1e-12, atol=1e-12)
