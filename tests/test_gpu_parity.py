@@ -500,3 +500,32 @@ def test_table4_rows_dense_baseline(row):
         torch.cuda.synchronize()
         P.assert_close(to_np(o), o_ref, f"{row} dense o_{t}")
     P.assert_close(to_np(S), S_ref, f"{row} dense state")
+
+
+# ---------------------------------------------------------------------------
+# DeltaProduct ([EL] Table 4 caption): n_h delta-rule sub-steps per token,
+# each an instance of the recurrence with its own record; the token's output
+# is read after the last sub-step.  The existing calls cover it: sub-steps
+# are consecutive window positions (p a multiple of n_h), the window closes
+# at a token boundary.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fused", [False, True])
+def test_deltaproduct_substeps(fused):
+    nh, tokens_, n, p, r = 2, 24, 10, 16, 4
+    steps = nh * tokens_
+    cfg, S0, tok = _workload(1, n, steps, seed=33)          # sub-step inputs, [steps, n, ...]
+    tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
+    o_ref, bounds = O.run_windowed(S0.numpy(), tokn, p, r, O.GATE_GDN)
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    st = lq.LeapQuantState(n, p, r, "gdn", DEV)
+    out = torch.empty((steps, n, 128), device=DEV)
+    for w in range(steps // p):
+        upload_boundary(st, bounds[w])
+        run_window(st, tokd, w * p, p, out, fused=fused)
+        torch.cuda.synchronize()
+        # token outputs: after sub-steps nh-1, 2nh-1, ... of the window
+        sl = slice(w * p + nh - 1, (w + 1) * p, nh)
+        P.assert_close(to_np(out[sl]), o_ref[sl], f"DeltaProduct window {w} token outputs")
+        _, _, S_end, _ = O.window(bounds[w], tokn, w * p, p, O.GATE_GDN, r)
+        P.compare_boundary(boundary_np(st), bounds[w + 1], S_end.astype(np.float32), r,
+                           f"DeltaProduct boundary {w + 1}")
