@@ -61,7 +61,8 @@
  *     A failed launch returns LQ_ERR_HIP.
  *   - Values are not checked: NaN or Inf inputs give unspecified (but
  *     in-bounds) results.  comp_idx entries outside [0, dk) are ignored when
- *     the state is read.
+ *     the state is read; the r entries of a state are distinct rows (the
+ *     split always writes them so), and duplicates give unspecified results.
  */
 #ifndef LEAPQUANT_H
 #define LEAPQUANT_H
