@@ -411,10 +411,59 @@ def ablations(args, cfg, dev, reps=3):
     t2, ref = table(rows2, None)
     t3, _ = table(rows3, ref)
     tcb, _ = table(rows_cb, ref)
+    lat = latency(dev)
     return {"metric": "kernel throughput ablations (head-tokens/s; speedup over fp32 per-step)",
             "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph",
             "schedule": "one launch per layer and token; last token of each window fused with its close",
-            "table2": t2, "table3_r": cfg.r, "table3": t3, "continuous_batching": tcb}
+            "table2": t2, "table3_r": cfg.r, "table3": t3, "continuous_batching": tcb,
+            "latency_single_state": lat}
+
+
+def latency(dev, windows=8, reps=20):
+    """Per-token latency of the single-head, batch-1 workload (one state, one
+    layer): a window of decode steps with the fused last token, replayed from
+    a graph; reported as microseconds per token (window time / p)."""
+    import torch
+    import recurrent_state_quant_amd as lq
+    from workloads import generators as G
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS[0]
+    T = windows * cfg.p
+    g = G.make_generator(cfg.seed, dev)
+    S_init = G.initial_state(cfg, 1, g, dev)
+    tok = G.token_inputs(cfg, 1, T, g, dev)
+    out = torch.empty((1, cfg.dv), device=dev)
+    res = {}
+    for sched in ("fused", "separate"):
+        st = lq.LeapQuantState(1, cfg.p, cfg.r, cfg.gate, dev)
+        lq.leapquant_quantize_state(st, S_init)
+
+        def run():
+            for t in range(T):
+                j = t % cfg.p
+                args = (tok["q"][t], tok["k"][t], tok["v"][t], tok["beta"][t], tok["alpha"][t], out)
+                if j == cfg.p - 1 and sched == "fused":
+                    lq.leapquant_decode_close(st, j, *args)
+                else:
+                    lq.leapquant_decode_step(st, j, *args)
+                    if j == cfg.p - 1:
+                        lq.leapquant_window_close(st, cfg.p)
+        stream = torch.cuda.Stream(device=dev)
+        with torch.cuda.stream(stream):
+            run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            run()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        res[sched + "_us_per_token"] = round((time.perf_counter() - t0) / (reps * T) * 1e6, 2)
+    res["workload"] = cfg.name
+    return res
 
 
 def copy_calibration(dev, nbytes=1 << 31, reps=5):
