@@ -161,6 +161,50 @@ def test_decode_step_entry(gate, p, t, r):
         np.testing.assert_array_equal(to_np(st.buf_u[:, i]), ur)
 
 
+# The decode launcher picks its kernel by slab size (two waves per state up
+# to 4,096 states, one wave above).  Both sides of the switch, with per-slot
+# window positions and idle slots, on slabs tiled from m distinct states so
+# that the oracle computes m states and every slot is still compared.
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("n", [4096, 4097])
+def test_decode_step_slab_sizes(gate, n):
+    rng = np.random.default_rng(2000 + n + 7 * (gate == "kda"))
+    m, p, r = 13, 16, 4
+    base_t = rng.integers(0, p, m)
+    base_t[0], base_t[1] = 0, p - 1
+    b, recs = _random_window_inputs(rng, m, p, p - 1, gate, r)
+    tok = _token(rng, m, gate)
+    tile = np.arange(n) % m
+    pos = base_t[tile].astype(np.int32)
+    idle = np.zeros(n, bool)
+    idle[[5, n // 2, n - 1]] = True
+    pos[idle] = [-1, p, -1]
+    st = lq.LeapQuantState(n, p, r, gate, DEV)
+    upload_boundary(st, {k: v[tile] for k, v in b.items()})
+    _upload_records(st, [(a[tile], kt[tile], u[tile]) for a, kt, u in recs], gate)
+    st.buf_u[:, p - 1] = float("nan")
+    o = torch.full((n, 128), float("nan"), device=DEV)
+    lq.leapquant_decode_step_slots(st, torch.as_tensor(pos, device=DEV),
+                                   *[_dev(tok[x][tile]) for x in ("q", "k", "v", "beta", "alpha")], o)
+    torch.cuda.synchronize()
+    o_ref = np.empty((m, 128))
+    u_ref = np.empty((m, 128))
+    t64 = {k: v.astype(np.float64) for k, v in tok.items()}
+    for t in np.unique(base_t):
+        j = np.nonzero(base_t == t)[0]
+        S_prev = O.replay(O.dequantize({k: v[j] for k, v in b.items()}),
+                          _oracle_records([(a[j], kt[j], u[j]) for a, kt, u in recs[:t]], gate))
+        o_j, _, (_, _, u_j) = O.step(S_prev, *[t64[x][j] for x in ("q", "k", "v", "beta", "alpha")],
+                                     _gate(gate))
+        o_ref[j], u_ref[j] = o_j, u_j
+    og, ug = to_np(o), to_np(st.buf_u)
+    act = ~idle
+    P.assert_close(og[act], o_ref[tile[act]], f"o_t, {n} slots")
+    P.assert_close(ug[act, pos[act]], u_ref[tile[act]], f"u_t, {n} slots")
+    assert np.isnan(og[idle]).all(), "idle slots wrote o"
+    assert np.isnan(ug[idle, p - 1]).all(), "idle slots wrote a record"
+
+
 # ---------------------------------------------------------------------------
 # a5-a8: window close against synthetic records
 # ---------------------------------------------------------------------------
