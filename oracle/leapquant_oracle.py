@@ -37,6 +37,18 @@ What is computed (all floating point in fp64 unless a step says fp32):
   pages; this build's reading): the r rows of largest L2 norm, ties to the
   lower row index, stored in descending-norm order.
 
+* Dense Compensator Tokens (flag DENSE_COMP; a second reading of the same
+  passages): a compensator is a token (k_c, w_c) with a dense unit key k_c,
+  entering the state as k_c w_c^T and following the update path of the
+  window's real tokens.  The keys span an approximation of the state's
+  dominant left singular subspace (the "dominant large-magnitude structure"
+  of [EL] Figure 4): subspace iteration started from the one-hot keys of the
+  r largest-norm rows, `iters` rounds of Y = S S^T K, K = MGS(Y) (modified
+  Gram-Schmidt in compensator order; a column whose projected norm is at
+  most 1e-3 of its norm before projection, or zero, becomes the zero key).
+  Values w_c = S^T k_c from the fp32 keys, residual R = S - sum_c k_c w_c^T.
+  With iters = 0 this is exactly the row extraction above.
+
 * Residual smoothing ([EL] Abstract; [TM]): not specified by the pages; this
   build's reading is a per-value-column absmax scale s_j of the residual
   (after extraction), 1 for an all-zero column.
@@ -54,7 +66,11 @@ Parity pins (tests/test_oracle_pins.py): Table 4 closed forms for every row,
 hand-derived quantizer fixtures (tests/golden/), the half-step error bound,
 extraction/smoothing invariants, exact recurrence when quantization is off,
 the p=1 reduction to per-token quantization, and a brute-force dense
-implementation on tiny heads.  Parity unpinned: agreement with the authors'
+implementation on tiny heads.  Dense compensator tokens
+(tests/test_oracle_dense_comp.py): zero iterations equal the row
+extraction, orthonormal keys and an orthogonal residual, convergence to the
+SVD's leading subspace, LAPACK Householder QR of the same iterates on tiny
+heads, the half-step bound of the reconstruction, rank-deficient states.  Parity unpinned: agreement with the authors'
 own extraction and smoothing rules, which the pages do not state.
 """
 import numpy as np
@@ -64,6 +80,8 @@ GATE_KDA = 1   # D_t = Diag(alpha_t)       (Kimi Delta Attention reading)
 NO_SMOOTH = 1  # flag: s_j = 1 (ablation of residual smoothing)
 NO_DELTA = 2   # flag: b_t = 0, so u_t = v_t (the rows of Table 4 without the
                # delta correction: linear attention, RetNet, Mamba2, GLA family)
+DENSE_COMP = 4  # flag: compensator tokens with dense keys (subspace iteration)
+MGS_DROP = 1e-3  # relative projected norm at or below which a key is dropped
 
 _F32 = np.float32
 
@@ -141,13 +159,42 @@ def sequential_exact(S0, tokens, gate, keep_every=0, flags=0):
 # --------------------------------------------------------------------------
 # Quantized boundary state ([EL] Abstract, Figure 4; [TM])
 # --------------------------------------------------------------------------
-def quantize(S, r, flags=0):
-    """Split an fp32 state into compensator rows + smoothed int8 residual.
+def mgs(Y):
+    """Modified Gram-Schmidt on the columns of Y [dk, r] (fp64), in column
+    order.  A column whose norm after projection is zero or at most MGS_DROP
+    times its norm before projection gives a zero column."""
+    dk, r = Y.shape
+    K = np.zeros((dk, r))
+    for c in range(r):
+        v = Y[:, c].copy()
+        n0 = np.sqrt(v @ v)
+        for c2 in range(c):
+            v = v - (K[:, c2] @ v) * K[:, c2]
+        nv = np.sqrt(v @ v)
+        if nv > 0 and nv > MGS_DROP * n0:
+            K[:, c] = v / nv
+    return K
+
+
+def dense_keys(S64, start_rows, iters):
+    """Keys of the dense compensator tokens of one state: subspace iteration
+    on S S^T from the one-hot keys of `start_rows` (fp64, [dk, r])."""
+    dk = S64.shape[0]
+    K = np.zeros((dk, len(start_rows)))
+    K[start_rows, np.arange(len(start_rows))] = 1.0
+    for _ in range(iters):
+        K = mgs(S64 @ (S64.T @ K))
+    return K
+
+
+def quantize(S, r, flags=0, iters=0):
+    """Split an fp32 state into compensator tokens + smoothed int8 residual.
 
     S: [n, dk, dv], values taken as fp32 (the reconstructed FP32 state of
     [EL] Figure 4).  Returns a dict with codes int8 [n,dk,dv], row_scale
     fp32 [n,dk], col_scale fp32 [n,dv], comp_idx int32 [n,r], comp_val fp32
-    [n,r,dv].
+    [n,r,dv]; with DENSE_COMP also comp_key fp32 [n,r,dk] (comp_idx then
+    holds the rows the subspace iteration started from).
     """
     S32 = np.asarray(S, dtype=_F32)
     n, dk, dv = S32.shape
@@ -158,12 +205,26 @@ def quantize(S, r, flags=0):
     norm2 = np.einsum("nij,nij->ni", S64, S64)
     # 2. top-r rows: descending norm, ties to the lower index (stable sort)
     comp_idx = np.argsort(-norm2, axis=1, kind="stable")[:, :r].astype(np.int32)
-    # 3. compensator rows keep their fp32 values
-    comp_val = np.take_along_axis(S32, comp_idx[:, :, None].astype(np.int64), axis=1).copy()
-    # 4. residual: extracted rows zeroed
-    R = S32.copy()
-    for s in range(n):
-        R[s, comp_idx[s], :] = 0
+    if flags & DENSE_COMP:
+        # 3'. dense keys, values w_c = S^T k_c from the fp32 keys, and the
+        # residual S - sum_c k_c w_c^T (fp64, rounded once to fp32)
+        comp_key = np.zeros((n, r, dk), _F32)
+        comp_val = np.zeros((n, r, dv), _F32)
+        R = np.zeros_like(S32)
+        for s in range(n):
+            K32 = dense_keys(S64[s], comp_idx[s], iters).astype(_F32)
+            K = K32.astype(np.float64)
+            W32 = (K.T @ S64[s]).astype(_F32)
+            comp_key[s] = K32.T
+            comp_val[s] = W32
+            R[s] = (S64[s] - K @ W32.astype(np.float64)).astype(_F32)
+    else:
+        # 3. compensator rows keep their fp32 values
+        comp_val = np.take_along_axis(S32, comp_idx[:, :, None].astype(np.int64), axis=1).copy()
+        # 4. residual: extracted rows zeroed
+        R = S32.copy()
+        for s in range(n):
+            R[s, comp_idx[s], :] = 0
     # 5. smoothing scale per value column (absmax of the residual column)
     if flags & NO_SMOOTH:
         col_scale = np.ones((n, dv), _F32)
@@ -183,8 +244,11 @@ def quantize(S, r, flags=0):
     # 8. codes: round half to even, clamp to the symmetric range
     X = (Q * inv[:, :, None]).astype(_F32)
     codes = np.clip(np.rint(X), -127, 127).astype(np.int8)
-    return {"codes": codes, "row_scale": row_scale, "col_scale": col_scale,
-            "comp_idx": comp_idx, "comp_val": comp_val}
+    out = {"codes": codes, "row_scale": row_scale, "col_scale": col_scale,
+           "comp_idx": comp_idx, "comp_val": comp_val}
+    if flags & DENSE_COMP:
+        out["comp_key"] = comp_key
+    return out
 
 
 def prerounding_codes(S, boundary):
@@ -195,9 +259,14 @@ def prerounding_codes(S, boundary):
     """
     S32 = np.asarray(S, dtype=_F32)
     n = S32.shape[0]
-    R = S32.copy()
-    for s in range(n):
-        R[s, boundary["comp_idx"][s], :] = 0
+    if "comp_key" in boundary:
+        K = boundary["comp_key"].astype(np.float64)
+        W = boundary["comp_val"].astype(np.float64)
+        R = (S32.astype(np.float64) - np.einsum("nci,ncj->nij", K, W)).astype(_F32)
+    else:
+        R = S32.copy()
+        for s in range(n):
+            R[s, boundary["comp_idx"][s], :] = 0
     sigma = (_F32(1) / boundary["col_scale"]).astype(_F32)
     Q = (R * sigma[:, None, :]).astype(_F32)
     m = np.abs(Q).max(axis=2).astype(_F32)
@@ -207,11 +276,15 @@ def prerounding_codes(S, boundary):
 
 
 def dequantize(boundary):
-    """Boundary state B = deQ(codes, a, s) + compensator rows, in fp64."""
+    """Boundary state B = deQ(codes, a, s) + compensator tokens, in fp64."""
     c = boundary["codes"].astype(np.float64)
     a = boundary["row_scale"].astype(np.float64)
     s = boundary["col_scale"].astype(np.float64)
     B = c * a[:, :, None] * s[:, None, :]
+    if "comp_key" in boundary:
+        K = boundary["comp_key"].astype(np.float64)
+        W = boundary["comp_val"].astype(np.float64)
+        return B + np.einsum("nci,ncj->nij", K, W)
     idx = boundary["comp_idx"]
     w = boundary["comp_val"].astype(np.float64)
     n, r = idx.shape
@@ -231,7 +304,7 @@ def copy_boundary(b, sel=None):
 # --------------------------------------------------------------------------
 # Per-window decode ([EL] Figure 2) and the per-token baseline
 # --------------------------------------------------------------------------
-def window(boundary, tokens, t0, length, gate, r, flags=0, quantizer=True):
+def window(boundary, tokens, t0, length, gate, r, flags=0, quantizer=True, iters=0):
     """Decode `length` tokens from `boundary`, then close the window.
 
     Tokens t0 .. t0+length-1 of `tokens` are used.  Returns
@@ -248,11 +321,11 @@ def window(boundary, tokens, t0, length, gate, r, flags=0, quantizer=True):
                          tokens["beta"][t], tokens["alpha"][t], gate, flags)
         outs.append(o)
         records.append(rec)
-    nxt = quantize(S, r, flags) if quantizer else S
+    nxt = quantize(S, r, flags, iters) if quantizer else S
     return np.stack(outs), records, S, nxt
 
 
-def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None):
+def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None, iters=0):
     """Free-running per-window quantized decode over all tokens.
 
     Returns (outputs [T, n, dv], boundaries) where boundaries[w] is the
@@ -262,7 +335,7 @@ def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None)
     last token.
     """
     T = tokens["q"].shape[0]
-    b = quantize(S_init, r, flags) if quantizer else np.array(S_init, np.float64, copy=True)
+    b = quantize(S_init, r, flags, iters) if quantizer else np.array(S_init, np.float64, copy=True)
     outs = []
     bounds = {}
     w = 0
@@ -273,7 +346,7 @@ def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None)
         if t0 >= T:
             break
         length = min(p, T - t0)
-        o, _, _, b = window(b, tokens, t0, length, gate, r, flags, quantizer)
+        o, _, _, b = window(b, tokens, t0, length, gate, r, flags, quantizer, iters)
         outs.append(o)
         t0 += length
         w += 1
@@ -281,19 +354,19 @@ def run_windowed(S_init, tokens, p, r, gate, flags=0, quantizer=True, keep=None)
     return np.concatenate(outs, axis=0), bounds
 
 
-def run_per_token(S_init, tokens, r, gate, flags=0):
+def run_per_token(S_init, tokens, r, gate, flags=0, iters=0):
     """Per-token quantization baseline ([EL] Figure 2, left): the whole state
     is re-quantized after every update; the token's output is read from the
     updated state before it is quantized."""
     T = tokens["q"].shape[0]
-    b = quantize(S_init, r, flags)
+    b = quantize(S_init, r, flags, iters)
     outs = []
     for t in range(T):
         S = dequantize(b)
         o, S, _ = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
                        tokens["beta"][t], tokens["alpha"][t], gate, flags)
         outs.append(o)
-        b = quantize(S, r, flags)
+        b = quantize(S, r, flags, iters)
     return np.stack(outs), b
 
 
