@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define LEAPQUANT_ABI_VERSION 2
+#define LEAPQUANT_ABI_VERSION 3
 
 typedef enum lq_status {
   LQ_OK = 0,
@@ -93,13 +93,32 @@ typedef enum lq_gate {
 
 enum {
   LQ_NO_SMOOTH = 1u, /* ablation: s_j = 1 for every column                     */
-  LQ_NO_DELTA = 2u   /* b_t = 0, so u_t = v_t: the rows of [EL] Appendix Table 4
+  LQ_NO_DELTA = 2u,  /* b_t = 0, so u_t = v_t: the rows of [EL] Appendix Table 4
                         without the delta correction.  With LQ_GATE_GDN: linear
                         attention (alpha = 1, beta = 1), RetNet (alpha = gamma,
                         beta = 1), Mamba2 (beta = 1); with LQ_GATE_KDA: GLA /
                         RWKV6 / HGRN2 (beta = 1).  DeltaNet is LQ_GATE_GDN with
                         alpha = 1 and the flag clear.                          */
+  LQ_DENSE_COMP = 4u /* compensator tokens with dense keys (below)             */
 };
+
+/* Dense compensator tokens (LQ_DENSE_COMP).  The compensators are r tokens
+ * (k_c, w_c) with dense fp32 keys k_c (comp_key) and values w_c (comp_val):
+ * the boundary state is B = deQ + sum_c k_c w_c^T, and a compensator enters
+ * the window like a buffered record written before the window's first token
+ * (decay Gamma, weight k_c . (Gamma * y), update w_c), so it shares the
+ * update path of real tokens ([EL] Abstract; Figure 4, where compensators
+ * capture the state's dominant large-magnitude structure).  The window
+ * close joins them to the fp32 rebuild as r more records of the same MFMA
+ * contraction (K = len + r).  The split finds the keys by comp_iters rounds
+ * of subspace iteration on S S^T started from the one-hot keys of the r
+ * largest-norm rows: K <- MGS(S S^T K), modified Gram-Schmidt in compensator
+ * order, a key whose projected norm is zero or at most 1e-3 of its norm
+ * before projection becoming the zero key.  Then w_c = S^T k_c and the
+ * residual S - sum_c k_c w_c^T is smoothed and quantized as usual; comp_idx
+ * receives the starting rows.  With comp_iters = 0 the keys are the one-hot
+ * rows and every result equals the row extraction's.  Without the flag,
+ * comp_key is neither read nor written and comp_iters is ignored. */
 
 typedef struct lq_params {
   int32_t n;      /* number of independent states in the slab (>= 1)     */
@@ -108,12 +127,14 @@ typedef struct lq_params {
   int32_t p;      /* window length in tokens, 1..64                       */
   int32_t r;      /* compensator rows per state, 0..16                    */
   int32_t gate;   /* lq_gate                                              */
-  uint32_t flags; /* LQ_NO_SMOOTH | LQ_NO_DELTA, or 0                      */
+  uint32_t flags; /* LQ_NO_SMOOTH | LQ_NO_DELTA | LQ_DENSE_COMP, or 0      */
+  int32_t comp_iters; /* LQ_DENSE_COMP: subspace iterations, 0..8         */
 } lq_params;
 
-/* One slab of n states.  The first five arrays are the boundary state
- * (the prefix-cache snapshot); the last three are the window buffer.  For
- * r == 0, comp_idx and comp_val may be NULL. */
+/* One slab of n states.  codes .. comp_val and comp_key are the boundary
+ * state (the prefix-cache snapshot); buf_gate, buf_k and buf_u are the
+ * window buffer.  For r == 0, comp_idx, comp_val and comp_key may be NULL;
+ * comp_key may be NULL without LQ_DENSE_COMP. */
 typedef struct lq_state {
   int8_t *codes;     /* [n][dk*dv]  int8 residual codes c_ij (layout above) */
   float *row_scale;  /* [n][dk]     a_i                                     */
@@ -123,6 +144,7 @@ typedef struct lq_state {
   float *buf_gate;   /* GDN: [n][p]; KDA: [n][p][dk]   d_i (alpha_i)        */
   float *buf_k;      /* [n][p][dk]  k~_i = beta_i k_i                       */
   float *buf_u;      /* [n][p][dv]  u_i                                     */
+  float *comp_key;   /* [n][r][dk]  LQ_DENSE_COMP: compensator keys k_c     */
 } lq_state;
 
 /* Split fp32 states S [n][dk][dv] into the boundary state of `st` (codes,

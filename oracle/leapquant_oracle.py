@@ -187,14 +187,16 @@ def dense_keys(S64, start_rows, iters):
     return K
 
 
-def quantize(S, r, flags=0, iters=0):
+def quantize(S, r, flags=0, iters=0, keys=None):
     """Split an fp32 state into compensator tokens + smoothed int8 residual.
 
     S: [n, dk, dv], values taken as fp32 (the reconstructed FP32 state of
     [EL] Figure 4).  Returns a dict with codes int8 [n,dk,dv], row_scale
     fp32 [n,dk], col_scale fp32 [n,dv], comp_idx int32 [n,r], comp_val fp32
     [n,r,dv]; with DENSE_COMP also comp_key fp32 [n,r,dk] (comp_idx then
-    holds the rows the subspace iteration started from).
+    holds the rows the subspace iteration started from).  `keys` (fp32
+    [n,r,dk], DENSE_COMP only) replaces the subspace iteration: the split
+    into values, residual and codes is then made with these keys.
     """
     S32 = np.asarray(S, dtype=_F32)
     n, dk, dv = S32.shape
@@ -212,7 +214,10 @@ def quantize(S, r, flags=0, iters=0):
         comp_val = np.zeros((n, r, dv), _F32)
         R = np.zeros_like(S32)
         for s in range(n):
-            K32 = dense_keys(S64[s], comp_idx[s], iters).astype(_F32)
+            if keys is not None:
+                K32 = np.asarray(keys[s], _F32).T
+            else:
+                K32 = dense_keys(S64[s], comp_idx[s], iters).astype(_F32)
             K = K32.astype(np.float64)
             W32 = (K.T @ S64[s]).astype(_F32)
             comp_key[s] = K32.T

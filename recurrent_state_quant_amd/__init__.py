@@ -6,7 +6,7 @@ smoothing, as hand-written HIP kernels behind the C ABI of
 include/leapquant.h.  This package is the thin Python binding: it marshals
 torch device tensors and streams into the C calls and runs nothing itself.
 """
-from ._lib import (LQ_DENSE_BF16, LQ_DENSE_FP32, LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_DELTA, LQ_NO_SMOOTH,
+from ._lib import (LQ_DENSE_BF16, LQ_DENSE_COMP, LQ_DENSE_FP32, LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_DELTA, LQ_NO_SMOOTH,
                    LeapQuantError, LIB_PATH, load)
 from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matrix,
                   leapquant_abi_version, leapquant_decode_close, leapquant_decode_step,
@@ -16,7 +16,7 @@ from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matr
                   leapquant_status_string, leapquant_window_close)
 
 __all__ = [
-    "LQ_DENSE_BF16", "LQ_DENSE_FP32", "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_DELTA", "LQ_NO_SMOOTH",
+    "LQ_DENSE_BF16", "LQ_DENSE_COMP", "LQ_DENSE_FP32", "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_DELTA", "LQ_NO_SMOOTH",
     "LeapQuantError", "LIB_PATH", "load",
     "LeapQuantState", "code_offsets", "codes_from_matrix", "codes_to_matrix",
     "leapquant_abi_version", "leapquant_decode_close", "leapquant_decode_step",

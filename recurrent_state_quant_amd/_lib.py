@@ -8,6 +8,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libleapquant.so")
 
+ABI_VERSION = 3  # the lq_params / lq_state layout these structures mirror
+
 LQ_OK = 0
 LQ_ERR_NULL = -1
 LQ_ERR_SHAPE = -2
@@ -20,6 +22,7 @@ LQ_GATE_GDN = 0
 LQ_GATE_KDA = 1
 LQ_NO_SMOOTH = 1
 LQ_NO_DELTA = 2
+LQ_DENSE_COMP = 4
 LQ_DENSE_FP32 = 0
 LQ_DENSE_BF16 = 1
 
@@ -41,14 +44,15 @@ EXPORTED = (
 class LqParams(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("p", ctypes.c_int32), ("r", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("comp_iters", ctypes.c_int32)]
 
 
 class LqState(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
                 ("col_scale", ctypes.c_void_p), ("comp_idx", ctypes.c_void_p),
                 ("comp_val", ctypes.c_void_p), ("buf_gate", ctypes.c_void_p),
-                ("buf_k", ctypes.c_void_p), ("buf_u", ctypes.c_void_p)]
+                ("buf_k", ctypes.c_void_p), ("buf_u", ctypes.c_void_p),
+                ("comp_key", ctypes.c_void_p)]
 
 
 class LeapQuantError(RuntimeError):
@@ -88,6 +92,9 @@ def load():
     lib.leapquant_status_string.restype = ctypes.c_char_p
     lib.leapquant_abi_version.argtypes = []
     lib.leapquant_abi_version.restype = ctypes.c_int
+    if lib.leapquant_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.leapquant_abi_version()}, "
+                          f"this binding needs {ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 

@@ -85,15 +85,18 @@ class LeapQuantState:
     codes int8 [n][dk*dv] in the stored layout (see code_offsets);
     row_scale [n,dk]; col_scale [n,dv]; comp_idx int32 [n,r]; comp_val
     [n,r,dv]; buf_gate [n,p] (gdn) or [n,p,dk] (kda); buf_k [n,p,dk];
-    buf_u [n,p,dv].
+    buf_u [n,p,dv].  With LQ_DENSE_COMP in flags also comp_key [n,r,dk]
+    (dense compensator keys, found by comp_iters rounds of subspace
+    iteration at every split).
     """
 
     BOUNDARY = ("codes", "row_scale", "col_scale", "comp_idx", "comp_val")
 
-    def __init__(self, n, p, r, gate="gdn", device="cuda", flags=0, dk=128, dv=128):
+    def __init__(self, n, p, r, gate="gdn", device="cuda", flags=0, dk=128, dv=128, comp_iters=0):
         self.n, self.p, self.r, self.dk, self.dv = int(n), int(p), int(r), int(dk), int(dv)
         self.gate = _gate_id(gate)
         self.flags = int(flags)
+        self.comp_iters = int(comp_iters)
         dev = torch.device(device)
         self.device = dev
         self.codes = torch.zeros((n, dk * dv), dtype=_I8, device=dev)
@@ -105,9 +108,21 @@ class LeapQuantState:
         self.buf_gate = torch.zeros(gshape, dtype=_F32, device=dev)
         self.buf_k = torch.zeros((n, p, dk), dtype=_F32, device=dev)
         self.buf_u = torch.zeros((n, p, dv), dtype=_F32, device=dev)
+        self.comp_key = torch.zeros((n, r, dk) if self.dense else (0,), dtype=_F32, device=dev)
+
+    @property
+    def dense(self):
+        """Dense compensator keys (LQ_DENSE_COMP)."""
+        return bool(self.flags & L.LQ_DENSE_COMP)
+
+    @property
+    def boundary_keys(self):
+        """Names of the boundary-state arrays of this slab."""
+        return self.BOUNDARY + (("comp_key",) if self.dense else ())
 
     def params(self):
-        return L.LqParams(self.n, self.dk, self.dv, self.p, self.r, self.gate, self.flags)
+        return L.LqParams(self.n, self.dk, self.dv, self.p, self.r, self.gate, self.flags,
+                          self.comp_iters)
 
     def view(self, start, count):
         """States start .. start+count-1 of this slab as a slab of their own
@@ -118,9 +133,10 @@ class LeapQuantState:
             raise ValueError("view out of range")
         v = object.__new__(LeapQuantState)
         v.n, v.p, v.r, v.dk, v.dv = int(count), self.p, self.r, self.dk, self.dv
-        v.gate, v.flags, v.device = self.gate, self.flags, self.device
+        v.gate, v.flags, v.device, v.comp_iters = self.gate, self.flags, self.device, self.comp_iters
         for k in self.BOUNDARY + ("buf_gate", "buf_k", "buf_u"):
             setattr(v, k, getattr(self, k)[start:start + count])
+        v.comp_key = self.comp_key[start:start + count] if self.dense else self.comp_key
         return v
 
     def ptrs(self):
@@ -128,7 +144,7 @@ class LeapQuantState:
             return x.data_ptr() if x.numel() else None
         return L.LqState(vp(self.codes), vp(self.row_scale), vp(self.col_scale),
                          vp(self.comp_idx), vp(self.comp_val), vp(self.buf_gate),
-                         vp(self.buf_k), vp(self.buf_u))
+                         vp(self.buf_k), vp(self.buf_u), vp(self.comp_key))
 
     def _index(self, idx):
         if idx is None:
@@ -140,7 +156,7 @@ class LeapQuantState:
         the codes as row-major int8 matrices [m][dk][dv]."""
         ix = self._index(idx)
         out = {}
-        for k in self.BOUNDARY:
+        for k in self.boundary_keys:
             x = getattr(self, k)
             x = x.clone() if ix is None else x.index_select(0, ix)
             out[k] = codes_to_matrix(x) if k == "codes" else x
@@ -154,7 +170,7 @@ class LeapQuantState:
         """Write a boundary state (dict of tensors or arrays, codes as
         row-major matrices [m][dk][dv]) into all states or into states idx."""
         ix = self._index(idx)
-        for k in self.BOUNDARY:
+        for k in self.boundary_keys:
             dst = getattr(self, k)
             src = torch.as_tensor(b[k]).to(device=dst.device, dtype=dst.dtype)
             if k == "codes":

@@ -10,6 +10,7 @@ namespace {
 constexpr int kDim = 128;
 constexpr int kMaxP = 64;
 constexpr int kMaxR = 16;
+constexpr int kMaxIters = 8;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -27,8 +28,18 @@ int check_params(const lq_params *prm) {
   if (prm->dk != kDim || prm->dv != kDim) return LQ_ERR_UNSUPPORTED;
   if (prm->n < 1 || prm->p < 1 || prm->p > kMaxP || prm->r < 0 || prm->r > kMaxR) return LQ_ERR_SHAPE;
   if (prm->gate != LQ_GATE_GDN && prm->gate != LQ_GATE_KDA) return LQ_ERR_SHAPE;
-  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_SMOOTH | LQ_NO_DELTA)) return LQ_ERR_SHAPE;
+  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_SMOOTH | LQ_NO_DELTA | LQ_DENSE_COMP))
+    return LQ_ERR_SHAPE;
+  if (prm->comp_iters < 0 || prm->comp_iters > kMaxIters) return LQ_ERR_SHAPE;
   return LQ_OK;
+}
+
+bool dense_comp(const lq_params *prm) { return (prm->flags & LQ_DENSE_COMP) && prm->r > 0; }
+
+// Byte range of the compensator keys (empty without dense compensators).
+Range key_span(const lq_params *prm, const lq_state *st) {
+  if (!dense_comp(prm)) return Range{0, 0};
+  return span(st->comp_key, static_cast<size_t>(prm->n) * prm->r * kDim * sizeof(float));
 }
 
 // Boundary-state arrays (always needed).
@@ -39,6 +50,10 @@ int check_boundary(const lq_params *prm, const lq_state *st) {
   if (!aligned(st->codes, 16) || !aligned(st->row_scale, 16) || !aligned(st->col_scale, 16))
     return LQ_ERR_ALIGN;
   if (prm->r > 0 && (!aligned(st->comp_idx, 4) || !aligned(st->comp_val, 16))) return LQ_ERR_ALIGN;
+  if (dense_comp(prm)) {
+    if (!st->comp_key) return LQ_ERR_NULL;
+    if (!aligned(st->comp_key, 16)) return LQ_ERR_ALIGN;
+  }
   return LQ_OK;
 }
 
@@ -84,7 +99,8 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
       overlap(src, span(st->row_scale, n * kDim * sizeof(float))) ||
       overlap(src, span(st->col_scale, n * kDim * sizeof(float))) ||
       (prm->r > 0 && (overlap(src, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(src, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+                      overlap(src, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
+      overlap(src, key_span(prm, st)))
     return LQ_ERR_ALIAS;
   lq::CloseArgs a{};
   a.codes = st->codes;
@@ -92,6 +108,8 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  a.iters = prm->comp_iters;
   a.S_in = S;
   a.n = prm->n;
   a.p = prm->p;
@@ -133,7 +151,8 @@ int check_token_call(const lq_params *prm, const lq_state *st, int32_t t, const 
       overlap(out, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
       overlap(out, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
       (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
+      overlap(out, key_span(prm, st)))
     return LQ_ERR_ALIAS;
   return LQ_OK;
 }
@@ -154,6 +173,7 @@ int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, c
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -184,6 +204,7 @@ int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -193,6 +214,7 @@ int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len
   a.r = prm->r;
   a.len = len;
   a.flags = prm->flags;
+  a.iters = prm->comp_iters;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -207,6 +229,7 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t, 
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -222,6 +245,7 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t, 
   a.r = prm->r;
   a.len = t;
   a.flags = prm->flags;
+  a.iters = prm->comp_iters;
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -240,7 +264,8 @@ static int check_slots(const lq_params *prm, const lq_state *st, const int32_t *
       overlap(in, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
       overlap(in, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
       (prm->r > 0 && (overlap(in, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(in, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+                      overlap(in, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
+      overlap(in, key_span(prm, st)))
     return LQ_ERR_ALIAS;
   return LQ_OK;
 }
@@ -257,6 +282,7 @@ int leapquant_decode_step_slots(const lq_params *prm, const lq_state *st, const 
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -287,6 +313,7 @@ int leapquant_decode_close_slots(const lq_params *prm, const lq_state *st, const
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -302,6 +329,7 @@ int leapquant_decode_close_slots(const lq_params *prm, const lq_state *st, const
   a.r = prm->r;
   a.len = 0;
   a.flags = prm->flags;
+  a.iters = prm->comp_iters;
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -318,6 +346,7 @@ int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const
   a.col_scale = st->col_scale;
   a.comp_idx = st->comp_idx;
   a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.buf_gate = st->buf_gate;
   a.buf_k = st->buf_k;
   a.buf_u = st->buf_u;
@@ -327,6 +356,7 @@ int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const
   a.r = prm->r;
   a.len = 1;
   a.flags = prm->flags;
+  a.iters = prm->comp_iters;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -376,9 +406,11 @@ int leapquant_dequantize_state(const lq_params *prm, const lq_state *st, float *
       overlap(out, span(st->row_scale, n * kDim * sizeof(float))) ||
       overlap(out, span(st->col_scale, n * kDim * sizeof(float))) ||
       (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))))
+                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
+      overlap(out, key_span(prm, st)))
     return LQ_ERR_ALIAS;
   lq::DequantArgs a{};
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
   a.codes = st->codes;
   a.row_scale = st->row_scale;
   a.col_scale = st->col_scale;

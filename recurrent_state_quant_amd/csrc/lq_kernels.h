@@ -12,6 +12,7 @@ struct DecodeArgs {
   const float *col_scale;
   const int32_t *comp_idx;
   const float *comp_val;
+  const float *comp_key;  // dense compensator keys [n][r][dk] (nullptr: one-hot rows)
   float *buf_gate;
   float *buf_k;
   float *buf_u;
@@ -32,6 +33,7 @@ struct CloseArgs {
   float *col_scale;
   int32_t *comp_idx;
   float *comp_val;
+  float *comp_key;    // dense compensator keys [n][r][dk] (nullptr: one-hot rows)
   const float *buf_gate;
   const float *buf_k;
   const float *buf_u;
@@ -43,6 +45,7 @@ struct CloseArgs {
   // last token's window position
   const int32_t *lens;
   int n, p, r, len;  // len: buffered records the rebuild replays
+  int iters;         // dense compensators: subspace iterations of the split
   unsigned flags;
 };
 
@@ -52,6 +55,7 @@ struct DequantArgs {
   const float *col_scale;
   const int32_t *comp_idx;
   const float *comp_val;
+  const float *comp_key;  // dense compensator keys (nullptr: one-hot rows)
   float *S_out;
   int n, r;
 };

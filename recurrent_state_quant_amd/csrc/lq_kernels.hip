@@ -174,7 +174,7 @@ __device__ __forceinline__ uint32_t digits4(int x0) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-template <bool KDA>
+template <bool KDA, bool DENSE>
 __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   const int lane = threadIdx.x;
@@ -185,6 +185,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 
   __shared__ float2 sh_gy[D];  // Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_h[64];  // record weights (h_b, h_q)
+  __shared__ float2 sh_hc[DENSE ? 16 : 1];  // dense compensator weights (h_b, h_q)
   __shared__ float2 sh_z[D];   // GEMV result (z_b, z_q) per column
   __shared__ __attribute__((aligned(16))) uint8_t sh_dig[8 * 2 * 64];  // [vector*4+digit][half][slot]
   __shared__ __attribute__((aligned(16))) float sh_red[64 * kRedStride];
@@ -222,10 +223,12 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   load_chunk(lo, hi - lo);
   int cidx[kCompEarly];
   float2 cw[kCompEarly];
+  float2 ck[DENSE ? kCompEarly : 1];  // dense keys, rows 2l and 2l+1
 #pragma unroll
   for (int c = 0; c < kCompEarly; ++c) {
     if (c < r) {
-      cidx[c] = A.comp_idx[(size_t)s * r + c];
+      if constexpr (DENSE) ck[c] = ld2(A.comp_key + ((size_t)s * r + c) * D + 2 * lane);
+      else cidx[c] = A.comp_idx[(size_t)s * r + c];
       cw[c] = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
     }
   }
@@ -298,6 +301,38 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     hi = lo;
     lo = hi > kRecChunk ? hi - kRecChunk : 0;
     if (hi > 0) load_chunk(lo, hi - lo);
+  }
+  // ---- dense compensator tokens: records written before the window's
+  // first token (decay Gamma), weights h_c = k_c . (Gamma * y)
+  if constexpr (DENSE) {
+    const float2 G = KDA ? Pk : make_float2(Pg, Pg);
+    const float2 gb = make_float2(G.x * yb.x, G.y * yb.y);
+    const float2 gq = make_float2(G.x * yq.x, G.y * yq.y);
+    float *red = sh_red + lane * kRedStride;
+#pragma unroll
+    for (int c = 0; c < kCompEarly; ++c) {
+      if (c < r) {
+        red[2 * c] = ck[c].x * gb.x + ck[c].y * gb.y;
+        red[2 * c + 1] = ck[c].x * gq.x + ck[c].y * gq.y;
+      }
+    }
+    for (int c = kCompEarly; c < r; ++c) {
+      const float2 kc = ld2(A.comp_key + ((size_t)s * r + c) * D + 2 * lane);
+      red[2 * c] = kc.x * gb.x + kc.y * gb.y;
+      red[2 * c + 1] = kc.x * gq.x + kc.y * gq.y;
+    }
+    __syncthreads();
+    {
+      const int v = lane & 31, half = lane >> 5;
+      float acc = 0.f;
+      if (v < 2 * r) {
+#pragma unroll 8
+        for (int m = 0; m < 32; ++m) acc += sh_red[(32 * half + m) * kRedStride + v];
+      }
+      acc += __shfl_xor(acc, 32);
+      if (lane < 2 * r) reinterpret_cast<float *>(&sh_hc[lane >> 1])[lane & 1] = acc;
+    }
+    __syncthreads();
   }
   // U of the newest chunk, in flight during the GEMV
   const int ulo = t > kRecChunk ? t - kRecChunk : 0;
@@ -375,21 +410,38 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     zb.x *= sc.x; zb.y *= sc.y;
     zq.x *= sc.x; zq.y *= sc.y;
   }
+  if constexpr (DENSE) {
 #pragma unroll
-  for (int c = 0; c < kCompEarly; ++c) {
-    if (c < r && (unsigned)cidx[c] < (unsigned)D) {
-      const float2 gg = sh_gy[cidx[c]];
-      zb.x = fmaf(cw[c].x, gg.x, zb.x); zb.y = fmaf(cw[c].y, gg.x, zb.y);
-      zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
+    for (int c = 0; c < kCompEarly; ++c) {
+      if (c < r) {
+        const float2 gg = sh_hc[c];
+        zb.x = fmaf(cw[c].x, gg.x, zb.x); zb.y = fmaf(cw[c].y, gg.x, zb.y);
+        zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
+      }
     }
-  }
-  for (int c = kCompEarly; c < r; ++c) {
-    const int idx = A.comp_idx[(size_t)s * r + c];
-    if ((unsigned)idx < (unsigned)D) {
-      const float2 gg = sh_gy[idx];
+    for (int c = kCompEarly; c < r; ++c) {
+      const float2 gg = sh_hc[c];
       const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
       zb.x = fmaf(w.x, gg.x, zb.x); zb.y = fmaf(w.y, gg.x, zb.y);
       zq.x = fmaf(w.x, gg.y, zq.x); zq.y = fmaf(w.y, gg.y, zq.y);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < kCompEarly; ++c) {
+      if (c < r && (unsigned)cidx[c] < (unsigned)D) {
+        const float2 gg = sh_gy[cidx[c]];
+        zb.x = fmaf(cw[c].x, gg.x, zb.x); zb.y = fmaf(cw[c].y, gg.x, zb.y);
+        zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
+      }
+    }
+    for (int c = kCompEarly; c < r; ++c) {
+      const int idx = A.comp_idx[(size_t)s * r + c];
+      if ((unsigned)idx < (unsigned)D) {
+        const float2 gg = sh_gy[idx];
+        const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
+        zb.x = fmaf(w.x, gg.x, zb.x); zb.y = fmaf(w.y, gg.x, zb.y);
+        zq.x = fmaf(w.x, gg.y, zq.x); zq.y = fmaf(w.y, gg.y, zq.y);
+      }
     }
   }
   {
@@ -425,7 +477,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 // waves: with n <= 4,096 this fills the chip where one wave per state would
 // not (measured: +5% at 2,048 states, +18% for KDA at 4,096), while at
 // 8,192 states and more the one-wave kernel is faster (1.6%).
-template <bool KDA>
+template <bool KDA, bool DENSE>
 __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -438,6 +490,7 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
 
   __shared__ float2 sh_gy[D];           // Gamma_i * (y_b, y_q)_i
   __shared__ float2 sh_hp[2][64];       // per-wave partial record dots
+  __shared__ float2 sh_hcp[2][DENSE ? 16 : 1];  // per-wave partial dense compensator dots
   __shared__ float2 sh_z[2][D];         // per-wave GEMV partials (z_b, z_q)
   __shared__ float sh_kq[2];
   __shared__ __attribute__((aligned(16))) uint8_t sh_dig[2][8 * 64];  // [wave][vector*4+digit][slot]
@@ -466,10 +519,12 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   load_chunk(lo, hi - lo);
   int cidx[kCompEarly];
   float cw[kCompEarly];
+  float ck[DENSE ? kCompEarly : 1];  // dense keys at this lane's row
 #pragma unroll
   for (int c = 0; c < kCompEarly; ++c) {
     if (c < r) {
-      cidx[c] = A.comp_idx[(size_t)s * r + c];
+      if constexpr (DENSE) ck[c] = A.comp_key[((size_t)s * r + c) * D + row];
+      else cidx[c] = A.comp_idx[(size_t)s * r + c];
       cw[c] = A.comp_val[((size_t)s * r + c) * D + col];
     }
   }
@@ -534,6 +589,37 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
     lo = hi > kRecChunk ? hi - kRecChunk : 0;
     if (hi > 0) load_chunk(lo, hi - lo);
   }
+  // ---- dense compensator tokens: records written before the window's
+  // first token (decay Gamma); this wave's partial k_c . (Gamma * y)
+  if constexpr (DENSE) {
+    const float gb = P * yb, gq = P * yq;
+    auto put = [&](int c, float kc) {
+      float hb = kc * gb, hq = kc * gq;
+      hb += dpp<0xB1>(hb);  // pairs of rows
+      hq += dpp<0xB1>(hq);
+      if ((lane & 1) == 0) {
+        red[(lane >> 1) * kRedStride + 2 * c] = hb;
+        red[(lane >> 1) * kRedStride + 2 * c + 1] = hq;
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < kCompEarly; ++c)
+      if (c < r) put(c, ck[c]);
+    for (int c = kCompEarly; c < r; ++c) put(c, A.comp_key[((size_t)s * r + c) * D + row]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      const int v = lane & 31, half = lane >> 5;
+      float acc = 0.f;
+      if (v < 2 * r) {
+#pragma unroll 8
+        for (int m = 0; m < 16; ++m) acc += red[(16 * half + m) * kRedStride + v];
+      }
+      acc += __shfl_xor(acc, 32);
+      if (lane < 2 * r) reinterpret_cast<float *>(&sh_hcp[w][lane >> 1])[lane & 1] = acc;
+    }
+  }
   // u rows of this wave's columns, in flight during the GEMV
   const int ulo = t > kRecChunk ? t - kRecChunk : 0;
   float ur[kRecChunk];
@@ -588,21 +674,38 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
     zb *= sc;
     zq *= sc;
   }
+  if constexpr (DENSE) {
 #pragma unroll
-  for (int c = 0; c < kCompEarly; ++c) {
-    if (c < r && (unsigned)cidx[c] < (unsigned)D) {
-      const float2 gg = sh_gy[cidx[c]];
-      zb = fmaf(cw[c], gg.x, zb);
-      zq = fmaf(cw[c], gg.y, zq);
+    for (int c = 0; c < kCompEarly; ++c) {
+      if (c < r) {
+        const float2 h0 = sh_hcp[0][c], h1 = sh_hcp[1][c];
+        zb = fmaf(cw[c], h0.x + h1.x, zb);
+        zq = fmaf(cw[c], h0.y + h1.y, zq);
+      }
     }
-  }
-  for (int c = kCompEarly; c < r; ++c) {
-    const int idx = A.comp_idx[(size_t)s * r + c];
-    if ((unsigned)idx < (unsigned)D) {
-      const float2 gg = sh_gy[idx];
+    for (int c = kCompEarly; c < r; ++c) {
+      const float2 h0 = sh_hcp[0][c], h1 = sh_hcp[1][c];
       const float wv = A.comp_val[((size_t)s * r + c) * D + col];
-      zb = fmaf(wv, gg.x, zb);
-      zq = fmaf(wv, gg.y, zq);
+      zb = fmaf(wv, h0.x + h1.x, zb);
+      zq = fmaf(wv, h0.y + h1.y, zq);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < kCompEarly; ++c) {
+      if (c < r && (unsigned)cidx[c] < (unsigned)D) {
+        const float2 gg = sh_gy[cidx[c]];
+        zb = fmaf(cw[c], gg.x, zb);
+        zq = fmaf(cw[c], gg.y, zq);
+      }
+    }
+    for (int c = kCompEarly; c < r; ++c) {
+      const int idx = A.comp_idx[(size_t)s * r + c];
+      if ((unsigned)idx < (unsigned)D) {
+        const float2 gg = sh_gy[idx];
+        const float wv = A.comp_val[((size_t)s * r + c) * D + col];
+        zb = fmaf(wv, gg.x, zb);
+        zq = fmaf(wv, gg.y, zq);
+      }
     }
   }
   {
@@ -692,14 +795,138 @@ struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
   float *cmx;        // [8][D] column-max partials
   float *sig;        // [D] 1 / s_j
   float *inv;        // [D] 127 / m_i (0 for zero or extracted rows)
+  // dense compensator tokens only, [16][D] each
+  float *dq;         // keys K (row c: k_c)
+  float *dw;         // W = K S (row c: w_c)
+  float *dy;         // Y = S W^T (row c: column c of Y)
 };
 
+constexpr float kMgsDrop = 1e-3f;  // relative projected norm at or below which a key is dropped
+
+// Dense compensator tokens of the state in acc (r >= 1), after the top-r
+// rows have set one-hot keys in L.dq: `iters` rounds of subspace iteration
+// K <- MGS(S S^T K), then W = K S (w_c = S^T k_c), the keys and values
+// written out, and the residual S - sum_c k_c w_c^T left in acc.  Partial
+// sums of the two row halves (W) and of the two column halves (Y) meet in
+// LDS: one half stores into a free [16][D] array, then all threads add.
+__device__ __forceinline__ void dense_comp_split(floatx4 (&acc)[4][4], const SplitLds &L, float *comp_key,
+                                                 float *comp_val, size_t s, int r, int iters) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;
+  const int col0 = 64 * ch + lc;
+  // dst[e] += src[e] for the r rows of [16][D] arrays, all threads
+  auto add_halves = [&](float *dst, const float *src) {
+    for (int e = tid; e < r * (D / 4); e += 256) {
+      float4 x = reinterpret_cast<float4 *>(dst)[e];
+      const float4 y = reinterpret_cast<const float4 *>(src)[e];
+      x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      reinterpret_cast<float4 *>(dst)[e] = x;
+    }
+  };
+  for (int it = 0;; ++it) {
+    // ---- W = K S: each lane sums its 16 rows of the half, lanes 16 and 32
+    // apart hold the half's other rows; halves meet in dw (h = 0) + dy (h = 1)
+    float *wdst = h == 0 ? L.dw : L.dy;
+    for (int c = 0; c < r; ++c) {
+      float pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 k4 = *reinterpret_cast<const float4 *>(L.dq + c * D + rbase + 16 * rt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) pw[ct] = fmaf(f4get(k4, v), acc[rt][ct][v], pw[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        pw[ct] += __shfl_xor(pw[ct], 16);
+        pw[ct] += __shfl_xor(pw[ct], 32);
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) wdst[c * D + col0 + 16 * ct] = pw[ct];
+      }
+    }
+    __syncthreads();
+    add_halves(L.dw, L.dy);
+    __syncthreads();
+    if (it == iters) break;
+    // ---- Y = S W^T: each lane sums its 4 columns, the 16 lanes of a DPP
+    // row hold the half's other columns; halves meet in dy (ch = 0) + dq
+    // (ch = 1: the keys are not read again this round)
+    float *ydst = ch == 0 ? L.dy : L.dq;
+    for (int c = 0; c < r; ++c) {
+      float wv[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) wv[ct] = L.dw[c * D + col0 + 16 * ct];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) x = fmaf(acc[rt][ct][v], wv[ct], x);
+          y[v] = row16_sum(x);
+        }
+        if (lc == 0)
+          *reinterpret_cast<float4 *>(ydst + c * D + rbase + 16 * rt) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+    __syncthreads();
+    add_halves(L.dy, L.dq);
+    __syncthreads();
+    // ---- K = MGS(Y) on wave 0: lane l holds rows 2l and 2l+1
+    if (w == 0) {
+      for (int c = 0; c < r; ++c) {
+        float2 v = *reinterpret_cast<const float2 *>(L.dy + c * D + 2 * lane);
+        const float n0 = sqrtf(wave_sum(v.x * v.x + v.y * v.y));
+        for (int c2 = 0; c2 < c; ++c2) {
+          const float2 q = *reinterpret_cast<const float2 *>(L.dq + c2 * D + 2 * lane);
+          const float d = wave_sum(q.x * v.x + q.y * v.y);
+          v.x = fmaf(-d, q.x, v.x);
+          v.y = fmaf(-d, q.y, v.y);
+        }
+        const float nv = sqrtf(wave_sum(v.x * v.x + v.y * v.y));
+        const bool keep = nv > 0.f && nv > kMgsDrop * n0;
+        *reinterpret_cast<float2 *>(L.dq + c * D + 2 * lane) =
+            keep ? make_float2(v.x / nv, v.y / nv) : make_float2(0.f, 0.f);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- keys and values out; residual S - sum_c k_c w_c^T
+  for (int e = tid; e < r * (D / 4); e += 256) {
+    reinterpret_cast<float4 *>(comp_key + s * r * D)[e] = reinterpret_cast<const float4 *>(L.dq)[e];
+    reinterpret_cast<float4 *>(comp_val + s * r * D)[e] = reinterpret_cast<const float4 *>(L.dw)[e];
+  }
+  for (int c = 0; c < r; ++c) {
+    float wv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) wv[ct] = L.dw[c * D + col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(L.dq + c * D + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(-f4get(k4, v), wv[ct], acc[rt][ct][v]);
+    }
+  }
+}
+
 // a6-a8 on the fp32 state held in acc: row norms, top-r extraction (writes
-// comp_idx, comp_val), smoothing scales (col_scale), row scales (row_scale)
-// and int8 codes, all for state s.  Ends with every LDS array consumed.
+// comp_idx, comp_val; with DENSE the dense tokens started from those rows,
+// also comp_key), smoothing scales (col_scale), row scales (row_scale) and
+// int8 codes, all for state s.  Ends with every LDS array consumed.
+template <bool DENSE>
 __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds &L, int8_t *codes,
                                             float *row_scale, float *col_scale, int32_t *comp_idx,
-                                            float *comp_val, size_t s, int r, unsigned flags) {
+                                            float *comp_val, float *comp_key, size_t s, int r, int iters,
+                                            unsigned flags) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
@@ -718,6 +945,8 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
       if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = q;
     }
   if (tid < D) L.sel[tid] = -1;
+  if (DENSE)
+    for (int e = tid; e < r * D; e += 256) L.dq[e] = 0.f;
   __syncthreads();
   if (w == 0 && r > 0) {
     // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
@@ -748,7 +977,8 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
         if (odd) n1 = -1.f; else n0 = -1.f;
       }
       if (lane == 0) {
-        L.sel[wrow] = c;
+        if (DENSE) L.dq[c * D + wrow] = 1.f;  // one-hot start key
+        else L.sel[wrow] = c;
         comp_idx[s * r + c] = wrow;
       }
     }
@@ -758,7 +988,11 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
   // ---- extraction and a7 column absmax of the residual.  Extracted rows
   // are written out and zeroed in the lanes that hold them (a branch that
   // most waves skip), so they drop out of the column maxima and get row
-  // scale 0 (hence codes 0) below.
+  // scale 0 (hence codes 0) below.  DENSE: the dense tokens leave the
+  // residual S - sum_c k_c w_c^T instead.
+  if constexpr (DENSE) {
+    if (r > 0) dense_comp_split(acc, L, comp_key, comp_val, s, r, iters);
+  } else {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int4 sl4 = *reinterpret_cast<const int4 *>(L.sel + rbase + 16 * rt);
@@ -772,6 +1006,7 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
         for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = 0.f;
       }
     }
+  }
   }
   float cm[4];
 #pragma unroll
@@ -854,6 +1089,7 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
 }
 
 // ---- a9: split a caller fp32 state (one workgroup per state)
+template <bool DENSE>
 __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
   const size_t s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -864,6 +1100,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
   __shared__ __attribute__((aligned(16))) float sh_inv[D];
   __shared__ __attribute__((aligned(16))) int sh_sel[D];
   __shared__ __attribute__((aligned(16))) float sh_cmx[8 * D];
+  __shared__ __attribute__((aligned(16))) float sh_dq[DENSE ? 16 * D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_dw[DENSE ? 16 * D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_dy[DENSE ? 16 * D : 4];
   floatx4 acc[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -874,8 +1113,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
       for (int ct = 0; ct < 4; ++ct)
         acc[rt][ct][v] = __builtin_nontemporal_load(A.S_in + (s * D + row) * D + 64 * ch + 16 * ct + lc);
     }
-  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv};
-  split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, A.r, A.flags);
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv, sh_dq, sh_dw, sh_dy};
+  split_state<DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s,
+                     A.r, A.iters, A.flags);
 }
 
 // ---- a5-a8: window close, one workgroup per state.  With FUSED the
@@ -884,7 +1124,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
 // D_t S_{t-1}; then z = (D_t S_{t-1})^T k_t = S_{t-1}^T b_t and
 // (D_t S_{t-1})^T q_t = S_{t-1}^T (alpha_t q_t), u_t = v_t - z_b,
 // o_t = z_q + (k~_t . q_t) u_t, and S_t = D_t S_{t-1} + k~_t u_t^T is split.
-template <bool KDA, bool FUSED>
+template <bool KDA, bool FUSED, bool DENSE>
 __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   const size_t s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -905,7 +1145,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : kChunk];
   __shared__ __attribute__((aligned(16))) float sh_a[D];
   __shared__ __attribute__((aligned(16))) float sh_ag[D];  // a_i * Gamma_i
-  __shared__ float sh_gam[D];
+  __shared__ __attribute__((aligned(16))) float sh_gam[D];
   __shared__ __attribute__((aligned(16))) float sh_s[D];
   __shared__ __attribute__((aligned(16))) int sh_cslot[D];  // compensator slot of a row or -1
   __shared__ __attribute__((aligned(16))) float sh_comp[16 * D];  // compensator rows w_c
@@ -949,7 +1189,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       }
     }
     // compensator rows: the lanes holding row idx_c add Gamma_idx * w_c
-    // (sh_cslot maps a row to its compensator slot or -1)
+    // (sh_cslot maps a row to its compensator slot or -1); dense tokens
+    // join the contraction instead
+    if (DENSE) return;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int4 cs4 = *reinterpret_cast<const int4 *>(sh_cslot + rbase + 16 * rt);
@@ -989,7 +1231,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       const int e0 = tid, e1 = tid + 256;
       // the compensator rows (r * 32 float4) come with the first chunk;
       // rows 8 .. r-1 (r > 8 only) follow it
-      const int ncv = first ? r * (D / 4) : 0;
+      const int ncv = (first && !DENSE) ? r * (D / 4) : 0;
       float4 c0 = z4;
       if (e0 < ncv) c0 = ld4(A.comp_val + s * r * D + 4 * e0);
       float tk = 0.f, tq = 0.f, tv = 0.f, tb = 0.f;
@@ -1065,7 +1307,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
       sh_gam[tid] = P;
       sh_ag[tid] = sh_a[tid] * P;
     }
-    if (tid < r) {
+    if (!DENSE && tid < r) {
       // comp_idx entries outside [0, dk) are ignored
       const int idx = A.comp_idx[s * r + tid];
       if ((unsigned)idx < (unsigned)D) sh_cslot[idx] = tid;
@@ -1101,6 +1343,30 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
     }
     set_gamma();
     add_boundary(false);
+  }
+  if (DENSE && r > 0) {
+    // dense compensator tokens: r more records of the contraction, written
+    // before the window's first token: K column Gamma * k_c, U row w_c
+    __syncthreads();  // every wave is done with the staged records
+    {
+      const int r4 = (r + 3) & ~3;
+      float4 *dk = reinterpret_cast<float4 *>(sh_K);
+      float4 *du = reinterpret_cast<float4 *>(sh_U);
+      for (int e = tid; e < r4 * (D / 4); e += 256) {
+        const int c = e >> 5, i4 = e & 31;
+        float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), ww = kk;
+        if (c < r) {
+          kk = ld4(A.comp_key + (s * r + c) * D + 4 * i4);
+          ww = ld4(A.comp_val + (s * r + c) * D + 4 * i4);
+          const float4 g = *reinterpret_cast<const float4 *>(sh_gam + 4 * i4);
+          kk.x *= g.x; kk.y *= g.y; kk.z *= g.z; kk.w *= g.w;
+        }
+        dk[e] = kk;
+        du[e] = ww;
+      }
+    }
+    __syncthreads();
+    contract(r);
   }
   if (FUSED) {
     // z = acc^T k_t and acc^T q_t: each lane sums its 16 rows for its 4
@@ -1152,8 +1418,9 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
   // every read of this state's compensator rows is done before the split
   // overwrites them
   __syncthreads();
-  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv};
-  split_state(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, s, r, A.flags);
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv, sh_K, sh_U, sh_comp};
+  split_state<DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s, r,
+                     A.iters, A.flags);
 }
 
 // ---------------------------------------------------------------------------
@@ -1161,6 +1428,7 @@ __global__ __launch_bounds__(256) void close_kernel(const CloseArgs A) {
 // (half hh, column j) reads the 64 code bytes of its column segment and
 // writes column j of rows 64hh .. 64hh+63.
 // ---------------------------------------------------------------------------
+template <bool DENSE>
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
   const size_t s = blockIdx.x;
   const int j = threadIdx.x & (D - 1), hh = threadIdx.x >> 7;
@@ -1175,8 +1443,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
       const int row = 64 * hh + code_slot(slot);  // the slot map is its own inverse
       const uint32_t wd = u4get(cq, e >> 2);
       float x = (float)(int8_t)(wd >> (8 * (e & 3))) * A.row_scale[s * D + row] * sj;
-      for (int c = 0; c < r; ++c)
-        if (A.comp_idx[s * r + c] == row) x += A.comp_val[(s * r + c) * D + j];
+      if (DENSE) {
+        for (int c = 0; c < r; ++c) x = fmaf(A.comp_key[(s * r + c) * D + row], A.comp_val[(s * r + c) * D + j], x);
+      } else {
+        for (int c = 0; c < r; ++c)
+          if (A.comp_idx[s * r + c] == row) x += A.comp_val[(s * r + c) * D + j];
+      }
       A.S_out[(s * D + row) * D + j] = x;
     }
   }
@@ -1317,44 +1589,59 @@ hipError_t launch_dense_step(const DenseArgs &a, bool kda, bool bf16, hipStream_
 // Slabs of at most this many states take the two-wave decode kernel.
 constexpr int kSmallSlab = 4096;
 
+template <bool KDA, bool DENSE>
+void launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+  if (a.n <= kSmallSlab)
+    hipLaunchKernelGGL((decode_step2_kernel<KDA, DENSE>), dim3(a.n), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<KDA, DENSE>), dim3(a.n), dim3(64), 0, stream, a);
+}
+
+// Dense compensator tokens are on when the caller passes their keys.
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream) {
-  if (a.n <= kSmallSlab) {
-    if (kda)
-      hipLaunchKernelGGL(decode_step2_kernel<true>, dim3(a.n), dim3(128), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_step2_kernel<false>, dim3(a.n), dim3(128), 0, stream, a);
-  } else {
-    if (kda)
-      hipLaunchKernelGGL(decode_step_kernel<true>, dim3(a.n), dim3(64), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_step_kernel<false>, dim3(a.n), dim3(64), 0, stream, a);
-  }
+  const bool dense = a.comp_key != nullptr;
+  if (kda && dense) launch_decode_t<true, true>(a, stream);
+  else if (kda) launch_decode_t<true, false>(a, stream);
+  else if (dense) launch_decode_t<false, true>(a, stream);
+  else launch_decode_t<false, false>(a, stream);
+  return hipGetLastError();
+}
+
+template <bool FUSED>
+hipError_t launch_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  const bool dense = a.comp_key != nullptr;
+  if (kda && dense)
+    hipLaunchKernelGGL((close_kernel<true, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (kda)
+    hipLaunchKernelGGL((close_kernel<true, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (dense)
+    hipLaunchKernelGGL((close_kernel<false, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((close_kernel<false, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream) {
-  if (kda)
-    hipLaunchKernelGGL((close_kernel<true, false>), dim3(a.n), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((close_kernel<false, false>), dim3(a.n), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_close<false>(a, kda, stream);
 }
 
 hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream) {
-  if (kda)
-    hipLaunchKernelGGL((close_kernel<true, true>), dim3(a.n), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((close_kernel<false, true>), dim3(a.n), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_close<true>(a, kda, stream);
 }
 
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(quantize_kernel, dim3(a.n), dim3(256), 0, stream, a);
+  if (a.comp_key)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(dequant_kernel, dim3(a.n), dim3(256), 0, stream, a);
+  if (a.comp_key)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ def boundary_np(state, idx=None):
 def upload_boundary(state, b, idx=None):
     """Write boundary arrays (numpy, codes as row-major matrices) into the
     slab, optionally for states idx."""
-    state.load_boundary({k: np.ascontiguousarray(b[k]) for k in lq.LeapQuantState.BOUNDARY}, idx)
+    state.load_boundary({k: np.ascontiguousarray(b[k]) for k in state.boundary_keys}, idx)
 
 
 def tokens_np(tok, idx=None, t0=0, t1=None):

@@ -36,23 +36,24 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.leapquant_abi_version() == 2
+    assert lib.leapquant_abi_version() == L.ABI_VERSION == 3
     for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
                  L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
         assert lib.leapquant_status_string(code)
 
 
 def _params(**kw):
-    d = dict(n=4, dk=128, dv=128, p=16, r=4, gate=L.LQ_GATE_GDN, flags=0)
+    d = dict(n=4, dk=128, dv=128, p=16, r=4, gate=L.LQ_GATE_GDN, flags=0, comp_iters=0)
     d.update(kw)
-    return L.LqParams(d["n"], d["dk"], d["dv"], d["p"], d["r"], d["gate"], d["flags"])
+    return L.LqParams(d["n"], d["dk"], d["dv"], d["p"], d["r"], d["gate"], d["flags"], d["comp_iters"])
 
 
 def _state(**kw):
     n, p, r = 4, 16, 4
     base = FAKE
     sizes = dict(codes=n * 128 * 128, row_scale=n * 512, col_scale=n * 512, comp_idx=n * r * 4,
-                 comp_val=n * r * 512, buf_gate=n * p * 512, buf_k=n * p * 512, buf_u=n * p * 512)
+                 comp_val=n * r * 512, buf_gate=n * p * 512, buf_k=n * p * 512, buf_u=n * p * 512,
+                 comp_key=n * r * 512)
     addrs = {}
     for name, sz in sizes.items():
         addrs[name] = base
@@ -88,7 +89,8 @@ def _decode(lib, prm, st, t=0, **kw):
     (dict(dk=64), L.LQ_ERR_UNSUPPORTED), (dict(dv=256), L.LQ_ERR_UNSUPPORTED),
     (dict(n=0), L.LQ_ERR_SHAPE), (dict(p=0), L.LQ_ERR_SHAPE), (dict(p=65), L.LQ_ERR_SHAPE),
     (dict(r=-1), L.LQ_ERR_SHAPE), (dict(r=17), L.LQ_ERR_SHAPE), (dict(gate=2), L.LQ_ERR_SHAPE),
-    (dict(flags=4), L.LQ_ERR_SHAPE),
+    (dict(flags=8), L.LQ_ERR_SHAPE), (dict(comp_iters=-1), L.LQ_ERR_SHAPE),
+    (dict(comp_iters=9), L.LQ_ERR_SHAPE),
 ])
 def test_bad_params(lib, entry, kw, code):
     st, _ = _state()
@@ -202,3 +204,27 @@ def test_slot_entry_points_validation(lib):
     assert f(ctypes.byref(prm), ctypes.byref(st), None, None) == L.LQ_ERR_NULL
     assert f(ctypes.byref(prm), ctypes.byref(st), pos + 1, None) == L.LQ_ERR_ALIGN
     assert f(ctypes.byref(prm), ctypes.byref(st), st.codes + 128, None) == L.LQ_ERR_ALIAS
+
+
+def test_dense_compensator_validation(lib, entry):
+    """LQ_DENSE_COMP needs comp_key (16-byte aligned) when r > 0; without the
+    flag, or at r = 0, comp_key is not looked at."""
+    dense = _params(flags=L.LQ_DENSE_COMP, comp_iters=2)
+    st, _ = _state(comp_key=0)
+    assert _decode(lib, dense, st) == L.LQ_ERR_NULL
+    assert lib.leapquant_window_close(ctypes.byref(dense), ctypes.byref(st), 16, None) == L.LQ_ERR_NULL
+    assert lib.leapquant_quantize_state(ctypes.byref(dense), FAKE + (1 << 36), ctypes.byref(st), None) == L.LQ_ERR_NULL
+    assert lib.leapquant_dequantize_state(ctypes.byref(dense), ctypes.byref(st), FAKE + (1 << 36), None) == L.LQ_ERR_NULL
+    st, _ = _state()
+    st.comp_key = st.comp_key + 8
+    assert _decode(lib, dense, st) == L.LQ_ERR_ALIGN
+    # an output over the keys
+    st, _ = _state()
+    assert _decode(lib, dense, st, o=st.comp_key) == L.LQ_ERR_ALIAS
+    assert lib.leapquant_quantize_state(ctypes.byref(dense), st.comp_key, ctypes.byref(st), None) == L.LQ_ERR_ALIAS
+    assert lib.leapquant_dequantize_state(ctypes.byref(dense), ctypes.byref(st), st.comp_key, None) == L.LQ_ERR_ALIAS
+    # the same pointers are fine without the flag or at r = 0 (nothing is launched here:
+    # only argument errors are checked, so stop at the first call that would launch)
+    nokey, _ = _state(comp_key=0)
+    r0 = _params(flags=L.LQ_DENSE_COMP, r=0)
+    assert lib.leapquant_dequantize_state(ctypes.byref(r0), ctypes.byref(nokey), 0, None) == L.LQ_ERR_NULL

@@ -94,9 +94,9 @@ def test_dequantize_state():
 # ---------------------------------------------------------------------------
 # a1-a4: one decode step against synthetic buffered records
 # ---------------------------------------------------------------------------
-def _random_window_inputs(rng, n, p, nrec, gate, r):
+def _random_window_inputs(rng, n, p, nrec, gate, r, dense_iters=None):
     S = _states_with_outliers(rng, n)
-    b = O.quantize(S, r)
+    b = O.quantize(S, r) if dense_iters is None else O.quantize(S, r, O.DENSE_COMP, dense_iters)
     kda = gate == "kda"
     recs = []
     for _ in range(nrec):
@@ -166,20 +166,20 @@ def test_decode_step_entry(gate, p, t, r):
 # window positions and idle slots, on slabs tiled from m distinct states so
 # that the oracle computes m states and every slot is still compared.
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
-@pytest.mark.parametrize("n", [4096, 4097])
-def test_decode_step_slab_sizes(gate, n):
-    rng = np.random.default_rng(2000 + n + 7 * (gate == "kda"))
+@pytest.mark.parametrize("n,dense", [(4096, False), (4097, False), (4096, True), (4097, True)])
+def test_decode_step_slab_sizes(gate, n, dense):
+    rng = np.random.default_rng(2000 + n + 7 * (gate == "kda") + 3 * dense)
     m, p, r = 13, 16, 4
     base_t = rng.integers(0, p, m)
     base_t[0], base_t[1] = 0, p - 1
-    b, recs = _random_window_inputs(rng, m, p, p - 1, gate, r)
+    b, recs = _random_window_inputs(rng, m, p, p - 1, gate, r, 2 if dense else None)
     tok = _token(rng, m, gate)
     tile = np.arange(n) % m
     pos = base_t[tile].astype(np.int32)
     idle = np.zeros(n, bool)
     idle[[5, n // 2, n - 1]] = True
     pos[idle] = [-1, p, -1]
-    st = lq.LeapQuantState(n, p, r, gate, DEV)
+    st = lq.LeapQuantState(n, p, r, gate, DEV, flags=lq.LQ_DENSE_COMP if dense else 0, comp_iters=2)
     upload_boundary(st, {k: v[tile] for k, v in b.items()})
     _upload_records(st, [(a[tile], kt[tile], u[tile]) for a, kt, u in recs], gate)
     st.buf_u[:, p - 1] = float("nan")
