@@ -29,45 +29,58 @@ UNIT = "head-tokens/s"
 HBM_PEAK_GBS = 8000.0
 
 
-def step_bytes(t, dk, dv, r, kda):
+def _comp_read(dk, dv, r, dense):
+    """Compensator bytes a kernel reads per state: rows and indices, or
+    dense tokens (values and keys; the starting rows are not read)."""
+    return r * (4 * dv + 4 * dk) if dense else r * (4 * dv + 4)
+
+
+def _boundary_rw(dk, dv, r, dense):
+    """Boundary-state bytes a close reads and writes per state (dense
+    tokens: keys and values read; keys, values and starting rows written)."""
+    base = dk * dv + 4 * (dk + dv)
+    if dense:
+        return 2 * base + r * (4 * dv + 4 * dk) + r * (4 * dv + 4 * dk + 4)
+    return 2 * (base + r * (4 * dv + 4))
+
+
+def step_bytes(t, dk, dv, r, kda, dense=False):
     """Algorithmic HBM bytes of one decode step at window position t (t
     records already buffered) for one state: int8 codes, row and column
-    scales, compensator rows and indices, t buffered records, the token's
-    inputs, its output and the record it appends."""
+    scales, compensators, t buffered records, the token's inputs, its
+    output and the record it appends."""
     G = dk if kda else 1
     R = G + dk + dv
-    return (dk * dv + 4 * (dk + dv) + r * (4 * dv + 4) + 4 * t * R
+    return (dk * dv + 4 * (dk + dv) + _comp_read(dk, dv, r, dense) + 4 * t * R
             + 4 * (2 * dk + dv + 1 + G) + 4 * dv + 4 * R)
 
 
-def close_bytes(p, dk, dv, r, kda):
+def close_bytes(p, dk, dv, r, kda, dense=False):
     """Algorithmic HBM bytes of one window close for one state: read and
     write the boundary state, read the p buffered records."""
     G = dk if kda else 1
     R = G + dk + dv
-    boundary = dk * dv + 4 * (dk + dv) + r * (4 * dv + 4)
-    return 2 * boundary + 4 * p * R
+    return _boundary_rw(dk, dv, r, dense) + 4 * p * R
 
 
-def fused_bytes(t, dk, dv, r, kda):
+def fused_bytes(t, dk, dv, r, kda, dense=False):
     """Algorithmic HBM bytes of one fused last-token decode and window close
     for one state: read and write the boundary state, read the t buffered
     records and the token's inputs, write its output."""
     G = dk if kda else 1
     R = G + dk + dv
-    boundary = dk * dv + 4 * (dk + dv) + r * (4 * dv + 4)
-    return 2 * boundary + 4 * t * R + 4 * (2 * dk + dv + 1 + G) + 4 * dv
+    return _boundary_rw(dk, dv, r, dense) + 4 * t * R + 4 * (2 * dk + dv + 1 + G) + 4 * dv
 
 
-def bytes_per_head_token(p, dk, dv, r, kda, fused=False):
+def bytes_per_head_token(p, dk, dv, r, kda, fused=False, dense=False):
     """Algorithmic bytes per state and token, the window's work spread over
     its p tokens: p decode steps and a window close, or p - 1 decode steps
     and the fused last-token decode and close."""
     if fused:
-        dec = sum(step_bytes(t, dk, dv, r, kda) for t in range(p - 1))
-        return (dec + fused_bytes(p - 1, dk, dv, r, kda)) / p
-    dec = sum(step_bytes(t, dk, dv, r, kda) for t in range(p)) / p
-    return dec + close_bytes(p, dk, dv, r, kda) / p
+        dec = sum(step_bytes(t, dk, dv, r, kda, dense) for t in range(p - 1))
+        return (dec + fused_bytes(p - 1, dk, dv, r, kda, dense)) / p
+    dec = sum(step_bytes(t, dk, dv, r, kda, dense) for t in range(p)) / p
+    return dec + close_bytes(p, dk, dv, r, kda, dense) / p
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gdn_b256_4layers.txt")
@@ -102,6 +115,10 @@ def parse():
     ap.add_argument("--close", choices=("fused", "separate"), default="fused",
                     help="fused: last token decoded and window closed per layer in one launch; "
                          "separate: p decode steps, then one window close over all layers")
+    ap.add_argument("--comp", choices=("rows", "dense"), default="rows",
+                    help="compensator form: rows of largest norm (default) or dense tokens "
+                         "(LQ_DENSE_COMP, keys by subspace iteration)")
+    ap.add_argument("--comp-iters", type=int, default=2, help="subspace iterations with --comp dense")
     ap.add_argument("--ablations", action="store_true",
                     help="instead of the headline line, print one line with the kernel-throughput "
                          "analogues of the pages' Table 2 (per-step fp32 / bf16 / int8 baselines, "
@@ -150,7 +167,9 @@ def main():
 
     # the layers' states live in one slab: decoded layer by layer through
     # views, quantized and window-closed together in one launch each
-    slab = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, dev)
+    dense = args.comp == "dense" and cfg.r > 0
+    comp_flags = lq.LQ_DENSE_COMP if dense else 0
+    slab = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, dev, comp_flags, comp_iters=args.comp_iters)
     slabs = [slab.view(l * nl, nl) for l in range(L)]
     outs = [torch.empty((nl, cfg.dv), device=dev) for _ in range(L)]
 
@@ -240,20 +259,20 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     head_tokens = n * T
     value = head_tokens / (wall / args.steps)
-    bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, fused)
-    bpht_unfused = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda)
+    bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, fused, dense)
+    bpht_unfused = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, dense=dense)
     n_dec = args.steps * windows * n_steps * L
     dec_avg_ms = dec_ms / n_dec
-    dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(n_steps)) / n_steps
+    dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda, dense) for t in range(n_steps)) / n_steps
     dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     close_launches = L if fused else 1          # per window
     close_states = nl if fused else n           # per launch
-    close_state_bytes = (fused_bytes(cfg.p - 1, cfg.dk, cfg.dv, cfg.r, kda) if fused
-                         else close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda))
+    close_state_bytes = (fused_bytes(cfg.p - 1, cfg.dk, cfg.dv, cfg.r, kda, dense) if fused
+                         else close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, dense))
     close_avg_ms = close_ms / (args.steps * windows * close_launches)
     close_gbs = close_states * close_state_bytes / (close_avg_ms * 1e-3) / 1e9
     whole_gbs = value * bpht / 1e9
-    traffic = measured_traffic(cfg)
+    traffic = {} if dense else measured_traffic(cfg)
     dkey = "decode_fused" if fused else "decode_separate"
     dec_traffic = round(traffic[dkey] * nl) if dkey in traffic else None
     ckey = "fused" if fused else "close"
@@ -284,8 +303,10 @@ def main():
         "hbm_copy_GBs": round(copy_gbs, 1),
     }
 
+    if dense:
+        result["config"]["compensators"] = f"dense tokens, {args.comp_iters} subspace iterations"
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args, cfg, S_init, tok)
+        result["cpu_baseline"] = cpu_baseline(args, cfg, S_init, tok, comp_flags, args.comp_iters)
     print(json.dumps(result), flush=True)
 
 
@@ -346,8 +367,8 @@ def ablations(args, cfg, dev, reps=3):
         del S, views
         return value, dense_bytes(cfg.dk, cfg.dv, kda, 4 if dtype == torch.float32 else 2)
 
-    def windowed(p, r, flags):
-        slab = lq.LeapQuantState(n, p, r, cfg.gate, dev, flags)
+    def windowed(p, r, flags, iters=0):
+        slab = lq.LeapQuantState(n, p, r, cfg.gate, dev, flags, comp_iters=iters)
         lq.leapquant_quantize_state(slab, S_init)
         views = [slab.view(l * nl, nl) for l in range(L)]
 
@@ -361,7 +382,8 @@ def ablations(args, cfg, dev, reps=3):
                         lq.leapquant_decode_step(views[l], j, *targs(t, l))
         value = timed(run)
         del slab, views
-        return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
+        return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True,
+                                           dense=bool(flags & lq.LQ_DENSE_COMP) and r > 0)
 
     def slots(p, r):
         # continuous batching: every slot has its own window phase (seeded,
@@ -408,14 +430,20 @@ def ablations(args, cfg, dev, reps=3):
 
     rows_cb = [("lockstep windows (all slots at the same position)", lambda: windowed(cfg.p, cfg.r, 0)),
                ("continuous batching (slot phases spread over the window)", lambda: slots(cfg.p, cfg.r))]
+    DC = lq.LQ_DENSE_COMP
+    rows_dc = [("row compensators", lambda: windowed(cfg.p, cfg.r, 0))] + \
+        [(f"dense tokens, {i} subspace iteration{'s' if i != 1 else ''}", (lambda i=i: windowed(cfg.p, cfg.r, DC, i)))
+         for i in (0, 1, 2)]
     t2, ref = table(rows2, None)
     t3, _ = table(rows3, ref)
     tcb, _ = table(rows_cb, ref)
+    tdc, _ = table(rows_dc, ref)
     lat = latency(dev)
     return {"metric": "kernel throughput ablations (head-tokens/s; speedup over fp32 per-step)",
             "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph",
             "schedule": "one launch per layer and token; last token of each window fused with its close",
             "table2": t2, "table3_r": cfg.r, "table3": t3, "continuous_batching": tcb,
+            "compensator_forms": tdc,
             "latency_single_state": lat}
 
 
@@ -484,7 +512,7 @@ def copy_calibration(dev, nbytes=1 << 31, reps=5):
     return gbs
 
 
-def cpu_baseline(args, cfg, S_init, tok):
+def cpu_baseline(args, cfg, S_init, tok, comp_flags=0, iters=0):
     """The CPU oracle, free-running on a bounded sample of the same inputs:
     groups of `cpu_sample_states` states of layer 0, each decoded over all
     tokens, until about `cpu_seconds` of wall time have been spent."""
@@ -503,9 +531,10 @@ def cpu_baseline(args, cfg, S_init, tok):
         idx = torch.arange(groups * ns, (groups + 1) * ns, device=S_init.device)
         S0 = S_init.index_select(0, idx).cpu().numpy()
         tk = {k: v.index_select(1, idx).cpu().numpy().astype(np.float64) for k, v in tok.items()}
-        b = O.quantize(S0, cfg.r)
+        flags = O.DENSE_COMP if comp_flags else 0
+        b = O.quantize(S0, cfg.r, flags, iters)
         for t0_ in range(0, T, cfg.p):
-            _, _, _, b = O.window(b, tk, t0_, cfg.p, gate, cfg.r)
+            _, _, _, b = O.window(b, tk, t0_, cfg.p, gate, cfg.r, flags, iters=iters)
         head_tokens += ns * T
         groups += 1
     wall = time.perf_counter() - t0

@@ -106,9 +106,9 @@ enum {
  * (k_c, w_c) with dense fp32 keys k_c (comp_key) and values w_c (comp_val):
  * the boundary state is B = deQ + sum_c k_c w_c^T, and a compensator enters
  * the window like a buffered record written before the window's first token
- * (decay Gamma, weight k_c . (Gamma * y), update w_c), so it shares the
- * update path of real tokens ([EL] Abstract; Figure 4, where compensators
- * capture the state's dominant large-magnitude structure).  The window
+ * (decay Gamma, weight k_c . (Gamma * y), update w_c): it is updated
+ * exactly like a real token ([EL] Abstract; in Figure 4 the compensators
+ * hold the state's largest components).  The window
  * close joins them to the fp32 rebuild as r more records of the same MFMA
  * contraction (K = len + r).  The split finds the keys by comp_iters rounds
  * of subspace iteration on S S^T started from the one-hot keys of the r
@@ -158,7 +158,7 @@ int leapquant_quantize_state(const lq_params *prm, const float *S,
 
 /* Decode token t (0-based position inside the current window, 0 <= t < p)
  * for all n states ([EL] Figure 2, per-window quantization; [EL] Abstract,
- * compensators share the update path of real tokens).  Reads the boundary
+ * compensators are updated like real tokens).  Reads the boundary
  * state and the records 0..t-1 of the buffer, writes
  *   o[n][dv] = S_t^T q_t, with S_t the exact recurrence from the boundary
  *              state through the buffered records and this token,

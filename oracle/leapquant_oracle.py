@@ -39,10 +39,10 @@ What is computed (all floating point in fp64 unless a step says fp32):
 
 * Dense Compensator Tokens (flag DENSE_COMP; a second reading of the same
   passages): a compensator is a token (k_c, w_c) with a dense unit key k_c,
-  entering the state as k_c w_c^T and following the update path of the
-  window's real tokens.  The keys span an approximation of the state's
-  dominant left singular subspace (the "dominant large-magnitude structure"
-  of [EL] Figure 4): subspace iteration started from the one-hot keys of the
+  entering the state as k_c w_c^T and updated exactly like the window's own
+  tokens.  The keys approximate the span of the state's leading left
+  singular vectors (the largest components, which [EL] Figure 4 assigns to
+  the compensators): subspace iteration started from the one-hot keys of the
   r largest-norm rows, `iters` rounds of Y = S S^T K, K = MGS(Y) (modified
   Gram-Schmidt in compensator order; a column whose projected norm is at
   most 1e-3 of its norm before projection, or zero, becomes the zero key).

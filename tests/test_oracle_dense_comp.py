@@ -1,8 +1,8 @@
 """Pins of the oracle's dense Compensator Tokens (flag DENSE_COMP).
 
-The pages describe compensators as a few high-precision tokens that capture
-the state's dominant large-magnitude structure and share the update path of
-real tokens ([EL] Abstract, Figure 4).  The dense reading keeps r tokens
+In the pages, compensators are a few high-precision tokens that hold the
+state's largest components and are updated like real tokens ([EL] Abstract,
+Figure 4).  The dense reading keeps r tokens
 (k_c, w_c) with unit keys from subspace iteration on S S^T started at the
 one-hot keys of the largest-norm rows.  What mathematics fixes, and what is
 checked here without a GPU:
