@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "decode head-tokens/s (dk=dv=128, int8 state, p=16) + % of HBM BW roofline"
 UNIT = "head-tokens/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 
 
 def _comp_read(dk, dv, r, dense):
@@ -271,6 +272,11 @@ def main():
                          else close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, dense))
     close_avg_ms = close_ms / (args.steps * windows * close_launches)
     close_gbs = close_states * close_state_bytes / (close_avg_ms * 1e-3) / 1e9
+    # issued MFMA flops of the rebuild: 2 dk dv per record slot, the records
+    # (plus dense tokens) padded to a multiple of 4
+    slots = (cfg.p - 1 if fused else cfg.p) + (cfg.r if dense else 0)
+    close_flops = close_states * 2 * cfg.dk * cfg.dv * ((slots + 3) // 4 * 4)
+    close_mfma_util = close_flops / (close_avg_ms * 1e-3) / (MFMA_FP32_PEAK_TFLOPS * 1e12)
     whole_gbs = value * bpht / 1e9
     traffic = {} if dense else measured_traffic(cfg)
     dkey = "decode_fused" if fused else "decode_separate"
@@ -295,7 +301,8 @@ def main():
                          "avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
                          "bytes_per_launch": close_states * close_state_bytes,
                          "states_per_launch": close_states, "launches_per_window": close_launches,
-                         "traffic": close_traffic},
+                         "traffic": close_traffic, "mfma_flops_per_launch": close_flops,
+                         "mfma_util": round(close_mfma_util, 4)},
         "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
                        "bytes_per_head_token": round(bpht, 1),
                        "unfused_bytes_per_head_token": round(bpht_unfused, 1),

@@ -573,3 +573,48 @@ def test_deltaproduct_substeps(fused):
         _, _, S_end, _ = O.window(bounds[w], tokn, w * p, p, O.GATE_GDN, r)
         P.compare_boundary(boundary_np(st), bounds[w + 1], S_end.astype(np.float32), r,
                            f"DeltaProduct boundary {w + 1}")
+
+
+# ---------------------------------------------------------------------------
+# Graph replay (the benchmark's launch mode): a captured window replays to
+# the eager result, bit for bit, on every replay
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dense", [False, True])
+def test_graph_replay_matches_eager(dense):
+    cfg, S0, tok = _workload(1, 64, 16)
+    flags = lq.LQ_DENSE_COMP if dense else 0
+    st = lq.LeapQuantState(64, cfg.p, cfg.r, cfg.gate, DEV, flags=flags, comp_iters=2)
+    tokd = {k: v.to(DEV) for k, v in tok.items()}
+    out = torch.zeros((16, 64, 128), device=DEV)
+    lq.leapquant_quantize_state(st, S0.to(DEV))
+    torch.cuda.synchronize()
+    start = {k: getattr(st, k).clone() for k in st.boundary_keys + ("buf_gate", "buf_k", "buf_u")}
+
+    def restore():
+        for k, v in start.items():
+            getattr(st, k).copy_(v)
+        out.zero_()
+
+    def window():
+        run_window(st, tokd, 0, cfg.p, out, fused=True)
+
+    window()
+    torch.cuda.synchronize()
+    ref = {k: to_np(getattr(st, k)) for k in st.boundary_keys}
+    ref_o = to_np(out)
+    stream = torch.cuda.Stream(device=DEV)
+    restore()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        window()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(out), ref_o, err_msg=f"replay {rep}: outputs")
+        for k in st.boundary_keys:
+            np.testing.assert_array_equal(to_np(getattr(st, k)), ref[k], err_msg=f"replay {rep}: {k}")
+        torch.zeros(1 << 20, device=DEV).sum()   # eager work between replays
