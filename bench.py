@@ -93,7 +93,8 @@ def measured_traffic(cfg):
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary; empty when the counters were
     taken on another workload or on kernel source that has changed since."""
     import hashlib
-    if cfg.cid != 2 or not os.path.exists(TRAFFIC_FILE):
+    from workloads.configs import HEADLINE
+    if cfg.name != HEADLINE or not os.path.exists(TRAFFIC_FILE):
         return {}
     doc = json.load(open(TRAFFIC_FILE))
     if doc.get("source_sha256") != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
@@ -110,7 +111,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=2, help="workload id (default: the batch-256 4-layer workload)")
+    ap.add_argument("--workload", default="gdn_b256_h32_4layers",
+                    choices=("gdn_single_head_b1", "gdn_layer_h32_b64", "gdn_b256_h32_4layers",
+                             "kda_h32_b128", "gdn_long64k_h16_b8"),
+                    help="workload (default: the batch-256 x 32-head x 4-layer GDN decode)")
     ap.add_argument("--tokens", type=int, default=0, help="tokens per step (default: the workload's)")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--close", choices=("fused", "separate"), default="fused",
@@ -135,7 +139,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(states shard with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the states shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -143,9 +147,9 @@ def main():
 
     import recurrent_state_quant_amd as lq
     from workloads import generators as G
-    from workloads.configs import CONFIGS
+    from workloads.configs import WORKLOADS
 
-    cfg = CONFIGS[args.config]
+    cfg = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.ablations:
@@ -461,8 +465,8 @@ def latency(dev, windows=8, reps=20):
     import torch
     import recurrent_state_quant_amd as lq
     from workloads import generators as G
-    from workloads.configs import CONFIGS
-    cfg = CONFIGS[0]
+    from workloads.configs import WORKLOADS
+    cfg = WORKLOADS["gdn_single_head_b1"]
     T = windows * cfg.p
     g = G.make_generator(cfg.seed, dev)
     S_init = G.initial_state(cfg, 1, g, dev)

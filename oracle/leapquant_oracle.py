@@ -34,7 +34,7 @@ What is computed (all floating point in fp64 unless a step says fp32):
 * Compensator Tokens ([EL] Abstract, Figure 4; [NL] Key points): r rows of the
   state kept in fp32; they are part of the boundary state, so they follow the
   same recurrence as everything else.  Extraction rule (not given by the
-  pages; this build's reading): the r rows of largest L2 norm, ties to the
+  pages; the reading taken here): the r rows of largest L2 norm, ties to the
   lower row index, stored in descending-norm order.
 
 * Dense Compensator Tokens (flag DENSE_COMP; a second reading of the same

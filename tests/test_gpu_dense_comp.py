@@ -138,12 +138,12 @@ def test_window_close_entry(gate, fused, p, length, r, iters):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("cid,n,steps", [(1, 16, 96), (3, 16, 96)])
-def test_oracle_forced_windows(cid, n, steps, fused):
+@pytest.mark.parametrize("name,n,steps", [("gdn_layer_h32_b64", 16, 96), ("kda_h32_b128", 16, 96)])
+def test_oracle_forced_windows(name, n, steps, fused):
     """Whole windows of the synthetic workloads with dense tokens (2
     iterations); every GPU window starts from the oracle's boundary."""
     iters = 2
-    cfg, S0, tok = _workload(cid, n, steps)
+    cfg, S0, tok = _workload(name, n, steps)
     S0n = S0.numpy()
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
     o_ref, bounds = O.run_windowed(S0n, tokn, cfg.p, cfg.r, _gate(cfg.gate), O.DENSE_COMP, iters=iters)
@@ -156,13 +156,13 @@ def test_oracle_forced_windows(cid, n, steps, fused):
         run_window(st, tokd, w * cfg.p, cfg.p, out, fused=fused)
         torch.cuda.synchronize()
         sl = slice(w * cfg.p, (w + 1) * cfg.p)
-        P.assert_close(to_np(out[sl]), o_ref[sl], f"cfg{cid} window {w} outputs")
+        P.assert_close(to_np(out[sl]), o_ref[sl], f"{name} window {w} outputs")
         _, _, S_end, _ = O.window(bounds[w], tokn, w * cfg.p, cfg.p, _gate(cfg.gate), cfg.r, O.DENSE_COMP,
                                   iters=iters)
         s = P.compare_dense_boundary(boundary_np(st), S_end.astype(np.float32), cfg.r, iters, 0,
-                                     f"cfg{cid} boundary {w + 1}")
+                                     f"{name} boundary {w + 1}")
         flips += s["flips"]
-    print(f"cfg{cid} dense: {flips} flipped codes")
+    print(f"{name} dense: {flips} flipped codes")
 
 
 def test_zero_iterations_decode_matches_row_extraction():

@@ -15,7 +15,7 @@ from oracle import leapquant_oracle as O
 from tests import parity as P
 from tests.gpu_run import boundary_np, run_window, to_np, tokens_np, upload_boundary
 from workloads import generators as G
-from workloads.configs import CONFIGS
+from workloads.configs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -69,14 +69,14 @@ def test_quantize_state_bitexact(r, flags):
 
 
 def test_quantize_state_workload_initial_states():
-    for cid in (0, 1, 3):
-        cfg = CONFIGS[cid]
-        n = 1 if cid == 0 else 64
+    for name in ("gdn_single_head_b1", "gdn_layer_h32_b64", "kda_h32_b128"):
+        cfg = WORKLOADS[name]
+        n = 1 if cfg.n_states == 1 else 64
         S = G.initial_state(cfg, n, G.make_generator(cfg.seed, "cpu"), "cpu").numpy()
         st = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, DEV)
         lq.leapquant_quantize_state(st, _dev(S))
         torch.cuda.synchronize()
-        P.compare_boundary(boundary_np(st), O.quantize(S, cfg.r), S, cfg.r, f"cfg{cid} init", exact=True)
+        P.compare_boundary(boundary_np(st), O.quantize(S, cfg.r), S, cfg.r, f"{name} init", exact=True)
 
 
 def test_dequantize_state():
@@ -258,8 +258,8 @@ def test_decode_close_entry(gate, p, t, r, flags):
 # ---------------------------------------------------------------------------
 # Whole windows: the GPU starts each window from the oracle's boundary
 # ---------------------------------------------------------------------------
-def _workload(cid, n, steps, device="cpu", seed=None):
-    cfg = CONFIGS[cid]
+def _workload(name, n, steps, device="cpu", seed=None):
+    cfg = WORKLOADS[name]
     g = G.make_generator(cfg.seed if seed is None else seed, device)
     S0 = G.initial_state(cfg, n, g, device)
     tok = G.token_inputs(cfg, n, steps, g, device)
@@ -267,9 +267,10 @@ def _workload(cid, n, steps, device="cpu", seed=None):
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 24, 128), (3, 24, 128)])
-def test_oracle_forced_windows(cid, n, steps, fused):
-    cfg, S0, tok = _workload(cid, n, steps)
+@pytest.mark.parametrize("name,n,steps", [("gdn_single_head_b1", 1, 256), ("gdn_layer_h32_b64", 24, 128),
+                                          ("kda_h32_b128", 24, 128)])
+def test_oracle_forced_windows(name, n, steps, fused):
+    cfg, S0, tok = _workload(name, n, steps)
     S0n = S0.numpy()
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
     o_ref, bounds = O.run_windowed(S0n, tokn, cfg.p, cfg.r, _gate(cfg.gate))
@@ -282,22 +283,23 @@ def test_oracle_forced_windows(cid, n, steps, fused):
         run_window(st, tokd, w * cfg.p, cfg.p, out, fused=fused)
         torch.cuda.synchronize()
         sl = slice(w * cfg.p, (w + 1) * cfg.p)
-        P.assert_close(to_np(out[sl]), o_ref[sl], f"cfg{cid} window {w} outputs")
+        P.assert_close(to_np(out[sl]), o_ref[sl], f"{name} window {w} outputs")
         _, _, S_end, _ = O.window(bounds[w], tokn, w * cfg.p, cfg.p, _gate(cfg.gate), cfg.r)
         s = P.compare_boundary(boundary_np(st), bounds[w + 1], S_end.astype(np.float32), cfg.r,
-                               f"cfg{cid} boundary {w + 1}")
+                               f"{name} boundary {w + 1}")
         for k in total:
             total[k] += s[k]
-    print(f"cfg{cid}: {total}")
+    print(f"{name}: {total}")
 
 
 # ---------------------------------------------------------------------------
 # Free-running: strict until the first legitimate rounding-boundary flip
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("cid,n,steps", [(0, 1, 256), (1, 16, 256), (3, 16, 256)])
-def test_free_running(cid, n, steps, fused):
-    cfg, S0, tok = _workload(cid, n, steps)
+@pytest.mark.parametrize("name,n,steps", [("gdn_single_head_b1", 1, 256), ("gdn_layer_h32_b64", 16, 256),
+                                          ("kda_h32_b128", 16, 256)])
+def test_free_running(name, n, steps, fused):
+    cfg, S0, tok = _workload(name, n, steps)
     S0n = S0.numpy()
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
     o_ref, bounds = O.run_windowed(S0n, tokn, cfg.p, cfg.r, _gate(cfg.gate))
@@ -314,17 +316,17 @@ def test_free_running(cid, n, steps, fused):
         og, orf = to_np(out[sl]), o_ref[sl]
         strict = ~diverged
         if strict.any():
-            P.assert_close(og[:, strict], orf[:, strict], f"cfg{cid} window {w} outputs")
+            P.assert_close(og[:, strict], orf[:, strict], f"{name} window {w} outputs")
         if diverged.any():
             rel = np.linalg.norm(og[:, diverged] - orf[:, diverged]) / np.linalg.norm(orf[:, diverged])
             worst_rel = max(worst_rel, rel)
-            assert rel < 2e-2, f"cfg{cid} window {w}: diverged trajectories differ by {rel}"
+            assert rel < 2e-2, f"{name} window {w}: diverged trajectories differ by {rel}"
         gb = boundary_np(st)
         same = np.all(gb["codes"] == bounds[w + 1]["codes"], axis=(1, 2))
         if cfg.r:
             same &= np.all(gb["comp_idx"] == bounds[w + 1]["comp_idx"], axis=1)
         diverged |= ~same
-    print(f"cfg{cid}: diverged states {diverged.sum()}/{n}, worst diverged rel err {worst_rel:.2e}")
+    print(f"{name}: diverged states {diverged.sum()}/{n}, worst diverged rel err {worst_rel:.2e}")
 
 
 # ---------------------------------------------------------------------------
@@ -345,7 +347,7 @@ def _run_free(cfg, n, steps, S0d, tokd, snapshot_at=None, start=0, st=None):
 
 
 def test_determinism_and_resume():
-    cfg, S0, tok = _workload(1, 96, 96, device=DEV)
+    cfg, S0, tok = _workload("gdn_layer_h32_b64", 96, 96, device=DEV)
     out1, st1, snap = _run_free(cfg, 96, 96, S0, tok, snapshot_at=48)
     out2, st2, _ = _run_free(cfg, 96, 96, S0, tok)
     assert torch.equal(out1, out2)
@@ -420,15 +422,15 @@ def test_dense_bf16_step(gate):
 # Continuous batching: slots join and finish at different steps, each with
 # its own window phase; partial windows are closed at sequence end
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("cid", [1, 3])
-def test_continuous_batching_slots(cid):
-    cfg = CONFIGS[cid]
+@pytest.mark.parametrize("name", ["gdn_layer_h32_b64", "kda_h32_b128"])
+def test_continuous_batching_slots(name):
+    cfg = WORKLOADS[name]
     n, T, p = 12, 64, cfg.p
-    rng = np.random.default_rng(70 + cid)
+    rng = np.random.default_rng(73 if cfg.gate == "kda" else 71)
     join = rng.integers(0, 24, n)
     end = np.minimum(T, join + rng.integers(8, 60, n))
     end[0], join[0] = T, 0                          # one slot runs the whole time
-    cfgw, S0, tok = _workload(cid, n, T)
+    cfgw, S0, tok = _workload(name, n, T)
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
     tokd = {k: v.to(DEV) for k, v in tok.items()}
     gate = _gate(cfg.gate)
@@ -473,7 +475,7 @@ def test_continuous_batching_slots(cid):
             flips += stats["flips"]
             upload_boundary(st, ref_b[s][window[s]], [s])   # next window starts from the oracle's state
     assert window.sum() == sum(int(np.ceil((end[s] - join[s]) / p)) for s in range(n))
-    print(f"cfg{cid}: {window.sum()} slot windows, {flips} flipped codes")
+    print(f"{name}: {window.sum()} slot windows, {flips} flipped codes")
 
 
 # ---------------------------------------------------------------------------
@@ -490,7 +492,7 @@ _TABLE4 = {  # row: (gate, alpha rule, beta = 1?, no delta?)
 
 def _table4_tokens(row, n, T, seed):
     gate, arule, beta1, _ = _TABLE4[row]
-    cfg = CONFIGS[3 if gate == "kda" else 1]
+    cfg = WORKLOADS["kda_h32_b128" if gate == "kda" else "gdn_layer_h32_b64"]
     g = G.make_generator(seed, "cpu")
     S0 = G.initial_state(cfg, n, g, "cpu")
     tok = G.token_inputs(cfg, n, T, g, "cpu")
@@ -557,7 +559,7 @@ def test_table4_rows_dense_baseline(row):
 def test_deltaproduct_substeps(fused):
     nh, tokens_, n, p, r = 2, 24, 10, 16, 4
     steps = nh * tokens_
-    cfg, S0, tok = _workload(1, n, steps, seed=33)          # sub-step inputs, [steps, n, ...]
+    cfg, S0, tok = _workload("gdn_layer_h32_b64", n, steps, seed=33)        # sub-step inputs, [steps, n, ...]
     tokn = {k: v.numpy().astype(np.float64) for k, v in tok.items()}
     o_ref, bounds = O.run_windowed(S0.numpy(), tokn, p, r, O.GATE_GDN)
     tokd = {k: v.to(DEV) for k, v in tok.items()}
@@ -581,7 +583,7 @@ def test_deltaproduct_substeps(fused):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dense", [False, True])
 def test_graph_replay_matches_eager(dense):
-    cfg, S0, tok = _workload(1, 64, 16)
+    cfg, S0, tok = _workload("gdn_layer_h32_b64", 64, 16)
     flags = lq.LQ_DENSE_COMP if dense else 0
     st = lq.LeapQuantState(64, cfg.p, cfg.r, cfg.gate, DEV, flags=flags, comp_iters=2)
     tokd = {k: v.to(DEV) for k, v in tok.items()}

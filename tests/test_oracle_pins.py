@@ -17,7 +17,7 @@ import torch
 from oracle import leapquant_oracle as O
 from tests import brute
 from workloads import generators as G
-from workloads.configs import CONFIGS, WorkloadConfig
+from workloads.configs import WORKLOADS, WorkloadConfig
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -197,7 +197,7 @@ def test_config0_planted_rows_are_extracted():
     """The four x20 rows planted in the single-head workload are exactly the
     compensator rows of the first boundary state ([EL] Abstract: compensators
     keep the largest outliers)."""
-    cfg = CONFIGS[0]
+    cfg = WORKLOADS["gdn_single_head_b1"]
     g = G.make_generator(cfg.seed, "cpu")
     S = G.initial_state(cfg, 1, g, "cpu").numpy()
     norms = np.linalg.norm(S[0].astype(np.float64), axis=1)
@@ -287,7 +287,7 @@ def test_per_window_beats_per_token_state_error():
     """Qualitative claim of [EL] Figure 3: quantizing once per window keeps the
     state closer to the exact recurrence than quantizing every token.  The
     pages print no values, so only the ordering is checked."""
-    cfg = WorkloadConfig(99, "mse", "gdn", 1, 4, 1, 256, 16, 4, "pct1")
+    cfg = WorkloadConfig("mse_gdn_h4_b1", "gdn", 1, 4, 1, 256, 16, 4, "pct1")
     g = G.make_generator(7, "cpu")
     S0 = G.initial_state(cfg, 4, g, "cpu").numpy()
     tok = {k: v.numpy().astype(np.float64) for k, v in G.token_inputs(cfg, 4, 256, g, "cpu").items()}
@@ -301,7 +301,7 @@ def test_per_window_beats_per_token_state_error():
 
 def test_generators_match_recipe():
     """Input recipe: unit-norm q and k, beta in (0,1), alpha in (0,1)."""
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS["kda_h32_b128"]
     g = G.make_generator(0, "cpu")
     tok = G.token_inputs(cfg, 5, 4, g, "cpu")
     assert tok["alpha"].shape == (4, 5, 128)

@@ -26,7 +26,6 @@ from dataclasses import dataclass
 
 @dataclass(frozen=True)
 class WorkloadConfig:
-    cid: int
     name: str
     gate: str
     batch: int
@@ -54,15 +53,16 @@ class WorkloadConfig:
         return self.steps // self.p
 
 
-CONFIGS = {
-    0: WorkloadConfig(0, "gdn_single_head_b1", "gdn", 1, 1, 1, 256, 16, 4, "rows4x20"),
-    1: WorkloadConfig(1, "gdn_layer_h32_b64", "gdn", 64, 32, 1, 4096, 16, 4, "pct1"),
-    2: WorkloadConfig(2, "gdn_b256_h32_4layers", "gdn", 256, 32, 4, 1024, 16, 4, "pct1"),
-    3: WorkloadConfig(3, "kda_h32_b128", "kda", 128, 32, 1, 2048, 16, 8, "pct1"),
-    4: WorkloadConfig(4, "gdn_long64k_h16_b8", "gdn", 8, 16, 1, 65536, 16, 4, "pct1",
-                      snapshot_every=1024),
-}
+_ALL = (
+    WorkloadConfig("gdn_single_head_b1", "gdn", 1, 1, 1, 256, 16, 4, "rows4x20"),
+    WorkloadConfig("gdn_layer_h32_b64", "gdn", 64, 32, 1, 4096, 16, 4, "pct1"),
+    WorkloadConfig("gdn_b256_h32_4layers", "gdn", 256, 32, 4, 1024, 16, 4, "pct1"),
+    WorkloadConfig("kda_h32_b128", "kda", 128, 32, 1, 2048, 16, 8, "pct1"),
+    WorkloadConfig("gdn_long64k_h16_b8", "gdn", 8, 16, 1, 65536, 16, 4, "pct1", snapshot_every=1024),
+)
+WORKLOADS = {w.name: w for w in _ALL}
+HEADLINE = "gdn_b256_h32_4layers"  # the throughput workload: batch 256 x 32 heads x 4 layers
 
 
-def get_config(cid: int) -> WorkloadConfig:
-    return CONFIGS[int(cid)]
+def get_workload(name: str) -> WorkloadConfig:
+    return WORKLOADS[name]
