@@ -422,9 +422,11 @@ def test_dense_bf16_step(gate):
 # Continuous batching: slots join and finish at different steps, each with
 # its own window phase; partial windows are closed at sequence end
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["gdn_layer_h32_b64", "kda_h32_b128"])
-def test_continuous_batching_slots(name):
+@pytest.mark.parametrize("name,dense", [("gdn_layer_h32_b64", False), ("kda_h32_b128", False),
+                                        ("gdn_layer_h32_b64", True)])
+def test_continuous_batching_slots(name, dense):
     cfg = WORKLOADS[name]
+    flags, iters = (O.DENSE_COMP, 2) if dense else (0, 0)
     n, T, p = 12, 64, cfg.p
     rng = np.random.default_rng(73 if cfg.gate == "kda" else 71)
     join = rng.integers(0, 24, n)
@@ -437,11 +439,12 @@ def test_continuous_batching_slots(name):
     ref_o, ref_b, ref_tok = [], [], []
     for s in range(n):
         ts = {k: v[join[s]:end[s], s:s + 1] for k, v in tokn.items()}
-        o_s, b_s = O.run_windowed(S0.numpy()[s:s + 1], ts, p, cfg.r, gate)
+        o_s, b_s = O.run_windowed(S0.numpy()[s:s + 1], ts, p, cfg.r, gate, flags, iters=iters)
         ref_o.append(o_s[:, 0])
         ref_b.append(b_s)
         ref_tok.append(ts)
-    st = lq.LeapQuantState(n, p, cfg.r, cfg.gate, DEV)
+    st = lq.LeapQuantState(n, p, cfg.r, cfg.gate, DEV, flags=lq.LQ_DENSE_COMP if dense else 0,
+                           comp_iters=iters)
     for s in range(n):
         upload_boundary(st, ref_b[s][0], [s])
     window = np.zeros(n, int)
@@ -469,13 +472,16 @@ def test_continuous_batching_slots(name):
             gb = boundary_np(st, [s])
             w0 = (window[s] - 1) * p          # the window's first token, in slot s's own count
             _, _, S_end, _ = O.window(ref_b[s][window[s] - 1], ref_tok[s], w0, t - join[s] + 1 - w0,
-                                      gate, cfg.r)
-            stats = P.compare_boundary(gb, ref_b[s][window[s]], S_end.astype(np.float32), cfg.r,
-                                       f"slot {s} boundary {window[s]}")
+                                      gate, cfg.r, flags, iters=iters)
+            what = f"slot {s} boundary {window[s]}"
+            if dense:
+                stats = P.compare_dense_boundary(gb, S_end.astype(np.float32), cfg.r, iters, 0, what)
+            else:
+                stats = P.compare_boundary(gb, ref_b[s][window[s]], S_end.astype(np.float32), cfg.r, what)
             flips += stats["flips"]
             upload_boundary(st, ref_b[s][window[s]], [s])   # next window starts from the oracle's state
     assert window.sum() == sum(int(np.ceil((end[s] - join[s]) / p)) for s in range(n))
-    print(f"{name}: {window.sum()} slot windows, {flips} flipped codes")
+    print(f"{name}{' dense' if dense else ''}: {window.sum()} slot windows, {flips} flipped codes")
 
 
 # ---------------------------------------------------------------------------
