@@ -395,6 +395,36 @@ def step_dense_bf16(S, q, k, v, beta, alpha, gate, flags=0):
     return o, round_bf16(S_new)
 
 
+def window_bf16(B, tokens, t0, length, gate, flags=0):
+    """One window of the "BF16 + per-window" row of [EL] Table 2: the
+    boundary state B (fp64 array of bf16 values) stays fixed, the window's
+    tokens are the exact recurrence from it (what the fp32 buffered records
+    reproduce), and the state after the window's last token is stored rounded
+    to bf16.  Returns (outputs [length, n, dv], records, S_end, next B)."""
+    S = np.array(B, np.float64, copy=True)
+    outs, records = [], []
+    for t in range(t0, t0 + length):
+        o, S, rec = step(S, tokens["q"][t], tokens["k"][t], tokens["v"][t],
+                         tokens["beta"][t], tokens["alpha"][t], gate, flags)
+        outs.append(o)
+        records.append(rec)
+    return np.stack(outs), records, S, round_bf16(S)
+
+
+def run_windowed_bf16(S_init, tokens, p, gate, flags=0):
+    """Free-running "BF16 + per-window" decode: B_0 = bf16(S_init), then
+    windows of p tokens (a final partial window is closed after its last
+    token).  Returns (outputs [T, n, dv], list of boundary states)."""
+    T = tokens["q"].shape[0]
+    B = round_bf16(S_init)
+    outs, bounds = [], [B]
+    for t0 in range(0, T, p):
+        o, _, _, B = window_bf16(B, tokens, t0, min(p, T - t0), gate, flags)
+        outs.append(o)
+        bounds.append(B)
+    return np.concatenate(outs, axis=0), bounds
+
+
 def state_mse(boundary, S_exact):
     """mean((B - S_exact)^2) per state, B the dequantized boundary state."""
     B = dequantize(boundary)

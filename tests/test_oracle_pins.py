@@ -422,3 +422,54 @@ def test_windowing_is_exact_without_delta(kda):
     o_w, b = O.run_windowed(S0, tok, 4, 0, gate, flags=O.NO_DELTA, quantizer=False)
     np.testing.assert_allclose(o_w, o_ref, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b[max(b)], S_ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# "BF16 + per-window" ([EL] Table 2): a bf16 boundary state, fp32 records
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kda", [False, True])
+def test_bf16_window_of_one_is_bf16_per_step(kda):
+    """With p = 1 the state is rounded to bf16 after every token: exactly the
+    "BF16 per-step" row."""
+    rng = np.random.default_rng(4100 + kda)
+    T, n, dk, dv = 9, 3, 128, 128
+    tok = _rand_tokens(rng, T, n, dk, dv, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    S0 = 0.1 * rng.standard_normal((n, dk, dv))
+    o_w, bounds = O.run_windowed_bf16(S0, tok, 1, gate)
+    S = O.round_bf16(S0)
+    for t in range(T):
+        o, S = O.step_dense_bf16(S, tok["q"][t], tok["k"][t], tok["v"][t], tok["beta"][t], tok["alpha"][t], gate)
+        np.testing.assert_array_equal(o_w[t], o)
+        np.testing.assert_array_equal(bounds[t + 1], S)
+
+
+def test_bf16_window_boundaries_are_bf16_and_outputs_exact():
+    """Boundary states hold bf16 values; inside a window the outputs are the
+    exact recurrence from the boundary (nothing is rounded mid-window)."""
+    rng = np.random.default_rng(4200)
+    T, n, p = 12, 2, 4
+    tok = _rand_tokens(rng, T, n, 128, 128, False)
+    S0 = 0.1 * rng.standard_normal((n, 128, 128))
+    o_w, bounds = O.run_windowed_bf16(S0, tok, p, O.GATE_GDN)
+    for B in bounds:
+        np.testing.assert_array_equal(O.round_bf16(B), B)
+    for w in range(T // p):
+        o_ref, _, _ = O.sequential_exact(bounds[w], {k: v[w * p:(w + 1) * p] for k, v in tok.items()}, O.GATE_GDN)
+        np.testing.assert_allclose(o_w[w * p:(w + 1) * p], o_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_per_window_error_below_per_step():
+    """The qualitative claim behind the row ([EL] Table 2, per-window bf16
+    close to fp32): rounding once per window accumulates less state error
+    than rounding after every token."""
+    rng = np.random.default_rng(4300)
+    T, n = 64, 2
+    tok = _rand_tokens(rng, T, n, 128, 128, False, alpha_lo=0.9, alpha_hi=1.0)
+    S0 = 0.1 * rng.standard_normal((n, 128, 128))
+    _, S_exact, _ = O.sequential_exact(S0, tok, O.GATE_GDN)
+    _, bw = O.run_windowed_bf16(S0, tok, 16, O.GATE_GDN)
+    _, bs = O.run_windowed_bf16(S0, tok, 1, O.GATE_GDN)
+    err_w = np.mean((bw[-1] - S_exact) ** 2)
+    err_s = np.mean((bs[-1] - S_exact) ** 2)
+    assert err_w < err_s, (err_w, err_s)
