@@ -328,6 +328,18 @@ def dense_bytes(dk, dv, kda, elem):
     return 2 * elem * dk * dv + 4 * (2 * dk + dv + 1 + G) + 4 * dv
 
 
+def bf16w_bytes(p, dk, dv, kda):
+    """Algorithmic bytes per state and token of the "BF16 + per-window" row:
+    p decode steps (read the bf16 boundary state and the buffered records,
+    read the token's inputs, write its output and record) and one window
+    close (read and write the bf16 state, read the p records), spread over
+    the window's p tokens."""
+    G = dk if kda else 1
+    R = G + dk + dv
+    dec = sum(2 * dk * dv + 4 * t * R + 4 * (2 * dk + dv + 1 + G) + 4 * dv + 4 * R for t in range(p)) / p
+    return dec + (4 * dk * dv + 4 * p * R) / p
+
+
 def ablations(args, cfg, dev, reps=3):
     """Kernel-level analogues of the pages' Table 2 and Table 3 on this
     workload's shape: head-tokens/s of each variant (all layers' states
@@ -378,6 +390,23 @@ def ablations(args, cfg, dev, reps=3):
         del S, views
         return value, dense_bytes(cfg.dk, cfg.dv, kda, 4 if dtype == torch.float32 else 2)
 
+    def bf16win(p):
+        B = S_init.to(torch.bfloat16)
+        slab = lq.LeapQuantState(n, p, 0, cfg.gate, dev)
+        views = [(slab.view(l * nl, nl), B[l * nl:(l + 1) * nl]) for l in range(L)]
+
+        def run():
+            for t in range(T):
+                j = t % p
+                for l in range(L):
+                    lq.leapquant_bf16w_decode_step(views[l][0], views[l][1], j, *targs(t, l))
+                if j == p - 1:
+                    for l in range(L):
+                        lq.leapquant_bf16w_window_close(views[l][0], views[l][1], p)
+        value = timed(run)
+        del B, slab, views
+        return value, bf16w_bytes(p, cfg.dk, cfg.dv, kda)
+
     def windowed(p, r, flags, iters=0):
         slab = lq.LeapQuantState(n, p, r, cfg.gate, dev, flags, comp_iters=iters)
         lq.leapquant_quantize_state(slab, S_init)
@@ -422,6 +451,7 @@ def ablations(args, cfg, dev, reps=3):
 
     rows2 = [("FP32 per-step", lambda: dense(torch.float32)),
              ("BF16 per-step", lambda: dense(torch.bfloat16)),
+             ("BF16 + per-window (p = 16, separate close)", lambda: bf16win(16)),
              ("INT8 per-step", lambda: windowed(1, 0, 1)),
              ("+ Per-window (p = 16)", lambda: windowed(16, 0, 1)),
              ("+ Comp. Tokens (r = 4) and smoothing", lambda: windowed(16, cfg.r, 0))]

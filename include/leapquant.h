@@ -260,6 +260,30 @@ int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype,
 /* Static description of a status code (never NULL). */
 const char *leapquant_status_string(int status);
 
+/* ---- "BF16 + per-window" ([EL] Table 2, the row between BF16 per-step and
+ * INT8 per-step): the boundary state is a dense bf16 state B [n][dk][dv]
+ * (row-major, bfloat16 bit patterns), fixed for the window.  Within the
+ * window the tokens are buffered in the fp32 records of `st` exactly as in
+ * the int8 path (only buf_gate, buf_k and buf_u of `st` are used; r,
+ * LQ_NO_SMOOTH and LQ_DENSE_COMP do not apply: flags may hold only
+ * LQ_NO_DELTA).  The decode step reads B and the records.  The window close
+ * rebuilds S = Gamma * B + K_w U in fp32 (rows scaled by the decay product
+ * Gamma of the window) and writes it back into B rounded to bf16, nearest
+ * with ties to even.  There is no fused last-token close for this row. */
+
+/* Decode token t (0 <= t < p) of the window for all n states: reads B and
+ * records 0 .. t-1, writes o and record t.  Errors as for
+ * leapquant_decode_step; B must be 16-byte aligned and overlap neither the
+ * buffer nor o. */
+int leapquant_bf16w_decode_step(const lq_params *prm, const void *B, const lq_state *st, int32_t t,
+                                const float *q, const float *k, const float *v, const float *beta,
+                                const float *alpha, float *o, hipStream_t stream);
+
+/* Close the window after len tokens (1 <= len <= p): B <- bf16(Gamma * B +
+ * K_w U).  The buffer is read, not written. */
+int leapquant_bf16w_window_close(const lq_params *prm, void *B, const lq_state *st, int32_t len,
+                                 hipStream_t stream);
+
 /* LEAPQUANT_ABI_VERSION of the loaded library. */
 int leapquant_abi_version(void);
 

@@ -9,7 +9,8 @@ torch device tensors and streams into the C calls and runs nothing itself.
 from ._lib import (LQ_DENSE_BF16, LQ_DENSE_COMP, LQ_DENSE_FP32, LQ_GATE_GDN, LQ_GATE_KDA, LQ_NO_DELTA, LQ_NO_SMOOTH,
                    LeapQuantError, LIB_PATH, load)
 from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matrix,
-                  leapquant_abi_version, leapquant_decode_close, leapquant_decode_step,
+                  leapquant_abi_version, leapquant_bf16w_decode_step, leapquant_bf16w_window_close,
+                  leapquant_decode_close, leapquant_decode_step,
                   leapquant_decode_close_slots, leapquant_decode_step_slots, leapquant_dense_step,
                   leapquant_window_close_slots,
                   leapquant_dequantize_state, leapquant_quantize_state,
@@ -19,7 +20,8 @@ __all__ = [
     "LQ_DENSE_BF16", "LQ_DENSE_COMP", "LQ_DENSE_FP32", "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_DELTA", "LQ_NO_SMOOTH",
     "LeapQuantError", "LIB_PATH", "load",
     "LeapQuantState", "code_offsets", "codes_from_matrix", "codes_to_matrix",
-    "leapquant_abi_version", "leapquant_decode_close", "leapquant_decode_step",
+    "leapquant_abi_version", "leapquant_bf16w_decode_step", "leapquant_bf16w_window_close",
+    "leapquant_decode_close", "leapquant_decode_step",
     "leapquant_decode_close_slots", "leapquant_decode_step_slots", "leapquant_dense_step",
     "leapquant_window_close_slots",
     "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",

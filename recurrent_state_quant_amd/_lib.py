@@ -36,6 +36,8 @@ EXPORTED = (
     "leapquant_decode_close_slots",
     "leapquant_window_close_slots",
     "leapquant_dequantize_state",
+    "leapquant_bf16w_decode_step",
+    "leapquant_bf16w_window_close",
     "leapquant_status_string",
     "leapquant_abi_version",
 )
@@ -83,10 +85,13 @@ def load():
     lib.leapquant_decode_close_slots.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_window_close_slots.argtypes = [P, S, vp, vp]
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
+    lib.leapquant_bf16w_decode_step.argtypes = [P, vp, S, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_bf16w_window_close.argtypes = [P, vp, S, i32, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
               "leapquant_decode_close", "leapquant_dense_step", "leapquant_decode_step_slots",
               "leapquant_decode_close_slots", "leapquant_window_close_slots",
-              "leapquant_dequantize_state"):
+              "leapquant_dequantize_state", "leapquant_bf16w_decode_step",
+              "leapquant_bf16w_window_close"):
         getattr(lib, f).restype = ctypes.c_int
     lib.leapquant_status_string.argtypes = [ctypes.c_int]
     lib.leapquant_status_string.restype = ctypes.c_char_p

@@ -242,6 +242,28 @@ def leapquant_window_close_slots(state, lengths, stream=None):
                                                   _stream(stream, state.device)))
 
 
+def _bf16_ptr(state, B):
+    return _ptr(B, torch.bfloat16, (state.n, state.dk, state.dv), "B")
+
+
+def leapquant_bf16w_decode_step(state, B, t, q, k, v, beta, alpha, o, stream=None):
+    """"BF16 + per-window": decode token t from the bf16 boundary state B
+    [n, dk, dv] (torch.bfloat16) and the window buffer of `state` (its
+    int8 boundary arrays are not used)."""
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_bf16w_decode_step(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
+                                                 int(t), *args, _stream(stream, state.device)))
+
+
+def leapquant_bf16w_window_close(state, B, length, stream=None):
+    """"BF16 + per-window": B <- bf16(Gamma * B + K_w U) over `length`
+    buffered records."""
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_bf16w_window_close(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
+                                                  int(length), _stream(stream, state.device)))
+
+
 def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0):
     """One token for dense states S [n][dk][dv] (float32, or bfloat16), in
     place; the uncompressed baseline of the quantized path.  flags may hold

@@ -393,6 +393,82 @@ int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const flo
   return hip_status(lq::launch_dense_step(a, kda, bf16, stream));
 }
 
+// ---- "BF16 + per-window": dense bf16 boundary state, fp32 window buffer
+static int check_bf16w(const lq_params *prm, const void *B, const lq_state *st) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if (prm->flags & ~static_cast<uint32_t>(LQ_NO_DELTA)) return LQ_ERR_SHAPE;
+  if (!st || !B) return LQ_ERR_NULL;
+  if ((rc = check_buffer(prm, st))) return rc;
+  if (!aligned(B, 16)) return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const Range b = span(B, n * kDim * kDim * 2);
+  const size_t gate_elems = prm->gate == LQ_GATE_KDA ? n * prm->p * kDim : n * prm->p;
+  if (overlap(b, span(st->buf_gate, gate_elems * sizeof(float))) ||
+      overlap(b, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
+      overlap(b, span(st->buf_u, n * prm->p * kDim * sizeof(float))))
+    return LQ_ERR_ALIAS;
+  return LQ_OK;
+}
+
+int leapquant_bf16w_decode_step(const lq_params *prm, const void *B, const lq_state *st, int32_t t,
+                                const float *q, const float *k, const float *v, const float *beta,
+                                const float *alpha, float *o, hipStream_t stream) {
+  int rc = check_bf16w(prm, B, st);
+  if (rc) return rc;
+  if (t < 0 || t >= prm->p) return LQ_ERR_SHAPE;
+  if (!q || !k || !v || !beta || !alpha || !o) return LQ_ERR_NULL;
+  const bool kda = prm->gate == LQ_GATE_KDA;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(beta, 4) || !aligned(alpha, kda ? 16 : 4))
+    return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const size_t vec = n * kDim * sizeof(float);
+  const Range out = span(o, vec);
+  const size_t gate_elems = kda ? n * prm->p * kDim : n * prm->p;
+  if (overlap(out, span(q, vec)) || overlap(out, span(k, vec)) || overlap(out, span(v, vec)) ||
+      overlap(out, span(beta, n * sizeof(float))) ||
+      overlap(out, span(alpha, kda ? vec : n * sizeof(float))) ||
+      overlap(out, span(B, n * kDim * kDim * 2)) ||
+      overlap(out, span(st->buf_gate, gate_elems * sizeof(float))) ||
+      overlap(out, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
+      overlap(out, span(st->buf_u, n * prm->p * kDim * sizeof(float))))
+    return LQ_ERR_ALIAS;
+  lq::Bf16WinArgs a{};
+  a.B = static_cast<uint16_t *>(const_cast<void *>(B));
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.t = t;
+  a.flags = prm->flags;
+  return hip_status(lq::launch_bf16w_decode(a, kda, stream));
+}
+
+int leapquant_bf16w_window_close(const lq_params *prm, void *B, const lq_state *st, int32_t len,
+                                 hipStream_t stream) {
+  int rc = check_bf16w(prm, B, st);
+  if (rc) return rc;
+  if (len < 1 || len > prm->p) return LQ_ERR_SHAPE;
+  lq::Bf16WinArgs a{};
+  a.B = static_cast<uint16_t *>(B);
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.t = len;
+  a.flags = prm->flags;
+  return hip_status(lq::launch_bf16w_close(a, prm->gate == LQ_GATE_KDA, stream));
+}
+
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st, float *S_out,
                                hipStream_t stream) {
   int rc = check_params(prm);

@@ -70,7 +70,23 @@ struct DenseArgs {
   unsigned flags;  // bit 1: b_t = 0 (no delta correction)
 };
 
+// "BF16 + per-window": a dense bf16 boundary state B [n][dk][dv] and the
+// fp32 window buffer.  t: the token's window position (decode) or the
+// number of records to replay (close).
+struct Bf16WinArgs {
+  uint16_t *B;
+  float *buf_gate;
+  float *buf_k;
+  float *buf_u;
+  const float *q, *k, *v, *beta, *alpha;
+  float *o;
+  int n, p, t;
+  unsigned flags;  // bit 1: b_t = 0 (no delta correction)
+};
+
 hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_bf16w_decode(const Bf16WinArgs &a, bool kda, hipStream_t stream);
+hipError_t launch_bf16w_close(const Bf16WinArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_dense_step(const DenseArgs &a, bool kda, bool bf16, hipStream_t stream);
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream);

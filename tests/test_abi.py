@@ -228,3 +228,34 @@ def test_dense_compensator_validation(lib, entry):
     nokey, _ = _state(comp_key=0)
     r0 = _params(flags=L.LQ_DENSE_COMP, r=0)
     assert lib.leapquant_dequantize_state(ctypes.byref(r0), ctypes.byref(nokey), 0, None) == L.LQ_ERR_NULL
+
+
+def test_bf16_window_validation(lib):
+    """"BF16 + per-window": B must be given, 16-byte aligned and apart from
+    the buffer; only LQ_NO_DELTA applies; t and len ranges as for the int8
+    entry points."""
+    st, base = _state()
+    prm = _params()
+    vec = 4 * 512
+    B = base + (1 << 30)
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+
+    def dec(B_=B, prm_=prm, t=0, **kw):
+        x = dict(a, **kw)
+        return lib.leapquant_bf16w_decode_step(ctypes.byref(prm_), B_, ctypes.byref(st), t, x["q"], x["k"],
+                                               x["v"], x["beta"], x["alpha"], x["o"], None)
+
+    def close(B_=B, prm_=prm, n_=16):
+        return lib.leapquant_bf16w_window_close(ctypes.byref(prm_), B_, ctypes.byref(st), n_, None)
+
+    assert dec(B_=None) == L.LQ_ERR_NULL and close(B_=None) == L.LQ_ERR_NULL
+    assert dec(B_=B + 8) == L.LQ_ERR_ALIGN and close(B_=B + 8) == L.LQ_ERR_ALIGN
+    assert dec(B_=st.buf_k) == L.LQ_ERR_ALIAS and close(B_=st.buf_u) == L.LQ_ERR_ALIAS
+    assert dec(o=B + 4096) == L.LQ_ERR_ALIAS
+    assert dec(prm_=_params(flags=L.LQ_NO_SMOOTH)) == L.LQ_ERR_SHAPE
+    assert dec(prm_=_params(flags=L.LQ_DENSE_COMP)) == L.LQ_ERR_SHAPE
+    assert dec(t=-1) == L.LQ_ERR_SHAPE and dec(t=16) == L.LQ_ERR_SHAPE
+    assert close(n_=0) == L.LQ_ERR_SHAPE and close(n_=17) == L.LQ_ERR_SHAPE
+    assert dec(q=0) == L.LQ_ERR_NULL
+    assert close(prm_=_params(dk=64)) == L.LQ_ERR_UNSUPPORTED
