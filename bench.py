@@ -85,19 +85,28 @@ def bytes_per_head_token(p, dk, dv, r, kda, fused=False, dense=False):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gdn_b256_4layers.txt")
-KERNEL_SRC = os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", "lq_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", f)
+               for f in ("lq_device.h", "lq_decode.hip", "lq_close.hip", "lq_baselines.hip")]
+
+
+def kernel_source_sha256():
+    """sha256 of the kernel sources, concatenated in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(cfg):
     """HBM bytes per state {decode, close, fused} from the committed
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary; empty when the counters were
     taken on another workload or on kernel source that has changed since."""
-    import hashlib
     from workloads.configs import HEADLINE
     if cfg.name != HEADLINE or not os.path.exists(TRAFFIC_FILE):
         return {}
     doc = json.load(open(TRAFFIC_FILE))
-    if doc.get("source_sha256") != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
+    if doc.get("source_sha256") != kernel_source_sha256():
         return {}
     names = {"decode_fused": "decode_step_kernel<GDN> (fused schedule)",
              "decode_separate": "decode_step_kernel<GDN> (separate schedule)",

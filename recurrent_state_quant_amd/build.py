@@ -6,7 +6,9 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libleapquant.so")
-SOURCES = [os.path.join(PKG_DIR, "csrc", f) for f in ("lq_kernels.hip", "lq_abi.cpp")]
+KERNEL_SOURCES = ("lq_device.h", "lq_decode.hip", "lq_close.hip", "lq_baselines.hip")
+SOURCES = [os.path.join(PKG_DIR, "csrc", f) for f in ("lq_decode.hip", "lq_close.hip", "lq_baselines.hip",
+                                                     "lq_abi.cpp")]
 ARCH = "gfx950"
 
 

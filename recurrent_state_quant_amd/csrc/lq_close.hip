@@ -1,0 +1,774 @@
+// LeapQuant window close, fused last-token close, initial split and
+// dequantize for gfx950: one 256-thread workgroup per state.
+#include "lq_device.h"
+
+namespace lq {
+
+// ---------------------------------------------------------------------------
+// Window close and initial quantization: 256 threads (4 waves) per state.
+//
+// The rebuilt fp32 state lives in MFMA accumulators.  Wave w owns the rows
+// of half h = w & 1 (64h .. 64h+63) and the columns of half ch = w >> 1
+// (64ch .. 64ch+63) as 4 x 4 tiles of 16 x 16 (tile ct holds columns
+// 64ch + 16ct .. +15).  Lane l (lr = l >> 4, lc = l & 15) holds, for each of
+// its 4 columns 64ch + 16ct + lc, the 16 rows 64h + 16rt + 4lr + v (rt, v =
+// 0..3), which are slots 16lr .. 16lr+15 of that column's segment in the
+// code layout: codes are read and written as one 16-byte access per column,
+// and one wave instruction covers 16 adjacent column segments (1 KiB of
+// whole cache lines).
+//   acc  = Gamma (deQ + comps)    (window of <= kChunk records: the MFMAs
+//                                  accumulate onto it)
+//   acc += K_w U                  (v_mfma_f32_16x16x4_f32 over the records,
+//                                  newest chunk first: the decays are
+//                                  running products)
+// with K_w[i][row] = rho_i[row] k~_i[row].  Longer windows start from zero
+// and add the boundary term after the last chunk.  Each record chunk is
+// staged in LDS with 128-bit loads issued by all 256 threads before the
+// first LDS write.
+// Then (split_state): row norms, top-r rank selection, extraction, column
+// absmax (smoothing scale), per-row absmax and int8 codes.  Row reductions
+// combine the two column-half waves through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kChunk = 16;  // records staged in LDS per MFMA pass
+
+// Code byte B of `word` from x = q * inv (|x| <= 127): adding 1.5 * 2^23
+// rounds x to the nearest integer, ties to even, and leaves that integer's
+// two's-complement low byte in the low byte of the sum's bit pattern; the
+// SDWA form of the add writes exactly that byte into byte B of `word` and
+// keeps the other three.
+template <int B>
+__device__ __forceinline__ void pack_code(uint32_t &word, float x) {
+  static_assert(B >= 0 && B < 4, "byte index");
+  const float magic = 12582912.0f;
+  if (B == 0)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else if (B == 1)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else if (B == 2)
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+  else
+    asm volatile("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+                 : "+v"(word) : "v"(x), "v"(magic));
+}
+
+__device__ __forceinline__ float f4get(const float4 &x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+__device__ __forceinline__ uint32_t u4get(const uint4 &x, int i) {
+  return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+}
+
+struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
+  float *part;       // [2][D] per column half: row norms^2, later row absmax
+  int *sel;          // [D] compensator slot of a row or -1
+  float *cmx;        // [8][D] column-max partials
+  float *sig;        // [D] 1 / s_j
+  float *inv;        // [D] 127 / m_i (0 for zero or extracted rows)
+  // dense compensator tokens only, [16][D] each
+  float *dq;         // keys K (row c: k_c)
+  float *dw;         // W = K S (row c: w_c)
+  float *dy;         // Y = S W^T (row c: column c of Y)
+};
+
+constexpr float kMgsDrop = 1e-3f;  // relative projected norm at or below which a key is dropped
+
+// Dense compensator tokens of the state in acc (r >= 1), after the top-r
+// rows have set one-hot keys in L.dq: `iters` rounds of subspace iteration
+// K <- MGS(S S^T K), then W = K S (w_c = S^T k_c), the keys and values
+// written out, and the residual S - sum_c k_c w_c^T left in acc.  Partial
+// sums of the two row halves (W) and of the two column halves (Y) meet in
+// LDS: one half stores into a free [16][D] array, then all threads add.
+__device__ __forceinline__ void dense_comp_split(floatx4 (&acc)[4][4], const SplitLds &L, float *comp_key,
+                                                 float *comp_val, size_t s, int r, int iters) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;
+  const int col0 = 64 * ch + lc;
+  // dst[e] += src[e] for the r rows of [16][D] arrays, all threads
+  auto add_halves = [&](float *dst, const float *src) {
+    for (int e = tid; e < r * (D / 4); e += 256) {
+      float4 x = reinterpret_cast<float4 *>(dst)[e];
+      const float4 y = reinterpret_cast<const float4 *>(src)[e];
+      x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+      reinterpret_cast<float4 *>(dst)[e] = x;
+    }
+  };
+  for (int it = 0;; ++it) {
+    // ---- W = K S: each lane sums its 16 rows of the half, lanes 16 and 32
+    // apart hold the half's other rows; halves meet in dw (h = 0) + dy (h = 1)
+    float *wdst = h == 0 ? L.dw : L.dy;
+    for (int c = 0; c < r; ++c) {
+      float pw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 k4 = *reinterpret_cast<const float4 *>(L.dq + c * D + rbase + 16 * rt);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) pw[ct] = fmaf(f4get(k4, v), acc[rt][ct][v], pw[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        pw[ct] += __shfl_xor(pw[ct], 16);
+        pw[ct] += __shfl_xor(pw[ct], 32);
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) wdst[c * D + col0 + 16 * ct] = pw[ct];
+      }
+    }
+    __syncthreads();
+    add_halves(L.dw, L.dy);
+    __syncthreads();
+    if (it == iters) break;
+    // ---- Y = S W^T: each lane sums its 4 columns, the 16 lanes of a DPP
+    // row hold the half's other columns; halves meet in dy (ch = 0) + dq
+    // (ch = 1: the keys are not read again this round)
+    float *ydst = ch == 0 ? L.dy : L.dq;
+    for (int c = 0; c < r; ++c) {
+      float wv[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) wv[ct] = L.dw[c * D + col0 + 16 * ct];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        float y[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) x = fmaf(acc[rt][ct][v], wv[ct], x);
+          y[v] = row16_sum(x);
+        }
+        if (lc == 0)
+          *reinterpret_cast<float4 *>(ydst + c * D + rbase + 16 * rt) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+    __syncthreads();
+    add_halves(L.dy, L.dq);
+    __syncthreads();
+    // ---- K = MGS(Y) on wave 0: lane l holds rows 2l and 2l+1
+    if (w == 0) {
+      for (int c = 0; c < r; ++c) {
+        float2 v = *reinterpret_cast<const float2 *>(L.dy + c * D + 2 * lane);
+        const float n0 = sqrtf(wave_sum(v.x * v.x + v.y * v.y));
+        for (int c2 = 0; c2 < c; ++c2) {
+          const float2 q = *reinterpret_cast<const float2 *>(L.dq + c2 * D + 2 * lane);
+          const float d = wave_sum(q.x * v.x + q.y * v.y);
+          v.x = fmaf(-d, q.x, v.x);
+          v.y = fmaf(-d, q.y, v.y);
+        }
+        const float nv = sqrtf(wave_sum(v.x * v.x + v.y * v.y));
+        const bool keep = nv > 0.f && nv > kMgsDrop * n0;
+        *reinterpret_cast<float2 *>(L.dq + c * D + 2 * lane) =
+            keep ? make_float2(v.x / nv, v.y / nv) : make_float2(0.f, 0.f);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- keys and values out; residual S - sum_c k_c w_c^T
+  for (int e = tid; e < r * (D / 4); e += 256) {
+    reinterpret_cast<float4 *>(comp_key + s * r * D)[e] = reinterpret_cast<const float4 *>(L.dq)[e];
+    reinterpret_cast<float4 *>(comp_val + s * r * D)[e] = reinterpret_cast<const float4 *>(L.dw)[e];
+  }
+  for (int c = 0; c < r; ++c) {
+    float wv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) wv[ct] = L.dw[c * D + col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(L.dq + c * D + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(-f4get(k4, v), wv[ct], acc[rt][ct][v]);
+    }
+  }
+}
+
+// a6-a8 on the fp32 state held in acc: row norms, top-r extraction (writes
+// comp_idx, comp_val; with DENSE the dense tokens started from those rows,
+// also comp_key), smoothing scales (col_scale), row scales (row_scale) and
+// int8 codes, all for state s.  Ends with every LDS array consumed.
+template <bool DENSE>
+__device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds &L, int8_t *codes,
+                                            float *row_scale, float *col_scale, int32_t *comp_idx,
+                                            float *comp_val, float *comp_key, size_t s, int r, int iters,
+                                            unsigned flags) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;  // row of (rt, v) = rbase + 16 rt + v
+  const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
+  // ---- a6 row L2 norms (squared, fp32; two column-half partials)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float q = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) q = fmaf(acc[rt][ct][v], acc[rt][ct][v], q);
+      q = row16_sum(q);
+      if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = q;
+    }
+  if (tid < D) L.sel[tid] = -1;
+  if (DENSE)
+    for (int e = tid; e < r * D; e += 256) L.dq[e] = 0.f;
+  __syncthreads();
+  if (w == 0 && r > 0) {
+    // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
+    // takes the largest remaining norm, ties to the lower row index
+    float n0 = L.part[2 * lane] + L.part[D + 2 * lane];
+    float n1 = L.part[2 * lane + 1] + L.part[D + 2 * lane + 1];
+    for (int c = 0; c < r; ++c) {
+      const bool pick1 = n1 > n0;  // equal norms keep the lower row
+      const float best = pick1 ? n1 : n0;
+      const float m = row16_max(best);
+      const float mx = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+                             fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+      const unsigned long long hit = __ballot(best == mx && best >= 0.f);
+      int wl, odd;
+      if (hit) {
+        wl = __ffsll((long long)hit) - 1;
+        odd = __builtin_amdgcn_readlane((int)pick1, wl);
+      } else {
+        // only reachable with NaN norms: take the lowest row not yet picked
+        const unsigned long long f0 = __ballot(n0 != -1.f), f1 = __ballot(n1 != -1.f);
+        wl = __ffsll((long long)(f0 | f1)) - 1;
+        odd = ((f0 >> wl) & 1ull) ? 0 : 1;
+      }
+      const int wrow = 2 * wl + odd;
+      if (lane == wl) {
+        if (odd) n1 = -1.f; else n0 = -1.f;
+      }
+      if (lane == 0) {
+        if (DENSE) L.dq[c * D + wrow] = 1.f;  // one-hot start key
+        else L.sel[wrow] = c;
+        comp_idx[s * r + c] = wrow;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- extraction and a7 column absmax of the residual.  Extracted rows
+  // are written out and zeroed in the lanes that hold them (a branch that
+  // most waves skip), so they drop out of the column maxima and get row
+  // scale 0 (hence codes 0) below.  DENSE: the dense tokens leave the
+  // residual S - sum_c k_c w_c^T instead.
+  if constexpr (DENSE) {
+    if (r > 0) dense_comp_split(acc, L, comp_key, comp_val, s, r, iters);
+  } else {
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int4 sl4 = *reinterpret_cast<const int4 *>(L.sel + rbase + 16 * rt);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int sel = v == 0 ? sl4.x : v == 1 ? sl4.y : v == 2 ? sl4.z : sl4.w;
+      if (sel >= 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) comp_val[(s * r + sel) * D + col0 + 16 * ct] = acc[rt][ct][v];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = 0.f;
+      }
+    }
+  }
+  }
+  float cm[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    float m = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(acc[rt][ct][v]));
+    cm[ct] = m;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) L.cmx[(4 * h + lr) * D + col0 + 16 * ct] = cm[ct];
+  __syncthreads();
+  if (tid < D) {
+    float m = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) m = fmaxf(m, L.cmx[g * D + tid]);
+    const float sc = (flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
+    col_scale[s * D + tid] = sc;
+    L.sig[tid] = 1.f / sc;  // sigma_j, correctly rounded
+  }
+  __syncthreads();
+
+  // ---- a8 smoothed residual q = R * sigma (in place), per-row absmax
+  {
+    float sig[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) sig[ct] = L.sig[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float m = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          acc[rt][ct][v] = acc[rt][ct][v] * sig[ct];
+          m = fmaxf(m, fabsf(acc[rt][ct][v]));
+        }
+        m = row16_max_nn(m);
+        if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = m;
+      }
+  }
+  __syncthreads();
+  if (tid < D) {
+    // row scale and its reciprocal, once per row (correctly rounded)
+    const float m = fmaxf(L.part[tid], L.part[D + tid]);
+    float a = 0.f, inv = 0.f;
+    if (m > 0.f && L.sel[tid] < 0) {
+      a = m / 127.f;
+      inv = 127.f / m;
+    }
+    row_scale[s * D + tid] = a;
+    L.inv[tid] = inv;
+  }
+  __syncthreads();
+  // codes: rne(q * inv), one v_add_f32 per code (see pack_code); the
+  // product is rounded on its own: no contraction into an FMA.
+  {
+    float4 iv[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) iv[rt] = *reinterpret_cast<const float4 *>(L.inv + rbase + 16 * rt);
+    int8_t *cdst = codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;  // + 1024 ct
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma clang fp contract(off)
+      uint32_t wd[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        wd[rt] = 0u;
+        pack_code<0>(wd[rt], acc[rt][ct][0] * iv[rt].x);
+        pack_code<1>(wd[rt], acc[rt][ct][1] * iv[rt].y);
+        pack_code<2>(wd[rt], acc[rt][ct][2] * iv[rt].z);
+        pack_code<3>(wd[rt], acc[rt][ct][3] * iv[rt].w);
+      }
+      __builtin_nontemporal_store(vu4{wd[0], wd[1], wd[2], wd[3]},
+                                  reinterpret_cast<vu4 *>(cdst + ct * 1024));
+    }
+  }
+}
+
+// ---- a9: split a caller fp32 state (one workgroup per state)
+template <bool DENSE>
+__global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
+  const size_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  __shared__ float sh_part[2 * D], sh_sig[D];
+  __shared__ __attribute__((aligned(16))) float sh_inv[D];
+  __shared__ __attribute__((aligned(16))) int sh_sel[D];
+  __shared__ __attribute__((aligned(16))) float sh_cmx[8 * D];
+  __shared__ __attribute__((aligned(16))) float sh_dq[DENSE ? 16 * D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_dw[DENSE ? 16 * D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_dy[DENSE ? 16 * D : 4];
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 64 * h + 16 * rt + 4 * lr + v;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        acc[rt][ct][v] = __builtin_nontemporal_load(A.S_in + (s * D + row) * D + 64 * ch + 16 * ct + lc);
+    }
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv, sh_dq, sh_dw, sh_dy};
+  split_state<DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s,
+                     A.r, A.iters, A.flags);
+}
+
+// ---- a5-a8: window close, one workgroup per state.  With FUSED the
+// workgroup first decodes the window's last token t from the rebuilt fp32
+// state: the decay chain starts at alpha_t, so the accumulators hold
+// D_t S_{t-1}; then z = (D_t S_{t-1})^T k_t = S_{t-1}^T b_t and
+// (D_t S_{t-1})^T q_t = S_{t-1}^T (alpha_t q_t), u_t = v_t - z_b,
+// o_t = z_q + (k~_t . q_t) u_t, and S_t = D_t S_{t-1} + k~_t u_t^T is split.
+// KDA row closes are held to 128 VGPRs (4 waves per SIMD; their LDS fits 4
+// workgroups per CU with the split's column maxima in the dead gate array):
+// 12% faster than 3 workgroups per CU.
+template <bool KDA, bool FUSED, bool DENSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DENSE ? 4 : 1))) void close_kernel(const CloseArgs A) {
+  const size_t s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;
+  const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
+  const int r = A.r, p = A.p;
+  // per-slot record counts (continuous batching); a slot outside the valid
+  // range is left untouched.  FUSED: len is the last token's position t.
+  const int len = A.lens ? A.lens[s] : A.len;
+  if (FUSED ? (len < 0 || len >= p) : (len < 1 || len > p)) return;
+  const size_t rec0 = s * p;
+
+  __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
+  __shared__ __attribute__((aligned(16))) float sh_U[kChunk * D];
+  __shared__ __attribute__((aligned(16))) float sh_g[KDA ? kChunk * D : kChunk];
+  __shared__ __attribute__((aligned(16))) float sh_a[D];
+  __shared__ __attribute__((aligned(16))) float sh_ag[D];  // a_i * Gamma_i
+  __shared__ __attribute__((aligned(16))) float sh_gam[D];
+  __shared__ __attribute__((aligned(16))) float sh_s[D];
+  __shared__ __attribute__((aligned(16))) int sh_cslot[D];  // compensator slot of a row or -1
+  __shared__ __attribute__((aligned(16))) float sh_comp[16 * D];  // compensator rows w_c
+  // FUSED: the last token's k, q, k~ per row, u per column, k~ . q per wave
+  __shared__ __attribute__((aligned(16))) float sh_tk[FUSED ? D : 4], sh_tq[FUSED ? D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_tkt[FUSED ? D : 4], sh_tu[FUSED ? D : 4];
+  __shared__ float sh_kq[2];
+  __shared__ float sh_part[2 * D], sh_sig[D];
+  __shared__ __attribute__((aligned(16))) float sh_inv[D];
+  __shared__ __attribute__((aligned(16))) int sh_sel[D];
+  // column-max partials of the split; KDA: in the per-row gate array, dead by then
+  __shared__ __attribute__((aligned(16))) float sh_cmx[KDA ? 4 : 8 * D];
+
+  // boundary-state side data and this lane's code segments, issued first
+  if (tid < D) {
+    sh_a[tid] = A.row_scale[s * D + tid];
+    sh_s[tid] = A.col_scale[s * D + tid];
+  }
+  if (tid < D) sh_cslot[tid] = -1;
+  const int8_t *csrc = A.codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;
+  uint4 cw[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
+
+  floatx4 acc[4][4];
+  // acc (+)= Gamma ((c (a Gamma)) s + compensator rows); Gamma from sh_gam
+  auto add_boundary = [&](bool first) {
+    float sv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) sv[ct] = sh_s[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 ag4 = *reinterpret_cast<const float4 *>(sh_ag + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float ag = f4get(ag4, v);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const float x = (float)(int8_t)(u4get(cw[ct], rt) >> (8 * v)) * (ag * sv[ct]);
+          acc[rt][ct][v] = first ? x : acc[rt][ct][v] + x;
+        }
+      }
+    }
+    // compensator rows: the lanes holding row idx_c add Gamma_idx * w_c
+    // (sh_cslot maps a row to its compensator slot or -1); dense tokens
+    // join the contraction instead
+    if (DENSE) return;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int4 cs4 = *reinterpret_cast<const int4 *>(sh_cslot + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = v == 0 ? cs4.x : v == 1 ? cs4.y : v == 2 ? cs4.z : cs4.w;
+        if (c >= 0) {
+          const float G = sh_gam[rbase + 16 * rt + v];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            acc[rt][ct][v] = fmaf(G, sh_comp[c * D + col0 + 16 * ct], acc[rt][ct][v]);
+        }
+      }
+    }
+  };
+
+  // stage records lo .. hi-1 in LDS (zero-padded to a multiple of 4) and
+  // fold the decays into K: sh_K[j] *= P, P *= gate_j, newest first.
+  // FUSED: the first call also stages the last token's k, q, k~ (rows) and
+  // v (columns), and starts the decay chain at alpha_t.
+  float P = 1.f;  // running decay product for row tid (tid < D)
+  auto stage = [&](int lo, int hi, bool first) {
+    const int cnt = hi - lo, cnt4 = (cnt + 3) & ~3;
+    __syncthreads();
+    {
+      // kChunk * D / 4 = 512 float4 per array: two per thread, all loads
+      // of the chunk issued before the first LDS write
+      static_assert(kChunk * D / 4 == 512, "staging assumes two float4 per thread");
+      const float *su = A.buf_u + (rec0 + lo) * D;
+      const float *sk = A.buf_k + (rec0 + lo) * D;
+      const float *sg = A.buf_gate + (rec0 + lo) * D;
+      float4 *du = reinterpret_cast<float4 *>(sh_U);
+      float4 *dk = reinterpret_cast<float4 *>(sh_K);
+      float4 *dg = reinterpret_cast<float4 *>(sh_g);
+      const int nvec = cnt * (D / 4), npad = cnt4 * (D / 4);
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int e0 = tid, e1 = tid + 256;
+      // the compensator rows (r * 32 float4) come with the first chunk;
+      // rows 8 .. r-1 (r > 8 only) follow it
+      const int ncv = (first && !DENSE) ? r * (D / 4) : 0;
+      float4 c0 = z4;
+      if (e0 < ncv) c0 = ld4(A.comp_val + s * r * D + 4 * e0);
+      float tk = 0.f, tq = 0.f, tv = 0.f, tb = 0.f;
+      if (FUSED && first && tid < D) {
+        tk = A.k[s * D + tid];
+        tq = A.q[s * D + tid];
+        tv = A.v[s * D + tid];
+        tb = A.beta[s];
+        P = KDA ? A.alpha[s * D + tid] : A.alpha[s];
+      }
+      float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
+      if (e0 < nvec) {
+        u0 = ld4(su + 4 * e0);
+        k0 = ld4(sk + 4 * e0);
+        if (KDA) g0 = ld4(sg + 4 * e0);
+      }
+      if (e1 < nvec) {
+        u1 = ld4(su + 4 * e1);
+        k1 = ld4(sk + 4 * e1);
+        if (KDA) g1 = ld4(sg + 4 * e1);
+      }
+      float gsc = 1.f;
+      if (!KDA && tid < cnt) gsc = A.buf_gate[rec0 + lo + tid];
+      if (e0 < npad) {
+        du[e0] = u0;
+        dk[e0] = k0;
+        if (KDA && e0 < nvec) dg[e0] = g0;
+      }
+      if (e1 < npad) {
+        du[e1] = u1;
+        dk[e1] = k1;
+        if (KDA && e1 < nvec) dg[e1] = g1;
+      }
+      if (!KDA && tid < cnt) sh_g[tid] = gsc;
+      float4 *dc = reinterpret_cast<float4 *>(sh_comp);
+      if (e0 < ncv) dc[e0] = c0;
+      if (e1 < ncv) dc[e1] = ld4(A.comp_val + s * r * D + 4 * e1);
+      if (FUSED && first && tid < D) {
+        sh_tk[tid] = (A.flags & 2u) ? 0.f : tk;  // b_t = 0 without the delta correction
+        sh_tq[tid] = tq;
+        sh_tkt[tid] = tb * tk;
+        sh_tu[tid] = tv;  // v_t; replaced by u_t after the decode
+      }
+    }
+    __syncthreads();
+    if (tid < D) {
+      for (int j = cnt - 1; j >= 0; --j) {
+        sh_K[j * D + tid] *= P;
+        P *= KDA ? sh_g[j * D + tid] : sh_g[j];
+      }
+    }
+  };
+  // acc += K_w U over the staged records
+  auto contract = [&](int cnt) {
+    const int cnt4 = (cnt + 3) & ~3;
+    for (int ks = 0; ks < cnt4 / 4; ++ks) {
+      const int kr = 4 * ks + lr;
+      float a[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) a[rt] = sh_K[kr * D + 64 * h + 16 * rt + lc];
+      float bb[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bb[ct] = sh_U[kr * D + col0 + 16 * ct];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt], bb[ct], acc[rt][ct], 0, 0, 0);
+    }
+  };
+  auto set_gamma = [&]() {
+    if (tid < D) {
+      sh_gam[tid] = P;
+      sh_ag[tid] = sh_a[tid] * P;
+    }
+    if (!DENSE && tid < r) {
+      // comp_idx entries outside [0, dk) are ignored
+      const int idx = A.comp_idx[s * r + tid];
+      if ((unsigned)idx < (unsigned)D) sh_cslot[idx] = tid;
+    }
+    if (FUSED && tid < D) {
+      const float kq = wave_sum(sh_tkt[tid] * sh_tq[tid]);  // waves 0 and 1, all lanes active
+      if (lane == 0) sh_kq[w] = kq;
+    }
+    __syncthreads();
+  };
+
+  if (len <= kChunk) {
+    // one chunk: Gamma is known before the contraction, so the boundary
+    // term initialises the accumulators
+    stage(0, len, true);
+    set_gamma();
+    add_boundary(true);
+    contract(len);
+  } else {
+    // newest chunk first; the accumulators start at zero after its staging
+    stage(len - kChunk, len, true);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    contract(kChunk);
+    for (int hi = len - kChunk; hi > 0; hi -= kChunk) {
+      const int lo = hi > kChunk ? hi - kChunk : 0;
+      stage(lo, hi, false);
+      __syncthreads();
+      contract(hi - lo);
+    }
+    set_gamma();
+    add_boundary(false);
+  }
+  if (DENSE && r > 0) {
+    // dense compensator tokens: r more records of the contraction, written
+    // before the window's first token: K column Gamma * k_c, U row w_c
+    __syncthreads();  // every wave is done with the staged records
+    {
+      const int r4 = (r + 3) & ~3;
+      float4 *dk = reinterpret_cast<float4 *>(sh_K);
+      float4 *du = reinterpret_cast<float4 *>(sh_U);
+      for (int e = tid; e < r4 * (D / 4); e += 256) {
+        const int c = e >> 5, i4 = e & 31;
+        float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), ww = kk;
+        if (c < r) {
+          kk = ld4(A.comp_key + (s * r + c) * D + 4 * i4);
+          ww = ld4(A.comp_val + (s * r + c) * D + 4 * i4);
+          const float4 g = *reinterpret_cast<const float4 *>(sh_gam + 4 * i4);
+          kk.x *= g.x; kk.y *= g.y; kk.z *= g.z; kk.w *= g.w;
+        }
+        dk[e] = kk;
+        du[e] = ww;
+      }
+    }
+    __syncthreads();
+    contract(r);
+  }
+  if (FUSED) {
+    // z = acc^T k_t and acc^T q_t: each lane sums its 16 rows for its 4
+    // columns; the 8 (row half, lane group) partials meet in LDS
+    float zb[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(sh_tk + rbase + 16 * rt);
+      const float4 q4 = *reinterpret_cast<const float4 *>(sh_tq + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          zb[ct] = fmaf(acc[rt][ct][v], f4get(k4, v), zb[ct]);
+          zq[ct] = fmaf(acc[rt][ct][v], f4get(q4, v), zq[ct]);
+        }
+    }
+    __syncthreads();  // every wave is done with sh_K
+    float2 *zp = reinterpret_cast<float2 *>(sh_K);  // [8][D]
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) zp[(4 * h + lr) * D + col0 + 16 * ct] = make_float2(zb[ct], zq[ct]);
+    __syncthreads();
+    if (tid < D) {
+      float b = 0.f, q = 0.f;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float2 x = zp[g * D + tid];
+        b += x.x;
+        q += x.y;
+      }
+      const float u = sh_tu[tid] - b;
+      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + tid);
+      sh_tu[tid] = u;
+    }
+    __syncthreads();
+    // S_t = D_t S_{t-1} + k~_t u_t^T
+    float uu[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) uu[ct] = sh_tu[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 kt4 = *reinterpret_cast<const float4 *>(sh_tkt + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(f4get(kt4, v), uu[ct], acc[rt][ct][v]);
+    }
+  }
+  // every read of this state's compensator rows is done before the split
+  // overwrites them
+  __syncthreads();
+  const SplitLds L{sh_part, sh_sel, KDA ? sh_g : sh_cmx, sh_sig, sh_inv, sh_K, sh_U, sh_comp};
+  split_state<DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s, r,
+                     A.iters, A.flags);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: S_out = deQ(codes, a, s) + compensator rows (fp32).  Thread
+// (half hh, column j) reads the 64 code bytes of its column segment and
+// writes column j of rows 64hh .. 64hh+63.
+// ---------------------------------------------------------------------------
+template <bool DENSE>
+__global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
+  const size_t s = blockIdx.x;
+  const int j = threadIdx.x & (D - 1), hh = threadIdx.x >> 7;
+  const int r = A.r;
+  const float sj = A.col_scale[s * D + j];
+  const uint4 *src = reinterpret_cast<const uint4 *>(A.codes + s * D * D + hh * 8192 + j * 64);
+  for (int q = 0; q < 4; ++q) {
+    const uint4 cq = src[q];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int slot = 16 * q + e;
+      const int row = 64 * hh + code_slot(slot);  // the slot map is its own inverse
+      const uint32_t wd = u4get(cq, e >> 2);
+      float x = (float)(int8_t)(wd >> (8 * (e & 3))) * A.row_scale[s * D + row] * sj;
+      if (DENSE) {
+        for (int c = 0; c < r; ++c) x = fmaf(A.comp_key[(s * r + c) * D + row], A.comp_val[(s * r + c) * D + j], x);
+      } else {
+        for (int c = 0; c < r; ++c)
+          if (A.comp_idx[s * r + c] == row) x += A.comp_val[(s * r + c) * D + j];
+      }
+      A.S_out[(s * D + row) * D + j] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <bool FUSED>
+hipError_t launch_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  const bool dense = a.comp_key != nullptr;
+  if (kda && dense)
+    hipLaunchKernelGGL((close_kernel<true, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (kda)
+    hipLaunchKernelGGL((close_kernel<true, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
+  else if (dense)
+    hipLaunchKernelGGL((close_kernel<false, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((close_kernel<false, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  return launch_close<false>(a, kda, stream);
+}
+
+hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  return launch_close<true>(a, kda, stream);
+}
+
+hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream) {
+  if (a.comp_key)
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t stream) {
+  if (a.comp_key)
+    hipLaunchKernelGGL(dequant_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, dim3(a.n), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace lq

@@ -1,5 +1,6 @@
 // Internal launch interface between the C ABI (lq_abi.cpp) and the gfx950
-// kernels (lq_kernels.hip).  Arguments are validated by the caller.
+// kernels (lq_decode.hip, lq_close.hip, lq_baselines.hip).  Arguments are
+// validated by the caller.
 #pragma once
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
