@@ -473,3 +473,44 @@ def test_bf16_per_window_error_below_per_step():
     err_w = np.mean((bw[-1] - S_exact) ** 2)
     err_s = np.mean((bs[-1] - S_exact) ** 2)
     assert err_w < err_s, (err_w, err_s)
+
+
+# ---------------------------------------------------------------------------
+# Helpers the GPU comparisons rely on
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dense", [False, True])
+def test_prerounding_codes_round_to_the_codes(dense):
+    """prerounding_codes gives the values quantize rounds: rounding them
+    (half to even, clamped) reproduces the codes exactly, for row and dense
+    compensators."""
+    rng = np.random.default_rng(4400 + dense)
+    S = _random_states(rng, 5, 128, 128)
+    b = O.quantize(S, 4, O.DENSE_COMP if dense else 0, 2)
+    x = O.prerounding_codes(S, b)
+    np.testing.assert_array_equal(np.clip(np.rint(x), -127, 127).astype(np.int8), b["codes"])
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_replay_of_window_records_is_the_window_state(kda):
+    """Applying a window's buffered records (d_i, k~_i, u_i) to its boundary
+    state gives the window's end state: the algebra every GPU test uses to
+    build the oracle's state from records."""
+    rng = np.random.default_rng(4500 + kda)
+    T, n = 7, 3
+    tok = _rand_tokens(rng, T, n, 128, 128, kda)
+    gate = O.GATE_KDA if kda else O.GATE_GDN
+    b = O.quantize(_random_states(rng, n, 128, 128), 4)
+    _, recs, S_end, _ = O.window(b, tok, 0, T, gate, 4)
+    np.testing.assert_allclose(O.replay(O.dequantize(b), recs), S_end, rtol=1e-12, atol=1e-12)
+
+
+def test_state_mse_is_bounded_by_the_half_step():
+    """state_mse of a fresh split against the state it splits is at most the
+    mean squared half step (a s / 2)^2 of the codes (up to fp32 rounding)."""
+    rng = np.random.default_rng(4600)
+    S = _random_states(rng, 4, 128, 128)
+    b = O.quantize(S, 4)
+    mse = O.state_mse(b, S.astype(np.float64))
+    half = 0.5 * b["row_scale"].astype(np.float64)[:, :, None] * b["col_scale"].astype(np.float64)[:, None, :]
+    assert np.all(mse <= (half ** 2).mean(axis=(1, 2)) * (1 + 1e-3))
+    assert np.all(mse > 0)
