@@ -210,7 +210,7 @@ def test_decode_step_slab_sizes(gate, n, dense):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
 @pytest.mark.parametrize("p,length", [(1, 1), (16, 16), (16, 1), (16, 7), (32, 32), (64, 64), (64, 37)])
-@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (8, 0), (4, lq.LQ_NO_SMOOTH)])
+@pytest.mark.parametrize("r,flags", [(0, 0), (4, 0), (8, 0), (16, 0), (4, lq.LQ_NO_SMOOTH)])
 def test_window_close_entry(gate, p, length, r, flags):
     rng = np.random.default_rng(7 * p + length + 100 * r + flags + (gate == "kda"))
     n = 21
@@ -626,3 +626,49 @@ def test_graph_replay_matches_eager(dense):
         for k in st.boundary_keys:
             np.testing.assert_array_equal(to_np(getattr(st, k)), ref[k], err_msg=f"replay {rep}: {k}")
         torch.zeros(1 << 20, device=DEV).sum()   # eager work between replays
+
+
+
+# ---------------------------------------------------------------------------
+# Degenerate tokens: full forgetting (alpha = 0), no decay (alpha = 1), no
+# write (beta = 0), zero keys, queries and values, mixed across states
+# ---------------------------------------------------------------------------
+def _degenerate_token(rng, n, gate, t):
+    tok = _token(rng, n, gate)
+    kind = (np.arange(n) + t) % 6
+    a = tok["alpha"]
+    if gate == "kda":
+        a[kind == 0] = 0.0                       # forget every channel
+        a[kind == 1] = 1.0                       # no decay
+        a[kind == 5, ::2] = 0.0                  # half the channels forget
+    else:
+        a[kind == 0] = 0.0
+        a[kind == 1] = 1.0
+    tok["beta"][kind == 2] = 0.0                 # no write
+    tok["k"][kind == 3] = 0.0                    # zero key
+    tok["q"][kind == 4] = 0.0                    # zero query
+    tok["v"][kind == 4] = 0.0                    # and zero value
+    return tok
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_degenerate_tokens(gate, fused):
+    """A whole window of degenerate tokens from the oracle's boundary: every
+    output, and the next boundary, match the oracle."""
+    rng = np.random.default_rng(7000 + 2 * (gate == "kda") + fused)
+    n, p, r = 24, 16, 4
+    S = _states_with_outliers(rng, n)
+    b = O.quantize(S, r)
+    toks = [_degenerate_token(rng, n, gate, t) for t in range(p)]
+    tok = {k: np.stack([x[k] for x in toks]) for k in toks[0]}
+    st = lq.LeapQuantState(n, p, r, gate, DEV)
+    upload_boundary(st, b)
+    tokd = {k: _dev(v) for k, v in tok.items()}
+    out = torch.empty((p, n, 128), device=DEV)
+    run_window(st, tokd, 0, p, out, fused=fused)
+    torch.cuda.synchronize()
+    t64 = {k: v.astype(np.float64) for k, v in tok.items()}
+    o_ref, _, S_end, b_next = O.window(b, t64, 0, p, _gate(gate), r)
+    P.assert_close(to_np(out), o_ref, "degenerate outputs")
+    P.compare_boundary(boundary_np(st), b_next, S_end.astype(np.float32), r, "degenerate boundary")
