@@ -401,6 +401,13 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
     }
   };
   load_chunk(lo, hi - lo);
+  // u rows of this wave's columns: issued with the first loads (one round
+  // trip to memory fewer per wave; the registers fit 4 waves per SIMD)
+  const int ulo = t > kRecChunk ? t - kRecChunk : 0;
+  float ur[kRecChunk];
+#pragma unroll
+  for (int j = 0; j < kRecChunk; ++j)
+    if (j < t - ulo) ur[j] = A.buf_u[(rec0 + ulo + j) * D + col];
   int cidx[kCompEarly];
   float cw[kCompEarly];
   float ck[DENSE ? kCompEarly : 1];  // dense keys at this lane's row
@@ -504,12 +511,6 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
       if (lane < 2 * r) reinterpret_cast<float *>(&sh_hcp[w][lane >> 1])[lane & 1] = acc;
     }
   }
-  // u rows of this wave's columns, in flight during the GEMV
-  const int ulo = t > kRecChunk ? t - kRecChunk : 0;
-  float ur[kRecChunk];
-#pragma unroll
-  for (int j = 0; j < kRecChunk; ++j)
-    if (j < t - ulo) ur[j] = A.buf_u[(rec0 + ulo + j) * D + col];
 
   // ---- GEMV weights of this half: power-of-two scale per wave and vector
   int eb, eq;
