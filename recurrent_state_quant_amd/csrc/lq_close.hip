@@ -434,16 +434,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
   // column-max partials of the split; KDA: in the per-row gate array, dead by then
   __shared__ __attribute__((aligned(16))) float sh_cmx[KDA ? 4 : 8 * D];
 
-  // boundary-state side data and this lane's code segments, issued first
-  if (tid < D) {
-    sh_a[tid] = A.row_scale[s * D + tid];
-    sh_s[tid] = A.col_scale[s * D + tid];
-  }
-  if (tid < D) sh_cslot[tid] = -1;
+  // this lane's code segments and the boundary state's scales, issued
+  // first; the scales reach LDS with the first record chunk, so that no
+  // wait separates these loads from the records'
   const int8_t *csrc = A.codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;
   uint4 cw[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
+  float a_row = 0.f, s_col = 0.f;
+  if (tid < D) {
+    a_row = A.row_scale[s * D + tid];
+    s_col = A.col_scale[s * D + tid];
+    sh_cslot[tid] = -1;
+  }
 
   floatx4 acc[4][4];
   // acc (+)= Gamma ((c (a Gamma)) s + compensator rows); Gamma from sh_gam
@@ -510,13 +513,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
       const int ncv = (first && !DENSE) ? r * (D / 4) : 0;
       float4 c0 = z4;
       if (e0 < ncv) c0 = ld4(A.comp_val + s * r * D + 4 * e0);
-      float tk = 0.f, tq = 0.f, tv = 0.f, tb = 0.f;
+      float tk = 0.f, tq = 0.f, tv = 0.f, tx = 0.f, ta = 1.f;
       if (FUSED && first && tid < D) {
         tk = A.k[s * D + tid];
         tq = A.q[s * D + tid];
         tv = A.v[s * D + tid];
-        tb = A.beta[s];
-        P = KDA ? A.alpha[s * D + tid] : A.alpha[s];
+        // beta_t in even lanes and GDN's alpha_t in odd lanes: a lane-indexed
+        // vector load, broadcast once the record loads are issued (as scalar
+        // loads they would be waited for before those issue); KDA reads
+        // alpha_t per row
+        tx = *((lane & 1) ? A.alpha + (KDA ? s * D + tid : s) : A.beta + s);
+        if (KDA) ta = A.alpha[s * D + tid];
       }
       float4 u0 = z4, u1 = z4, k0 = z4, k1 = z4, g0 = z4, g1 = z4;
       if (e0 < nvec) {
@@ -545,7 +552,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
       float4 *dc = reinterpret_cast<float4 *>(sh_comp);
       if (e0 < ncv) dc[e0] = c0;
       if (e1 < ncv) dc[e1] = ld4(A.comp_val + s * r * D + 4 * e1);
+      if (first && tid < D) {
+        sh_a[tid] = a_row;
+        sh_s[tid] = s_col;
+      }
       if (FUSED && first && tid < D) {
+        const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 0));
+        P = KDA ? ta : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 1));
         sh_tk[tid] = (A.flags & 2u) ? 0.f : tk;  // b_t = 0 without the delta correction
         sh_tq[tid] = tq;
         sh_tkt[tid] = tb * tk;

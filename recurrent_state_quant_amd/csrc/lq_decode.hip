@@ -92,27 +92,32 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   int hi = t;
   int lo = hi > kRecChunk ? hi - kRecChunk : 0;
   float2 kr[kRecChunk], gr[kRecChunk];
-  float gs[kRecChunk];
+  // Per-state scalars (GDN gates, compensator row indices) are read with
+  // lane-indexed vector loads and broadcast with readlane where used.  As
+  // scalar loads they were waited for before the codes were issued (scalar
+  // loads return out of order, so any later scalar wait covers them), which
+  // put a second memory round trip in front of every wave.
+  float gv = 1.f;  // GDN: lane j holds the gate of record lo + j
   auto load_chunk = [&](int lo_, int cnt_) {
+    if (!KDA && lane < cnt_) gv = A.buf_gate[rec0 + lo_ + lane];
 #pragma unroll
     for (int j = 0; j < kRecChunk; ++j) {
       if (j < cnt_) {
         const size_t rr = (rec0 + lo_ + j) * D + 2 * lane;
         kr[j] = ld2(A.buf_k + rr);
         if (KDA) gr[j] = ld2(A.buf_gate + rr);
-        else gs[j] = A.buf_gate[rec0 + lo_ + j];
       }
     }
   };
   load_chunk(lo, hi - lo);
-  int cidx[kCompEarly];
+  int civ = -1;  // lane c < r: compensator row index c
+  if (!DENSE && lane < r) civ = A.comp_idx[(size_t)s * r + lane];
   float2 cw[kCompEarly];
   float2 ck[DENSE ? kCompEarly : 1];  // dense keys, rows 2l and 2l+1
 #pragma unroll
   for (int c = 0; c < kCompEarly; ++c) {
     if (c < r) {
       if constexpr (DENSE) ck[c] = ld2(A.comp_key + ((size_t)s * r + c) * D + 2 * lane);
-      else cidx[c] = A.comp_idx[(size_t)s * r + c];
       cw[c] = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
     }
   }
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         } else {
           hb = (kr[j].x * yb.x + kr[j].y * yb.y) * Pg;
           hq = (kr[j].x * yq.x + kr[j].y * yq.y) * Pg;
-          Pg *= gs[j];
+          Pg *= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j));
         }
         sh_red[lane * kRedStride + 2 * j] = hb;
         sh_red[lane * kRedStride + 2 * j + 1] = hq;
@@ -312,14 +317,15 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   } else {
 #pragma unroll
     for (int c = 0; c < kCompEarly; ++c) {
-      if (c < r && (unsigned)cidx[c] < (unsigned)D) {
-        const float2 gg = sh_gy[cidx[c]];
+      const int idx = __builtin_amdgcn_readlane(civ, c);
+      if (c < r && (unsigned)idx < (unsigned)D) {
+        const float2 gg = sh_gy[idx];
         zb.x = fmaf(cw[c].x, gg.x, zb.x); zb.y = fmaf(cw[c].y, gg.x, zb.y);
         zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
       }
     }
     for (int c = kCompEarly; c < r; ++c) {
-      const int idx = A.comp_idx[(size_t)s * r + c];
+      const int idx = __builtin_amdgcn_readlane(civ, c);
       if ((unsigned)idx < (unsigned)D) {
         const float2 gg = sh_gy[idx];
         const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
@@ -391,12 +397,16 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   int hi = t;
   int lo = hi > kRecChunk ? hi - kRecChunk : 0;
   float kr[kRecChunk], gr[kRecChunk];
+  // GDN gates and compensator row indices: lane-indexed vector loads,
+  // broadcast with readlane (no scalar-load wait before the codes issue)
+  float gv = 1.f;  // GDN: lane j holds the gate of record lo + j
   auto load_chunk = [&](int lo_, int cnt_) {
+    if (!KDA && lane < cnt_) gv = A.buf_gate[rec0 + lo_ + lane];
 #pragma unroll
     for (int j = 0; j < kRecChunk; ++j) {
       if (j < cnt_) {
         kr[j] = A.buf_k[(rec0 + lo_ + j) * D + row];
-        gr[j] = KDA ? A.buf_gate[(rec0 + lo_ + j) * D + row] : A.buf_gate[rec0 + lo_ + j];
+        if (KDA) gr[j] = A.buf_gate[(rec0 + lo_ + j) * D + row];
       }
     }
   };
@@ -408,14 +418,14 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
 #pragma unroll
   for (int j = 0; j < kRecChunk; ++j)
     if (j < t - ulo) ur[j] = A.buf_u[(rec0 + ulo + j) * D + col];
-  int cidx[kCompEarly];
+  int civ = -1;  // lane c < r: compensator row index c
+  if (!DENSE && lane < r) civ = A.comp_idx[(size_t)s * r + lane];
   float cw[kCompEarly];
   float ck[DENSE ? kCompEarly : 1];  // dense keys at this lane's row
 #pragma unroll
   for (int c = 0; c < kCompEarly; ++c) {
     if (c < r) {
       if constexpr (DENSE) ck[c] = A.comp_key[((size_t)s * r + c) * D + row];
-      else cidx[c] = A.comp_idx[(size_t)s * r + c];
       cw[c] = A.comp_val[((size_t)s * r + c) * D + col];
     }
   }
@@ -457,7 +467,7 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
           red[(lane >> 1) * kRedStride + 2 * j] = hb;
           red[(lane >> 1) * kRedStride + 2 * j + 1] = hq;
         }
-        P *= gr[j];
+        P *= KDA ? gr[j] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -577,14 +587,15 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   } else {
 #pragma unroll
     for (int c = 0; c < kCompEarly; ++c) {
-      if (c < r && (unsigned)cidx[c] < (unsigned)D) {
-        const float2 gg = sh_gy[cidx[c]];
+      const int idx = __builtin_amdgcn_readlane(civ, c);
+      if (c < r && (unsigned)idx < (unsigned)D) {
+        const float2 gg = sh_gy[idx];
         zb = fmaf(cw[c], gg.x, zb);
         zq = fmaf(cw[c], gg.y, zq);
       }
     }
     for (int c = kCompEarly; c < r; ++c) {
-      const int idx = A.comp_idx[(size_t)s * r + c];
+      const int idx = __builtin_amdgcn_readlane(civ, c);
       if ((unsigned)idx < (unsigned)D) {
         const float2 gg = sh_gy[idx];
         const float wv = A.comp_val[((size_t)s * r + c) * D + col];
