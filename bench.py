@@ -136,7 +136,7 @@ def parse():
     ap.add_argument("--ablations", action="store_true",
                     help="instead of the headline line, print one line with the kernel-throughput "
                          "analogues of the pages' Table 2 (per-step fp32 / bf16 / int8 baselines, "
-                         "per-window, compensators) and Table 3 (window length p) on this workload")
+                         "per-window, compensators) and Table 3 (window length p, compensator count r) on this workload")
     ap.add_argument("--ablation-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-states", type=int, default=64)
@@ -465,6 +465,7 @@ def ablations(args, cfg, dev, reps=3):
              ("+ Per-window (p = 16)", lambda: windowed(16, 0, 1)),
              ("+ Comp. Tokens (r = 4) and smoothing", lambda: windowed(16, cfg.r, 0))]
     rows3 = [(f"p = {p}", (lambda p=p: windowed(p, cfg.r, 0))) for p in (4, 8, 16, 32)]
+    rows3r = [(f"r = {r}", (lambda r=r: windowed(cfg.p, r, 0))) for r in (0, 2, 4, 8, 16)]
 
     def table(rows, ref):
         out = []
@@ -486,13 +487,15 @@ def ablations(args, cfg, dev, reps=3):
          for i in (0, 1, 2)]
     t2, ref = table(rows2, None)
     t3, _ = table(rows3, ref)
+    t3r, _ = table(rows3r, ref)
     tcb, _ = table(rows_cb, ref)
     tdc, _ = table(rows_dc, ref)
     lat = latency(dev)
     return {"metric": "kernel throughput ablations (head-tokens/s; speedup over fp32 per-step)",
             "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph",
             "schedule": "one launch per layer and token; last token of each window fused with its close",
-            "table2": t2, "table3_r": cfg.r, "table3": t3, "continuous_batching": tcb,
+            "table2": t2, "table3_r": cfg.r, "table3": t3, "table3_p": cfg.p, "table3_r_sweep": t3r,
+            "continuous_batching": tcb,
             "compensator_forms": tdc,
             "latency_single_state": lat}
 
