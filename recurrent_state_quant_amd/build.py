@@ -24,6 +24,33 @@ def hipcc_command(out=LIB_PATH, extra=()):
             *extra, "-o", out, *SOURCES]
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi", "lq_c_driver.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c_abi", "lq_c_driver")
+
+
+def c_driver_command(out=C_DRIVER):
+    """gcc line of the plain-C client of the ABI (tests/c_abi): C11, the
+    public header only, linked against the in-tree library."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+            "-o", out, C_DRIVER_SRC, "-L", PKG_DIR, "-lleapquant", "-L", os.path.join(rocm, "lib"),
+            "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../recurrent_state_quant_amd",
+            "-Wl,-rpath," + os.path.join(rocm, "lib")]
+
+
+def build_c_driver(verbose=False):
+    """Compile tests/c_abi/lq_c_driver against the built library."""
+    cmd = c_driver_command()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise subprocess.CalledProcessError(res.returncode, cmd, res.stdout, res.stderr)
+    return C_DRIVER
+
+
 def build(verbose=False):
     """Compile the HIP library; raises CalledProcessError on failure."""
     tmp = LIB_PATH + ".tmp"
@@ -40,3 +67,4 @@ def build(verbose=False):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_driver(verbose=True))
