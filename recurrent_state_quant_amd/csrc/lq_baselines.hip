@@ -146,6 +146,16 @@ __global__ __launch_bounds__(256) void bf16w_decode_kernel(const Bf16WinArgs A) 
   uint4 bw[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) bw[m] = ldu4(Bs + (rg + 16 * m) * D + 8 * cg);
+  // u rows of the newest kRecChunk records at this thread's column (threads
+  // tid < D), issued with the state loads: they are consumed after the
+  // GEMV, one round trip later than these
+  const int ulo = t > kRecChunk ? t - kRecChunk : 0;
+  float ur[kRecChunk];
+  if (tid < D) {
+#pragma unroll
+    for (int j = 0; j < kRecChunk; ++j)
+      if (j < t - ulo) ur[j] = A.buf_u[(rec0 + ulo + j) * D + tid];
+  }
   if (tid < D) {
     const int row = tid;
     const float kk = A.k[so + row], qq = A.q[so + row];
@@ -164,11 +174,15 @@ __global__ __launch_bounds__(256) void bf16w_decode_kernel(const Bf16WinArgs A) 
     while (hi > 0) {
       const int lo = hi > kRecChunk ? hi - kRecChunk : 0, cnt = hi - lo;
       float kr[kRecChunk], gr[kRecChunk];
+      // GDN: lane j holds the gate of record lo + j (a vector load, so no
+      // scalar-load wait lands between the record loads)
+      float gv = 1.f;
+      if (!KDA && lane < cnt) gv = A.buf_gate[rec0 + lo + lane];
 #pragma unroll
       for (int j = 0; j < kRecChunk; ++j) {
         if (j < cnt) {
           kr[j] = A.buf_k[(rec0 + lo + j) * D + row];
-          gr[j] = KDA ? A.buf_gate[(rec0 + lo + j) * D + row] : A.buf_gate[rec0 + lo + j];
+          if (KDA) gr[j] = A.buf_gate[(rec0 + lo + j) * D + row];
         }
       }
 #pragma unroll
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(256) void bf16w_decode_kernel(const Bf16WinArgs A) 
           const float kw = kr[j] * P;
           const float hb = wave_sum(kw * yb), hq = wave_sum(kw * yq);
           if (lane == 0) sh_hp[w][lo + j] = make_float2(hb, hq);
-          P *= gr[j];
+          P *= KDA ? gr[j] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j));
         }
       }
       hi = lo;
@@ -223,11 +237,19 @@ __global__ __launch_bounds__(256) void bf16w_decode_kernel(const Bf16WinArgs A) 
       zb += sh_zp[ww][col].x;
       zq += sh_zp[ww][col].y;
     }
-    for (int i = 0; i < t; ++i) {
+    for (int i = 0; i < ulo; ++i) {  // records older than the newest chunk (p > kRecChunk)
       const float u = A.buf_u[(rec0 + i) * D + col];
       const float2 h0 = sh_hp[0][i], h1 = sh_hp[1][i];
       zb = fmaf(u, h0.x + h1.x, zb);
       zq = fmaf(u, h0.y + h1.y, zq);
+    }
+#pragma unroll
+    for (int j = 0; j < kRecChunk; ++j) {
+      if (j < t - ulo) {
+        const float2 h0 = sh_hp[0][ulo + j], h1 = sh_hp[1][ulo + j];
+        zb = fmaf(ur[j], h0.x + h1.x, zb);
+        zq = fmaf(ur[j], h0.y + h1.y, zq);
+      }
     }
     const float ut = A.v[so + col] - zb;
     __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], ut, zq), A.o + so + col);
@@ -264,12 +286,41 @@ __global__ __launch_bounds__(256) void bf16w_close_kernel(const Bf16WinArgs A) {
   for (int hi = len; hi > 0;) {
     const int lo = hi > kRecChunk ? hi - kRecChunk : 0, cnt = hi - lo;
     __syncthreads();  // the previous chunk's contraction is done
-    for (int e = tid; e < cnt * (D / 4); e += 256) {
-      reinterpret_cast<float4 *>(sh_K)[e] = ld4(A.buf_k + (rec0 + lo) * D + 4 * e);
-      reinterpret_cast<float4 *>(sh_U)[e] = ld4(A.buf_u + (rec0 + lo) * D + 4 * e);
-      if (KDA) reinterpret_cast<float4 *>(sh_g)[e] = ld4(A.buf_gate + (rec0 + lo) * D + 4 * e);
+    {
+      // kRecChunk * D / 4 = 512 float4 per array: two per thread, every
+      // load issued before the first LDS write
+      static_assert(kRecChunk * D / 4 == 512, "staging assumes two float4 per thread");
+      const int nvec = cnt * (D / 4), e0 = tid, e1 = tid + 256;
+      const float *sk = A.buf_k + (rec0 + lo) * D, *su = A.buf_u + (rec0 + lo) * D;
+      const float *sg = A.buf_gate + (rec0 + lo) * D;
+      const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 k0 = z4, k1 = z4, u0 = z4, u1 = z4, g0 = z4, g1 = z4;
+      if (e0 < nvec) {
+        k0 = ld4(sk + 4 * e0);
+        u0 = ld4(su + 4 * e0);
+        if (KDA) g0 = ld4(sg + 4 * e0);
+      }
+      if (e1 < nvec) {
+        k1 = ld4(sk + 4 * e1);
+        u1 = ld4(su + 4 * e1);
+        if (KDA) g1 = ld4(sg + 4 * e1);
+      }
+      float gs = 1.f;
+      if (!KDA && tid < cnt) gs = A.buf_gate[rec0 + lo + tid];
+      float4 *dk = reinterpret_cast<float4 *>(sh_K), *du = reinterpret_cast<float4 *>(sh_U);
+      float4 *dg = reinterpret_cast<float4 *>(sh_g);
+      if (e0 < nvec) {
+        dk[e0] = k0;
+        du[e0] = u0;
+        if (KDA) dg[e0] = g0;
+      }
+      if (e1 < nvec) {
+        dk[e1] = k1;
+        du[e1] = u1;
+        if (KDA) dg[e1] = g1;
+      }
+      if (!KDA && tid < cnt) sh_g[tid] = gs;
     }
-    if (!KDA && tid < cnt) sh_g[tid] = A.buf_gate[rec0 + lo + tid];
     __syncthreads();
     if (tid < D) {
       for (int j = cnt - 1; j >= 0; --j) {
