@@ -34,6 +34,7 @@ namespace lq {
 // they drain, which measurably lowers the streaming rate.
 // ---------------------------------------------------------------------------
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
+constexpr int kCompBatch = 4;    // later compensator rows: loads issued together, then used
 constexpr int kRedStride = 33;   // odd row stride of the transposed partials: no bank conflicts
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -205,10 +206,19 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         red[2 * c + 1] = ck[c].x * gq.x + ck[c].y * gq.y;
       }
     }
-    for (int c = kCompEarly; c < r; ++c) {
-      const float2 kc = ld2(A.comp_key + ((size_t)s * r + c) * D + 2 * lane);
-      red[2 * c] = kc.x * gb.x + kc.y * gb.y;
-      red[2 * c + 1] = kc.x * gq.x + kc.y * gq.y;
+    // the later keys, four loads in flight before their use
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {
+      float2 kc[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j)
+        if (c0 + j < r) kc[j] = ld2(A.comp_key + ((size_t)s * r + c0 + j) * D + 2 * lane);
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        if (c0 + j < r) {
+          red[2 * (c0 + j)] = kc[j].x * gb.x + kc[j].y * gb.y;
+          red[2 * (c0 + j) + 1] = kc[j].x * gq.x + kc[j].y * gq.y;
+        }
+      }
     }
     __syncthreads();
     {
@@ -308,11 +318,19 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
       }
     }
-    for (int c = kCompEarly; c < r; ++c) {
-      const float2 gg = sh_hc[c];
-      const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
-      zb.x = fmaf(w.x, gg.x, zb.x); zb.y = fmaf(w.y, gg.x, zb.y);
-      zq.x = fmaf(w.x, gg.y, zq.x); zq.y = fmaf(w.y, gg.y, zq.y);
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {
+      float2 wv[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j)
+        if (c0 + j < r) wv[j] = ld2(A.comp_val + ((size_t)s * r + c0 + j) * D + 2 * lane);
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        if (c0 + j < r) {
+          const float2 gg = sh_hc[c0 + j];
+          zb.x = fmaf(wv[j].x, gg.x, zb.x); zb.y = fmaf(wv[j].y, gg.x, zb.y);
+          zq.x = fmaf(wv[j].x, gg.y, zq.x); zq.y = fmaf(wv[j].y, gg.y, zq.y);
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -324,13 +342,22 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         zq.x = fmaf(cw[c].x, gg.y, zq.x); zq.y = fmaf(cw[c].y, gg.y, zq.y);
       }
     }
-    for (int c = kCompEarly; c < r; ++c) {
-      const int idx = __builtin_amdgcn_readlane(civ, c);
-      if ((unsigned)idx < (unsigned)D) {
-        const float2 gg = sh_gy[idx];
-        const float2 w = ld2(A.comp_val + ((size_t)s * r + c) * D + 2 * lane);
-        zb.x = fmaf(w.x, gg.x, zb.x); zb.y = fmaf(w.y, gg.x, zb.y);
-        zq.x = fmaf(w.x, gg.y, zq.x); zq.y = fmaf(w.y, gg.y, zq.y);
+    // the later rows, four loads in flight before their use
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {
+      int idx[kCompBatch];
+      float2 wv[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        idx[j] = c0 + j < r ? __builtin_amdgcn_readlane(civ, c0 + j) : -1;
+        if ((unsigned)idx[j] < (unsigned)D) wv[j] = ld2(A.comp_val + ((size_t)s * r + c0 + j) * D + 2 * lane);
+      }
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        if ((unsigned)idx[j] < (unsigned)D) {
+          const float2 gg = sh_gy[idx[j]];
+          zb.x = fmaf(wv[j].x, gg.x, zb.x); zb.y = fmaf(wv[j].y, gg.x, zb.y);
+          zq.x = fmaf(wv[j].x, gg.y, zq.x); zq.y = fmaf(wv[j].y, gg.y, zq.y);
+        }
       }
     }
   }
@@ -506,7 +533,15 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
 #pragma unroll
     for (int c = 0; c < kCompEarly; ++c)
       if (c < r) put(c, ck[c]);
-    for (int c = kCompEarly; c < r; ++c) put(c, A.comp_key[((size_t)s * r + c) * D + row]);
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {  // four loads in flight
+      float kc[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j)
+        if (c0 + j < r) kc[j] = A.comp_key[((size_t)s * r + c0 + j) * D + row];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j)
+        if (c0 + j < r) put(c0 + j, kc[j]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -578,11 +613,19 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
         zq = fmaf(cw[c], h0.y + h1.y, zq);
       }
     }
-    for (int c = kCompEarly; c < r; ++c) {
-      const float2 h0 = sh_hcp[0][c], h1 = sh_hcp[1][c];
-      const float wv = A.comp_val[((size_t)s * r + c) * D + col];
-      zb = fmaf(wv, h0.x + h1.x, zb);
-      zq = fmaf(wv, h0.y + h1.y, zq);
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {
+      float wv[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j)
+        if (c0 + j < r) wv[j] = A.comp_val[((size_t)s * r + c0 + j) * D + col];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        if (c0 + j < r) {
+          const float2 h0 = sh_hcp[0][c0 + j], h1 = sh_hcp[1][c0 + j];
+          zb = fmaf(wv[j], h0.x + h1.x, zb);
+          zq = fmaf(wv[j], h0.y + h1.y, zq);
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -594,13 +637,21 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
         zq = fmaf(cw[c], gg.y, zq);
       }
     }
-    for (int c = kCompEarly; c < r; ++c) {
-      const int idx = __builtin_amdgcn_readlane(civ, c);
-      if ((unsigned)idx < (unsigned)D) {
-        const float2 gg = sh_gy[idx];
-        const float wv = A.comp_val[((size_t)s * r + c) * D + col];
-        zb = fmaf(wv, gg.x, zb);
-        zq = fmaf(wv, gg.y, zq);
+    for (int c0 = kCompEarly; c0 < r; c0 += kCompBatch) {  // four loads in flight
+      int idx[kCompBatch];
+      float wv[kCompBatch];
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        idx[j] = c0 + j < r ? __builtin_amdgcn_readlane(civ, c0 + j) : -1;
+        if ((unsigned)idx[j] < (unsigned)D) wv[j] = A.comp_val[((size_t)s * r + c0 + j) * D + col];
+      }
+#pragma unroll
+      for (int j = 0; j < kCompBatch; ++j) {
+        if ((unsigned)idx[j] < (unsigned)D) {
+          const float2 gg = sh_gy[idx[j]];
+          zb = fmaf(wv[j], gg.x, zb);
+          zq = fmaf(wv[j], gg.y, zq);
+        }
       }
     }
   }
