@@ -237,11 +237,21 @@ __global__ __launch_bounds__(256) void bf16w_decode_kernel(const Bf16WinArgs A) 
       zb += sh_zp[ww][col].x;
       zq += sh_zp[ww][col].y;
     }
-    for (int i = 0; i < ulo; ++i) {  // records older than the newest chunk (p > kRecChunk)
-      const float u = A.buf_u[(rec0 + i) * D + col];
-      const float2 h0 = sh_hp[0][i], h1 = sh_hp[1][i];
-      zb = fmaf(u, h0.x + h1.x, zb);
-      zq = fmaf(u, h0.y + h1.y, zq);
+    // records older than the newest chunk (p > kRecChunk), eight loads in
+    // flight before their use
+    for (int i0 = 0; i0 < ulo; i0 += 8) {
+      float uo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (i0 + j < ulo) uo[j] = A.buf_u[(rec0 + i0 + j) * D + col];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (i0 + j < ulo) {
+          const float2 h0 = sh_hp[0][i0 + j], h1 = sh_hp[1][i0 + j];
+          zb = fmaf(uo[j], h0.x + h1.x, zb);
+          zq = fmaf(uo[j], h0.y + h1.y, zq);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < kRecChunk; ++j) {

@@ -35,6 +35,7 @@ namespace lq {
 // ---------------------------------------------------------------------------
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
 constexpr int kCompBatch = 4;    // later compensator rows: loads issued together, then used
+constexpr int kOldBatch = 8;     // u rows older than the newest record chunk, per batch
 constexpr int kRedStride = 33;   // odd row stride of the transposed partials: no bank conflicts
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -371,11 +372,20 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
         zuq.x = fmaf(ur[j].x, h.y, zuq.x); zuq.y = fmaf(ur[j].y, h.y, zuq.y);
       }
     }
-    for (int i = 0; i < ulo; ++i) {
-      const float2 u = ld2(A.buf_u + (rec0 + i) * D + 2 * lane);
-      const float2 h = sh_h[i];
-      zub.x = fmaf(u.x, h.x, zub.x); zub.y = fmaf(u.y, h.x, zub.y);
-      zuq.x = fmaf(u.x, h.y, zuq.x); zuq.y = fmaf(u.y, h.y, zuq.y);
+    // older records (p > kRecChunk): kOldBatch loads in flight before use
+    for (int i0 = 0; i0 < ulo; i0 += kOldBatch) {
+      float2 uo[kOldBatch];
+#pragma unroll
+      for (int j = 0; j < kOldBatch; ++j)
+        if (i0 + j < ulo) uo[j] = ld2(A.buf_u + (rec0 + i0 + j) * D + 2 * lane);
+#pragma unroll
+      for (int j = 0; j < kOldBatch; ++j) {
+        if (i0 + j < ulo) {
+          const float2 h = sh_h[i0 + j];
+          zub.x = fmaf(uo[j].x, h.x, zub.x); zub.y = fmaf(uo[j].y, h.x, zub.y);
+          zuq.x = fmaf(uo[j].x, h.y, zuq.x); zuq.y = fmaf(uo[j].y, h.y, zuq.y);
+        }
+      }
     }
     zb.x += zub.x; zb.y += zub.y;
     zq.x += zuq.x; zq.y += zuq.y;
@@ -665,11 +675,20 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
         zuq = fmaf(ur[j], h0.y + h1.y, zuq);
       }
     }
-    for (int i = 0; i < ulo; ++i) {
-      const float u = A.buf_u[(rec0 + i) * D + col];
-      const float2 h0 = sh_hp[0][i], h1 = sh_hp[1][i];
-      zub = fmaf(u, h0.x + h1.x, zub);
-      zuq = fmaf(u, h0.y + h1.y, zuq);
+    // older records (p > kRecChunk): kOldBatch loads in flight before use
+    for (int i0 = 0; i0 < ulo; i0 += kOldBatch) {
+      float uo[kOldBatch];
+#pragma unroll
+      for (int j = 0; j < kOldBatch; ++j)
+        if (i0 + j < ulo) uo[j] = A.buf_u[(rec0 + i0 + j) * D + col];
+#pragma unroll
+      for (int j = 0; j < kOldBatch; ++j) {
+        if (i0 + j < ulo) {
+          const float2 h0 = sh_hp[0][i0 + j], h1 = sh_hp[1][i0 + j];
+          zub = fmaf(uo[j], h0.x + h1.x, zub);
+          zuq = fmaf(uo[j], h0.y + h1.y, zuq);
+        }
+      }
     }
     zb += zub;
     zq += zuq;
