@@ -191,7 +191,14 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     __syncthreads();
     hi = lo;
     lo = hi > kRecChunk ? hi - kRecChunk : 0;
-    if (hi > 0) load_chunk(lo, hi - lo);
+    if (hi > 0) {
+      // Every load of the chunk just used has returned.  Saying so lets the
+      // next chunk's loads issue back to back: the compiler cannot pair the
+      // guarded loads (j < cnt) with their guarded uses, and would otherwise
+      // wait for each earlier load into the same registers first.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      load_chunk(lo, hi - lo);
+    }
   }
   // ---- dense compensator tokens: records written before the window's
   // first token (decay Gamma), weights h_c = k_c . (Gamma * y)
@@ -234,9 +241,13 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
     }
     __syncthreads();
   }
-  // U of the newest chunk, in flight during the GEMV
+  // U of the newest chunk, in flight during the GEMV.  The explicit wait
+  // (the codes are due for the GEMV next) lets these loads issue back to
+  // back: the compiler would otherwise wait before each of them, for the
+  // guarded loads that last used the same registers.
   const int ulo = t > kRecChunk ? t - kRecChunk : 0;
   float2 ur[kRecChunk];
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
   for (int j = 0; j < kRecChunk; ++j)
     if (j < t - ulo) ur[j] = ld2(A.buf_u + (rec0 + ulo + j) * D + 2 * lane);
@@ -525,7 +536,14 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     hi = lo;
     lo = hi > kRecChunk ? hi - kRecChunk : 0;
-    if (hi > 0) load_chunk(lo, hi - lo);
+    if (hi > 0) {
+      // Every load of the chunk just used has returned.  Saying so lets the
+      // next chunk's loads issue back to back: the compiler cannot pair the
+      // guarded loads (j < cnt) with their guarded uses, and would otherwise
+      // wait for each earlier load into the same registers first.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      load_chunk(lo, hi - lo);
+    }
   }
   // ---- dense compensator tokens: records written before the window's
   // first token (decay Gamma); this wave's partial k_c . (Gamma * y)

@@ -120,6 +120,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 constexpr int kRecChunk = 16;    // records in flight per chunk
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left free (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // slot of row i & 63 inside its column segment (see the state layout)
 __device__ __forceinline__ int code_slot(int x) {
