@@ -434,7 +434,7 @@ def ablations(args, cfg, dev, reps=3):
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True,
                                            dense=bool(flags & lq.LQ_DENSE_COMP) and r > 0)
 
-    def slots(p, r):
+    def slots(p, r, compact=False):
         # continuous batching: every slot has its own window phase (seeded,
         # uniform), so about 1/p of the slots close at every token; the
         # positions live on the device.  (Phases strided by a multiple of 8
@@ -448,12 +448,17 @@ def ablations(args, cfg, dev, reps=3):
         pos = [(phase + t) % p for t in range(T)]
         step_pos = [torch.where(x == p - 1, -1, x).to(torch.int32) for x in pos]
         close_pos = [torch.where(x == p - 1, x, -1).to(torch.int32) for x in pos]
+        # compact: the ids of the slots that close at token t, one workgroup each
+        close_list = [torch.nonzero(x == p - 1).flatten().to(torch.int32) for x in pos]
 
         def run():
             for t in range(T):
                 for l in range(L):
                     lq.leapquant_decode_step_slots(views[l], step_pos[t], *targs(t, l))
-                    lq.leapquant_decode_close_slots(views[l], close_pos[t], *targs(t, l))
+                    if compact:
+                        lq.leapquant_decode_close_list(views[l], pos[t], close_list[t], *targs(t, l))
+                    else:
+                        lq.leapquant_decode_close_slots(views[l], close_pos[t], *targs(t, l))
         value = timed(run)
         del slab, views
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
@@ -480,7 +485,9 @@ def ablations(args, cfg, dev, reps=3):
         return out, ref
 
     rows_cb = [("lockstep windows (all slots at the same position)", lambda: windowed(cfg.p, cfg.r, 0)),
-               ("continuous batching (slot phases spread over the window)", lambda: slots(cfg.p, cfg.r))]
+               ("continuous batching (slot phases spread over the window)", lambda: slots(cfg.p, cfg.r)),
+               ("continuous batching, closes launched for the closing slots only (slot list)",
+                lambda: slots(cfg.p, cfg.r, compact=True))]
     DC = lq.LQ_DENSE_COMP
     rows_dc = [("row compensators", lambda: windowed(cfg.p, cfg.r, 0))] + \
         [(f"dense tokens, {i} subspace iteration{'s' if i != 1 else ''}", (lambda i=i: windowed(cfg.p, cfg.r, DC, i)))

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define LEAPQUANT_ABI_VERSION 3
+#define LEAPQUANT_ABI_VERSION 4
 
 typedef enum lq_status {
   LQ_OK = 0,
@@ -234,6 +234,26 @@ int leapquant_decode_close_slots(const lq_params *prm, const lq_state *st, const
                                  hipStream_t stream);
 int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const int32_t *len,
                                  hipStream_t stream);
+
+/* Compacted closes.  At a given token only the slots whose windows end
+ * close, about one slot in p; the _slots calls above still start one
+ * workgroup per slot, and the idle ones cost launch time.  These calls take
+ * list[count], int32 slot ids in DEVICE memory (4-byte aligned, read-only,
+ * overlapping no state array, output or the per-slot array), and start
+ * one workgroup per entry: listed slot s is processed exactly as the
+ * matching _slots call processes it with pos[s] / len[s] (a listed slot
+ * whose pos or len is out of range is idle); ids outside [0, n) are
+ * skipped; unlisted slots are not touched.  0 <= count <= n (LQ_ERR_SHAPE
+ * otherwise); count == 0 launches nothing and returns LQ_OK.  A slot listed
+ * twice is closed twice concurrently, which races: the caller lists each
+ * slot at most once (device values cannot be checked on the host).  The
+ * other arguments and error codes are those of the _slots calls. */
+int leapquant_decode_close_list(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                const int32_t *list, int32_t count, const float *q,
+                                const float *k, const float *v, const float *beta,
+                                const float *alpha, float *o, hipStream_t stream);
+int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const int32_t *len,
+                                const int32_t *list, int32_t count, hipStream_t stream);
 
 /* ---- Uncompressed baselines ([EL] Table 2, rows "FP32 per-step" and
  * "BF16 per-step"): the same token update on a dense state that is read

@@ -12,7 +12,7 @@ from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matr
                   leapquant_abi_version, leapquant_bf16w_decode_step, leapquant_bf16w_window_close,
                   leapquant_decode_close, leapquant_decode_step,
                   leapquant_decode_close_slots, leapquant_decode_step_slots, leapquant_dense_step,
-                  leapquant_window_close_slots,
+                  leapquant_window_close_slots, leapquant_decode_close_list, leapquant_window_close_list,
                   leapquant_dequantize_state, leapquant_quantize_state,
                   leapquant_status_string, leapquant_window_close)
 
@@ -23,7 +23,7 @@ __all__ = [
     "leapquant_abi_version", "leapquant_bf16w_decode_step", "leapquant_bf16w_window_close",
     "leapquant_decode_close", "leapquant_decode_step",
     "leapquant_decode_close_slots", "leapquant_decode_step_slots", "leapquant_dense_step",
-    "leapquant_window_close_slots",
+    "leapquant_window_close_slots", "leapquant_decode_close_list", "leapquant_window_close_list",
     "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",
     "leapquant_window_close",
 ]

@@ -8,7 +8,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libleapquant.so")
 
-ABI_VERSION = 3  # the lq_params / lq_state layout these structures mirror
+ABI_VERSION = 4  # the lq_params / lq_state layout and entry points this binding mirrors
 
 LQ_OK = 0
 LQ_ERR_NULL = -1
@@ -35,6 +35,8 @@ EXPORTED = (
     "leapquant_decode_step_slots",
     "leapquant_decode_close_slots",
     "leapquant_window_close_slots",
+    "leapquant_decode_close_list",
+    "leapquant_window_close_list",
     "leapquant_dequantize_state",
     "leapquant_bf16w_decode_step",
     "leapquant_bf16w_window_close",
@@ -84,12 +86,15 @@ def load():
     lib.leapquant_decode_step_slots.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_decode_close_slots.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_window_close_slots.argtypes = [P, S, vp, vp]
+    lib.leapquant_decode_close_list.argtypes = [P, S, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.leapquant_window_close_list.argtypes = [P, S, vp, vp, i32, vp]
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     lib.leapquant_bf16w_decode_step.argtypes = [P, vp, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_bf16w_window_close.argtypes = [P, vp, S, i32, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
               "leapquant_decode_close", "leapquant_dense_step", "leapquant_decode_step_slots",
               "leapquant_decode_close_slots", "leapquant_window_close_slots",
+              "leapquant_decode_close_list", "leapquant_window_close_list",
               "leapquant_dequantize_state", "leapquant_bf16w_decode_step",
               "leapquant_bf16w_window_close"):
         getattr(lib, f).restype = ctypes.c_int

@@ -242,6 +242,35 @@ def leapquant_window_close_slots(state, lengths, stream=None):
                                                   _stream(stream, state.device)))
 
 
+def _list_ptr(slots):
+    if not isinstance(slots, torch.Tensor) or slots.dim() != 1:
+        raise ValueError("slots must be a 1-D int32 tensor of slot ids")
+    return _ptr(slots, _I32, (slots.numel(),), "slots"), slots.numel()
+
+
+def leapquant_decode_close_list(state, pos, slots, q, k, v, beta, alpha, o, stream=None):
+    """Fused last-token decode and close of the listed slots only: slots is
+    an int32 tensor of distinct slot ids on the device (one workgroup each);
+    slot s works as in leapquant_decode_close_slots with pos[s]."""
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    lp, count = _list_ptr(slots)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_decode_close_list(ctypes.byref(prm), ctypes.byref(st),
+                                                 _slots_ptr(pos, state.n, "pos"), lp, int(count), *args,
+                                                 _stream(stream, state.device)))
+
+
+def leapquant_window_close_list(state, lengths, slots, stream=None):
+    """Window close of the listed slots only (distinct int32 slot ids on
+    the device); slot s is closed with lengths[s] records as in
+    leapquant_window_close_slots."""
+    lp, count = _list_ptr(slots)
+    prm, st = state.params(), state.ptrs()
+    L.check(L.load().leapquant_window_close_list(ctypes.byref(prm), ctypes.byref(st),
+                                                 _slots_ptr(lengths, state.n, "lengths"), lp, int(count),
+                                                 _stream(stream, state.device)))
+
+
 def _bf16_ptr(state, B):
     return _ptr(B, torch.bfloat16, (state.n, state.dk, state.dv), "B")
 

@@ -360,6 +360,99 @@ int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
+// Compacted forms: the slot list (count int32 ids on the device) must not
+// overlap the state, the outputs or the per-slot array.
+static int check_list(const lq_params *prm, const lq_state *st, const int32_t *v, const int32_t *list,
+                      int32_t count, const float *o) {
+  if (count < 0 || count > prm->n) return LQ_ERR_SHAPE;
+  if (count == 0) return LQ_OK;
+  if (!list) return LQ_ERR_NULL;
+  if (!aligned(list, 4)) return LQ_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(prm->n);
+  const Range in = span(list, static_cast<size_t>(count) * sizeof(int32_t));
+  const size_t gate_elems = prm->gate == LQ_GATE_KDA ? n * prm->p * kDim : n * prm->p;
+  if ((o && overlap(in, span(o, n * kDim * sizeof(float)))) || overlap(in, span(v, n * sizeof(int32_t))) ||
+      overlap(in, span(st->codes, n * kDim * kDim)) ||
+      overlap(in, span(st->row_scale, n * kDim * sizeof(float))) ||
+      overlap(in, span(st->col_scale, n * kDim * sizeof(float))) ||
+      overlap(in, span(st->buf_gate, gate_elems * sizeof(float))) ||
+      overlap(in, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
+      overlap(in, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
+      (prm->r > 0 && (overlap(in, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
+                      overlap(in, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
+      overlap(in, key_span(prm, st)))
+    return LQ_ERR_ALIAS;
+  return LQ_OK;
+}
+
+int leapquant_decode_close_list(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                const int32_t *list, int32_t count, const float *q, const float *k,
+                                const float *v, const float *beta, const float *alpha, float *o,
+                                hipStream_t stream) {
+  int rc = check_token_call(prm, st, 0, q, k, v, beta, alpha, o);
+  if (rc) return rc;
+  if ((rc = check_slots(prm, st, pos, o))) return rc;
+  if ((rc = check_list(prm, st, pos, list, count, o))) return rc;
+  if (count == 0) return LQ_OK;
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+  a.lens = pos;
+  a.slots = list;
+  a.n_launch = count;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.len = 0;
+  a.flags = prm->flags;
+  a.iters = prm->comp_iters;
+  return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
+}
+
+int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const int32_t *len,
+                                const int32_t *list, int32_t count, hipStream_t stream) {
+  int rc = check_params(prm);
+  if (rc) return rc;
+  if ((rc = check_boundary(prm, st))) return rc;
+  if ((rc = check_buffer(prm, st))) return rc;
+  if ((rc = check_slots(prm, st, len, nullptr))) return rc;
+  if ((rc = check_list(prm, st, len, list, count, nullptr))) return rc;
+  if (count == 0) return LQ_OK;
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  a.lens = len;
+  a.slots = list;
+  a.n_launch = count;
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.len = 1;
+  a.flags = prm->flags;
+  a.iters = prm->comp_iters;
+  return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
+}
+
 int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const float *q,
                          const float *k, const float *v, const float *beta, const float *alpha,
                          float *o, hipStream_t stream) {

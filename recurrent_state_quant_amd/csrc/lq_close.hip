@@ -401,7 +401,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
 // 12% faster than 3 workgroups per CU.
 template <bool KDA, bool FUSED, bool DENSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DENSE ? 4 : 1))) void close_kernel(const CloseArgs A) {
-  const size_t s = blockIdx.x;
+  // the state: this workgroup's, or the listed slot of a compacted launch
+  int slot = blockIdx.x;
+  if (A.slots) {
+    slot = A.slots[blockIdx.x];
+    if ((unsigned)slot >= (unsigned)A.n) return;
+  }
+  const size_t s = slot;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int lr = lane >> 4, lc = lane & 15;
@@ -748,15 +754,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
 // ---------------------------------------------------------------------------
 template <bool FUSED>
 hipError_t launch_close(const CloseArgs &a, bool kda, hipStream_t stream) {
+  const dim3 grid(a.slots ? a.n_launch : a.n);
   const bool dense = a.comp_key != nullptr;
   if (kda && dense)
-    hipLaunchKernelGGL((close_kernel<true, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<true, FUSED, true>), grid, dim3(256), 0, stream, a);
   else if (kda)
-    hipLaunchKernelGGL((close_kernel<true, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<true, FUSED, false>), grid, dim3(256), 0, stream, a);
   else if (dense)
-    hipLaunchKernelGGL((close_kernel<false, FUSED, true>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<false, FUSED, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((close_kernel<false, FUSED, false>), dim3(a.n), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((close_kernel<false, FUSED, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

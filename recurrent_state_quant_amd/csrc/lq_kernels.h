@@ -45,6 +45,10 @@ struct CloseArgs {
   // per-state record counts (nullptr: len for all); for decode_close the
   // last token's window position
   const int32_t *lens;
+  // compacted launch: workgroup i closes state slots[i] (ids outside
+  // [0, n) skipped); nullptr: workgroup i closes state i
+  const int32_t *slots;
+  int n_launch;      // workgroups when slots != nullptr
   int n, p, r, len;  // len: buffered records the rebuild replays
   int iters;         // dense compensators: subspace iterations of the split
   unsigned flags;

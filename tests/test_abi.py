@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.leapquant_abi_version() == L.ABI_VERSION == 3
+    assert lib.leapquant_abi_version() == L.ABI_VERSION == 4
     for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
                  L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
         assert lib.leapquant_status_string(code)
@@ -204,6 +204,44 @@ def test_slot_entry_points_validation(lib):
     assert f(ctypes.byref(prm), ctypes.byref(st), None, None) == L.LQ_ERR_NULL
     assert f(ctypes.byref(prm), ctypes.byref(st), pos + 1, None) == L.LQ_ERR_ALIGN
     assert f(ctypes.byref(prm), ctypes.byref(st), st.codes + 128, None) == L.LQ_ERR_ALIAS
+
+
+def test_list_entry_points_validation(lib):
+    """Compacted closes: count in [0, n], the list non-NULL, 4-byte aligned
+    and clear of the state, the outputs and the per-slot array; count == 0
+    is accepted and launches nothing.  Every other call here fails its
+    checks, so nothing is launched on these host addresses."""
+    st, base = _state()
+    prm = _params()
+    vec = 4 * 512
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+    pos = base + 5 * vec
+    lst = base + 6 * vec
+    f = lib.leapquant_decode_close_list
+
+    def call(l_=lst, count=2, p_=pos, **kw):
+        x = dict(a, **kw)
+        return f(ctypes.byref(prm), ctypes.byref(st), p_, l_, count, x["q"], x["k"], x["v"], x["beta"],
+                 x["alpha"], x["o"], None)
+    assert call(count=-1) == L.LQ_ERR_SHAPE
+    assert call(count=5) == L.LQ_ERR_SHAPE                       # more entries than slots
+    assert call(l_=None) == L.LQ_ERR_NULL
+    assert call(l_=lst + 2) == L.LQ_ERR_ALIGN
+    assert call(l_=st.codes + 64) == L.LQ_ERR_ALIAS              # list inside the codes
+    assert call(l_=pos + 4) == L.LQ_ERR_ALIAS                    # list over the positions
+    assert call(l_=a["o"]) == L.LQ_ERR_ALIAS                     # list over the output
+    assert call(p_=None) == L.LQ_ERR_NULL
+    assert call(o=0) == L.LQ_ERR_NULL
+    assert call(l_=None, count=0) == L.LQ_OK                     # nothing to do: no launch
+    g = lib.leapquant_window_close_list
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, lst, -1, None) == L.LQ_ERR_SHAPE
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, lst, 5, None) == L.LQ_ERR_SHAPE
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, None, 1, None) == L.LQ_ERR_NULL
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, lst + 1, 1, None) == L.LQ_ERR_ALIGN
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, st.buf_k + 8, 1, None) == L.LQ_ERR_ALIAS
+    assert g(ctypes.byref(prm), ctypes.byref(st), None, lst, 1, None) == L.LQ_ERR_NULL
+    assert g(ctypes.byref(prm), ctypes.byref(st), pos, None, 0, None) == L.LQ_OK
 
 
 def test_dense_compensator_validation(lib, entry):
