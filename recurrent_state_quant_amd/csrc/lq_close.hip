@@ -721,28 +721,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
 // ---------------------------------------------------------------------------
 // Dequantize: S_out = deQ(codes, a, s) + compensator rows (fp32).  Thread
 // (half hh, column j) reads the 64 code bytes of its column segment and
-// writes column j of rows 64hh .. 64hh+63.
+// writes column j of rows 64hh .. 64hh+63; the row scales and compensator
+// data are staged in LDS once per state.
 // ---------------------------------------------------------------------------
 template <bool DENSE>
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs A) {
   const size_t s = blockIdx.x;
-  const int j = threadIdx.x & (D - 1), hh = threadIdx.x >> 7;
+  const int tid = threadIdx.x;
+  const int j = tid & (D - 1), hh = tid >> 7;  // column j, row half hh
   const int r = A.r;
-  const float sj = A.col_scale[s * D + j];
+  __shared__ float sh_a[D];                      // row scales
+  __shared__ int sh_cs[DENSE ? 1 : D];           // compensator slot of a row or -1
+  __shared__ float sh_key[DENSE ? 16 * D : 1];   // dense keys [c][row]
+  __shared__ float sh_val[16 * D];               // compensator rows [c][col]
+  // every load first: this thread's 64 codes (4 x 16 bytes of one column
+  // half), its column scale, then the per-state side data
   const uint4 *src = reinterpret_cast<const uint4 *>(A.codes + s * D * D + hh * 8192 + j * 64);
+  uint4 cq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cq[q] = src[q];
+  const float sj = A.col_scale[s * D + j];
+  if (tid < D) {
+    sh_a[tid] = A.row_scale[s * D + tid];
+    if (!DENSE) sh_cs[tid] = -1;
+  }
+  for (int e = tid; e < r * D; e += 256) {
+    sh_val[e] = A.comp_val[s * r * D + e];
+    if (DENSE) sh_key[e] = A.comp_key[s * r * D + e];
+  }
+  __syncthreads();
+  if (!DENSE && tid < r) {
+    const int idx = A.comp_idx[s * r + tid];  // entries outside [0, dk) are ignored
+    if ((unsigned)idx < (unsigned)D) sh_cs[idx] = tid;
+  }
+  __syncthreads();
+#pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 cq = src[q];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int slot = 16 * q + e;
       const int row = 64 * hh + code_slot(slot);  // the slot map is its own inverse
-      const uint32_t wd = u4get(cq, e >> 2);
-      float x = (float)(int8_t)(wd >> (8 * (e & 3))) * A.row_scale[s * D + row] * sj;
+      const uint32_t wd = u4get(cq[q], e >> 2);
+      float x = (float)(int8_t)(wd >> (8 * (e & 3))) * sh_a[row] * sj;
       if (DENSE) {
-        for (int c = 0; c < r; ++c) x = fmaf(A.comp_key[(s * r + c) * D + row], A.comp_val[(s * r + c) * D + j], x);
+        for (int c = 0; c < r; ++c) x = fmaf(sh_key[c * D + row], sh_val[c * D + j], x);
       } else {
-        for (int c = 0; c < r; ++c)
-          if (A.comp_idx[s * r + c] == row) x += A.comp_val[(s * r + c) * D + j];
+        const int c = sh_cs[row];
+        if (c >= 0) x += sh_val[c * D + j];
       }
       A.S_out[(s * D + row) * D + j] = x;
     }
