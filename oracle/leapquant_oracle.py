@@ -159,10 +159,13 @@ def sequential_exact(S0, tokens, gate, keep_every=0, flags=0):
 # --------------------------------------------------------------------------
 # Quantized boundary state ([EL] Abstract, Figure 4; [TM])
 # --------------------------------------------------------------------------
-def mgs(Y):
+def mgs(Y, ratios=None):
     """Modified Gram-Schmidt on the columns of Y [dk, r] (fp64), in column
     order.  A column whose norm after projection is zero or at most MGS_DROP
-    times its norm before projection gives a zero column."""
+    times its norm before projection gives a zero column.  If `ratios` is a
+    list, the ratio (norm after projection) / (norm before) of every column
+    is appended to it (0 for a zero column): a diagnostic only, the result
+    does not depend on it."""
     dk, r = Y.shape
     K = np.zeros((dk, r))
     for c in range(r):
@@ -171,19 +174,25 @@ def mgs(Y):
         for c2 in range(c):
             v = v - (K[:, c2] @ v) * K[:, c2]
         nv = np.sqrt(v @ v)
+        if ratios is not None:
+            ratios.append(nv / n0 if n0 > 0 else 0.0)
         if nv > 0 and nv > MGS_DROP * n0:
             K[:, c] = v / nv
     return K
 
 
-def dense_keys(S64, start_rows, iters):
+def dense_keys(S64, start_rows, iters, ratios=None):
     """Keys of the dense compensator tokens of one state: subspace iteration
-    on S S^T from the one-hot keys of `start_rows` (fp64, [dk, r])."""
+    on S S^T from the one-hot keys of `start_rows` (fp64, [dk, r]).  With a
+    list `ratios`, each round appends its list of MGS ratios (see mgs)."""
     dk = S64.shape[0]
     K = np.zeros((dk, len(start_rows)))
     K[start_rows, np.arange(len(start_rows))] = 1.0
     for _ in range(iters):
-        K = mgs(S64 @ (S64.T @ K))
+        rr = None if ratios is None else []
+        K = mgs(S64 @ (S64.T @ K), rr)
+        if ratios is not None:
+            ratios.append(rr)
     return K
 
 

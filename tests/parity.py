@@ -11,10 +11,14 @@ Tolerances:
   * compensator selection: identical row sets, unless the oracle's r-th and
     (r+1)-th row norms are a near tie (relative gap < 1e-5), in which case
     that state's boundary is reported as a tie and checked by invariants;
-  * dense compensator keys: within KEY_ATOL; the rest of a dense boundary is
-    compared with the oracle's split under the GPU's keys, except for states
-    of numerical rank <= r, whose residual is rounding noise: those must
-    reconstruct the state to NOISE_RESIDUAL of its largest entry.
+  * dense compensator keys: the leading keys that the fp32 state determines
+    (every Gram-Schmidt ratio of the oracle's iteration outside
+    (RATIO_DROPPED, RATIO_OK)) within KEY_ATOL; every GPU key unit or zero
+    and orthogonal to the others within a bound scaled by the keys'
+    conditioning; the rest of a dense boundary is compared with the
+    oracle's split under the GPU's keys, except for states of numerical
+    rank <= r, whose residual is rounding noise: those must reconstruct the
+    state to NOISE_RESIDUAL of its largest entry.
 """
 import numpy as np
 
@@ -31,6 +35,19 @@ TIE_GAP = 1e-5
 # mistake moves keys by O(0.1).
 KEY_ATOL = 1e-3
 NOISE_RESIDUAL = 1e-4  # residual / state magnitude below which a dense split is rank-exhausted
+# A Gram-Schmidt step that leaves a fraction rho of a column's norm amplifies
+# the error of that column by 1/rho.  The fp32 evaluation of S S^T K carries
+# up to about 1.5e-5 of |S S^T k| (two 128-term sums); below RATIO_OK that
+# error can exceed KEY_ATOL in the normalized key, and later keys inherit it
+# through their projections.  Columns below RATIO_DROPPED (a tenth of the
+# drop threshold) are dropped on both sides with margin.
+RATIO_OK = 2e-2
+RATIO_DROPPED = 1e-4
+# Loss of orthogonality between the GPU's nonzero keys c and d: the same
+# error, amplified by 1 / (the smaller of the two keys' ratios, at least the
+# drop threshold), with a floor for well-conditioned keys.
+KEY_ORTHO_EPS = 1.5e-5
+KEY_ORTHO_FLOOR = 1e-4
 
 
 def assert_close(gpu, ref, what, rtol=RTOL, atol=ATOL):
@@ -116,11 +133,41 @@ def compare_boundary(gpu, ref, S_ref, r, what, exact=False, band=None):
     return stats
 
 
+def key_ratios(S32, r, iters):
+    """Gram-Schmidt ratios of the oracle's dense-key iteration: [n, iters, r]
+    (see oracle mgs), for the states S32 started from their top-r rows."""
+    S32 = np.asarray(S32, np.float32)
+    out = np.ones((len(S32), iters, r))
+    for s in range(len(S32)):
+        S64 = S32[s].astype(np.float64)
+        start = np.argsort(-np.einsum("ij,ij->i", S64, S64), kind="stable")[:r]
+        ratios = []
+        O.dense_keys(S64, start, iters, ratios)
+        if iters:
+            out[s] = np.array(ratios)
+    return out
+
+
+def determined_keys(ratios):
+    """Per state, the number of leading dense keys that the fp32 state
+    determines to KEY_ATOL: keys up to the first one whose ratio, in any
+    round, lies between RATIO_DROPPED and RATIO_OK (key c depends only on
+    keys 0..c of this and earlier rounds)."""
+    bad = ((ratios > RATIO_DROPPED) & (ratios < RATIO_OK)).any(axis=1)  # [n, r]
+    r = ratios.shape[2]
+    return np.where(bad.any(axis=1), bad.argmax(axis=1), r)
+
+
 def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     """Dense compensator tokens.
 
     The keys come from an fp32 iteration on the GPU and an fp64 one in the
-    oracle, so they agree to KEY_ATOL; given the keys, the values follow.
+    oracle.  A key that survives a Gram-Schmidt step with a small fraction
+    of its norm carries the fp32 error amplified by the inverse of that
+    fraction, and so do the keys after it; the leading keys up to the first
+    such one agree to KEY_ATOL and are compared, every GPU key is checked
+    for unit norm (or zero) and orthogonality to the others.  Given the
+    keys, the values follow.
     The residual S - sum_c k_c w_c^T is evaluated in fp32 on the GPU; in rows
     that the tokens mostly carry it is small next to the terms it is computed
     from, so its rounding error (bounded below) is large in code units and
@@ -138,10 +185,28 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     ok = ~near_tie(S_ref, r)
     ref = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters)
     stats = {"states": len(S_ref), "ties": int((~ok).sum()), "flips": 0, "codes": 0, "low_rank": 0,
-             "max_excess": 0.0}
+             "max_excess": 0.0, "keys_compared": 0, "keys_undetermined": 0}
     if r and ok.any():
         np.testing.assert_array_equal(g_all["comp_idx"][ok], ref["comp_idx"][ok], err_msg=f"{what}: start rows")
-        assert_close(g_all["comp_key"][ok], ref["comp_key"][ok], f"{what}: comp_key", rtol=0, atol=KEY_ATOL)
+        # keys the fp32 state determines: against the oracle's; the rest:
+        # unit or zero and orthogonal (checked below for every key)
+        rat = key_ratios(S_ref[ok], r, iters)
+        det = determined_keys(rat)
+        mask = np.arange(r)[None, :] < det[:, None]
+        assert_close(g_all["comp_key"][ok][mask], ref["comp_key"][ok][mask], f"{what}: comp_key",
+                     rtol=0, atol=KEY_ATOL)
+        stats["keys_compared"] = int(mask.sum())
+        stats["keys_undetermined"] = int((~mask).sum())
+        Kg = g_all["comp_key"][ok].astype(np.float64)
+        G = np.einsum("nci,ndi->ncd", Kg, Kg)
+        nz = np.linalg.norm(Kg, axis=2) > 0.5
+        both = nz[:, :, None] & nz[:, None, :]
+        dev = np.abs(G - np.eye(r)[None])
+        rmin = np.maximum(rat.min(axis=1), O.MGS_DROP) if iters else np.ones((len(Kg), r))
+        tol = np.maximum(KEY_ORTHO_FLOOR, KEY_ORTHO_EPS / np.minimum(rmin[:, :, None], rmin[:, None, :]))
+        assert np.all(dev[both] <= tol[both]), \
+            f"{what}: GPU keys not orthonormal (worst excess {(dev - tol)[both].max()})"
+        assert np.all(Kg[~nz] == 0), f"{what}: a dropped GPU key is not zero"
     ref_g = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters, keys=g_all["comp_key"])
     K = g_all["comp_key"].astype(np.float64)
     W = ref_g["comp_val"].astype(np.float64)
