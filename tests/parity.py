@@ -43,9 +43,10 @@ NOISE_RESIDUAL = 1e-4  # residual / state magnitude below which a dense split is
 # drop threshold) are dropped on both sides with margin.
 RATIO_OK = 2e-2
 RATIO_DROPPED = 1e-4
-# Loss of orthogonality between the GPU's nonzero keys c and d: the same
-# error, amplified by 1 / (the smaller of the two keys' ratios, at least the
-# drop threshold), with a floor for well-conditioned keys.
+# Loss of orthogonality between the GPU's nonzero keys c < d: the same
+# error, amplified by 1 / (the smallest ratio, at least the drop threshold,
+# among the kept keys 0..d, which key d was projected against), with a
+# floor for well-conditioned keys.
 KEY_ORTHO_EPS = 1.5e-5
 KEY_ORTHO_FLOOR = 1e-4
 
@@ -202,10 +203,19 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
         nz = np.linalg.norm(Kg, axis=2) > 0.5
         both = nz[:, :, None] & nz[:, None, :]
         dev = np.abs(G - np.eye(r)[None])
-        rmin = np.maximum(rat.min(axis=1), O.MGS_DROP) if iters else np.ones((len(Kg), r))
-        tol = np.maximum(KEY_ORTHO_FLOOR, KEY_ORTHO_EPS / np.minimum(rmin[:, :, None], rmin[:, None, :]))
-        assert np.all(dev[both] <= tol[both]), \
-            f"{what}: GPU keys not orthonormal (worst excess {(dev - tol)[both].max()})"
+        if iters:
+            # per key, its smallest ratio over the rounds in which it was kept
+            kept = rat > RATIO_DROPPED
+            rk = np.where(kept, np.maximum(rat, O.MGS_DROP), 1.0).min(axis=1)
+            cum = np.minimum.accumulate(rk, axis=1)          # over keys 0..d
+        else:
+            cum = np.ones((len(Kg), r))
+        later = np.maximum(np.arange(r)[:, None], np.arange(r)[None, :])
+        tol = np.maximum(KEY_ORTHO_FLOOR, KEY_ORTHO_EPS / cum[:, later])
+        if not np.all(dev[both] <= tol[both]):
+            i = np.unravel_index(np.argmax(np.where(both, dev - tol, -np.inf)), dev.shape)
+            raise AssertionError(f"{what}: GPU keys not orthonormal: state {i[0]}, keys {i[1]}, {i[2]}: "
+                                 f"{dev[i]:.3g} > {tol[i]:.3g}")
         assert np.all(Kg[~nz] == 0), f"{what}: a dropped GPU key is not zero"
     ref_g = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters, keys=g_all["comp_key"])
     K = g_all["comp_key"].astype(np.float64)
