@@ -57,7 +57,9 @@
  *                          unknown gate or flag, t or len out of range
  *       LQ_ERR_UNSUPPORTED dk != 128 or dv != 128
  *       LQ_ERR_ALIGN       a pointer violates the alignment above
- *       LQ_ERR_ALIAS       an output range overlaps an input range
+ *       LQ_ERR_ALIAS       an output range overlaps an input range, or two
+ *                          arrays of the lq_state overlap (checked by every
+ *                          call that writes the state)
  *     A failed launch returns LQ_ERR_HIP.
  *   - Values are not checked: NaN or Inf inputs give unspecified (but
  *     in-bounds) results.  comp_idx entries outside [0, dk) are ignored when
@@ -134,7 +136,9 @@ typedef struct lq_params {
 /* One slab of n states.  codes .. comp_val and comp_key are the boundary
  * state (the prefix-cache snapshot); buf_gate, buf_k and buf_u are the
  * window buffer.  For r == 0, comp_idx, comp_val and comp_key may be NULL;
- * comp_key may be NULL without LQ_DENSE_COMP. */
+ * comp_key may be NULL without LQ_DENSE_COMP.  The arrays a call uses must
+ * not overlap one another, since a launch that writes some of them reads the
+ * others: the calls that write the state return LQ_ERR_ALIAS otherwise. */
 typedef struct lq_state {
   int8_t *codes;     /* [n][dk*dv]  int8 residual codes c_ij (layout above) */
   float *row_scale;  /* [n][dk]     a_i                                     */

@@ -65,6 +65,39 @@ int check_buffer(const lq_params *prm, const lq_state *st) {
   return LQ_OK;
 }
 
+// The arrays of one state must not overlap one another: a launch that writes
+// the state reads the same arrays (the boundary in the close, the buffer row
+// of the current token in the decode).  `boundary` and `buffer` select the
+// halves the call uses; NULL arrays of a half the call does not use are
+// skipped.
+int check_state_disjoint(const lq_params *prm, const lq_state *st, bool boundary, bool buffer) {
+  const size_t n = static_cast<size_t>(prm->n), p = static_cast<size_t>(prm->p);
+  const size_t r = static_cast<size_t>(prm->r);
+  const size_t vec = n * kDim * sizeof(float);
+  Range rs[9];
+  int m = 0;
+  if (boundary) {
+    rs[m++] = span(st->codes, n * kDim * kDim);
+    rs[m++] = span(st->row_scale, vec);
+    rs[m++] = span(st->col_scale, vec);
+    if (r > 0) {
+      rs[m++] = span(st->comp_idx, n * r * sizeof(int32_t));
+      rs[m++] = span(st->comp_val, n * r * kDim * sizeof(float));
+    }
+    rs[m++] = key_span(prm, st);
+  }
+  if (buffer) {
+    const size_t gate_elems = prm->gate == LQ_GATE_KDA ? n * p * kDim : n * p;
+    rs[m++] = span(st->buf_gate, gate_elems * sizeof(float));
+    rs[m++] = span(st->buf_k, n * p * kDim * sizeof(float));
+    rs[m++] = span(st->buf_u, n * p * kDim * sizeof(float));
+  }
+  for (int i = 0; i < m; ++i)
+    for (int j = i + 1; j < m; ++j)
+      if (overlap(rs[i], rs[j])) return LQ_ERR_ALIAS;
+  return LQ_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_HIP; }
 
 }  // namespace
@@ -80,7 +113,7 @@ const char *leapquant_status_string(int status) {
     case LQ_ERR_SHAPE: return "invalid size or parameter (n, p, r, gate, flags, t or len)";
     case LQ_ERR_UNSUPPORTED: return "unsupported head size (dk and dv must be 128)";
     case LQ_ERR_ALIGN: return "pointer is not aligned as required";
-    case LQ_ERR_ALIAS: return "an output overlaps an input";
+    case LQ_ERR_ALIAS: return "an output overlaps an input, or two arrays of the state overlap";
     case LQ_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
@@ -102,6 +135,7 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
                       overlap(src, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
       overlap(src, key_span(prm, st)))
     return LQ_ERR_ALIAS;
+  if ((rc = check_state_disjoint(prm, st, true, false))) return rc;
   lq::CloseArgs a{};
   a.codes = st->codes;
   a.row_scale = st->row_scale;
@@ -132,6 +166,7 @@ int check_token_call(const lq_params *prm, const lq_state *st, int32_t t, const 
   if (rc) return rc;
   if ((rc = check_boundary(prm, st))) return rc;
   if ((rc = check_buffer(prm, st))) return rc;
+  if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if (t < 0 || t >= prm->p) return LQ_ERR_SHAPE;
   if (!q || !k || !v || !beta || !alpha || !o) return LQ_ERR_NULL;
   const bool kda = prm->gate == LQ_GATE_KDA;
@@ -197,6 +232,7 @@ int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len
   if (rc) return rc;
   if ((rc = check_boundary(prm, st))) return rc;
   if ((rc = check_buffer(prm, st))) return rc;
+  if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if (len < 1 || len > prm->p) return LQ_ERR_SHAPE;
   lq::CloseArgs a{};
   a.codes = st->codes;
@@ -339,6 +375,7 @@ int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const
   if (rc) return rc;
   if ((rc = check_boundary(prm, st))) return rc;
   if ((rc = check_buffer(prm, st))) return rc;
+  if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if ((rc = check_slots(prm, st, len, nullptr))) return rc;
   lq::CloseArgs a{};
   a.codes = st->codes;
@@ -428,6 +465,7 @@ int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const 
   if (rc) return rc;
   if ((rc = check_boundary(prm, st))) return rc;
   if ((rc = check_buffer(prm, st))) return rc;
+  if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if ((rc = check_slots(prm, st, len, nullptr))) return rc;
   if ((rc = check_list(prm, st, len, list, count, nullptr))) return rc;
   if (count == 0) return LQ_OK;
@@ -501,7 +539,7 @@ static int check_bf16w(const lq_params *prm, const void *B, const lq_state *st) 
       overlap(b, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
       overlap(b, span(st->buf_u, n * prm->p * kDim * sizeof(float))))
     return LQ_ERR_ALIAS;
-  return LQ_OK;
+  return check_state_disjoint(prm, st, false, true);
 }
 
 int leapquant_bf16w_decode_step(const lq_params *prm, const void *B, const lq_state *st, int32_t t,

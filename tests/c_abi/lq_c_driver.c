@@ -110,6 +110,10 @@ static int check_mode(void) {
   EXPECT(leapquant_decode_step(&prm, &mis, 0, tok, tok, tok, tok, tok, o, NULL), LQ_ERR_ALIGN);
   /* the fp32 source of a quantize overlapping the codes it writes */
   EXPECT(leapquant_quantize_state(&prm, (const float *)st.codes, &st, NULL), LQ_ERR_ALIAS);
+  /* two arrays of the state overlapping each other */
+  lq_state ovl = st;
+  ovl.buf_u = ovl.buf_k;
+  EXPECT(leapquant_window_close(&prm, &ovl, 16, NULL), LQ_ERR_ALIAS);
   /* o overlapping a token input */
   EXPECT(leapquant_decode_step(&prm, &st, 0, tok, tok, tok, tok, tok, tok, NULL), LQ_ERR_ALIAS);
   /* dense compensators need comp_key */

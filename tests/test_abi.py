@@ -157,6 +157,44 @@ def test_aliasing_rejected(lib, entry):
     assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), st.row_scale, None) == L.LQ_ERR_ALIAS
 
 
+def test_overlapping_state_arrays_rejected(lib, entry):
+    """Every call that writes the state rejects a state whose own arrays
+    overlap (the launch would read what it writes); arrays a call does not
+    use are not looked at."""
+    prm = _params()
+    _, base = _state()
+    pos = base + 5 * 2048
+    lst = base + 6 * 2048
+    for f, g in (("buf_k", "codes"), ("buf_u", "buf_k"), ("comp_val", "row_scale"), ("buf_gate", "col_scale"),
+                 ("comp_idx", "comp_val")):
+        st, _ = _state()
+        setattr(st, f, getattr(st, g) + 256)
+        what = f"{f} inside {g}"
+        assert _decode(lib, prm, st) == L.LQ_ERR_ALIAS, what
+        assert lib.leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), 16, None) == L.LQ_ERR_ALIAS, what
+        assert lib.leapquant_window_close_slots(ctypes.byref(prm), ctypes.byref(st), pos, None) == L.LQ_ERR_ALIAS, what
+        assert lib.leapquant_window_close_list(ctypes.byref(prm), ctypes.byref(st), pos, lst, 1, None) == \
+            L.LQ_ERR_ALIAS, what
+    # quantize writes the boundary only: boundary arrays overlapping each
+    # other are rejected, the (unused) buffer is not looked at
+    st, _ = _state()
+    st.row_scale = st.codes + 4096
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), FAKE + (1 << 36), ctypes.byref(st), None) == L.LQ_ERR_ALIAS
+    st, _ = _state()
+    st.buf_u = st.buf_k
+    st.codes = st.codes + 8   # misaligned: the buffer overlap was not what failed
+    assert lib.leapquant_quantize_state(ctypes.byref(prm), FAKE + (1 << 36), ctypes.byref(st), None) == L.LQ_ERR_ALIGN
+    # the bf16 + per-window calls use only the buffer of the state
+    B = FAKE + (1 << 37)
+    st, _ = _state(codes=0, row_scale=0, col_scale=0, comp_idx=0, comp_val=0, comp_key=0)
+    st.buf_u = st.buf_k + 512
+    assert lib.leapquant_bf16w_window_close(ctypes.byref(prm), B, ctypes.byref(st), 16, None) == L.LQ_ERR_ALIAS
+    dense = _params(flags=L.LQ_DENSE_COMP, comp_iters=1)
+    st, _ = _state()
+    st.comp_key = st.buf_gate
+    assert _decode(lib, dense, st) == L.LQ_ERR_ALIAS
+
+
 def test_dense_step_validation(lib):
     prm = _params()
     _, base = _state()
