@@ -21,11 +21,13 @@ def _gate_id(gate):
     raise ValueError(f"unknown gate {gate!r}")
 
 
-def _ptr(x, dtype, shape, name):
+def _ptr(x, dtype, shape, name, device=None):
     if not isinstance(x, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if x.device.type != "cuda":
         raise ValueError(f"{name} must be in device memory")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} is on {x.device}, the state on {device}")
     if x.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
     if tuple(x.shape) != tuple(shape):
@@ -38,6 +40,8 @@ def _ptr(x, dtype, shape, name):
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the state on {device}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -109,6 +113,7 @@ class LeapQuantState:
         self.buf_k = torch.zeros((n, p, dk), dtype=_F32, device=dev)
         self.buf_u = torch.zeros((n, p, dv), dtype=_F32, device=dev)
         self.comp_key = torch.zeros((n, r, dk) if self.dense else (0,), dtype=_F32, device=dev)
+        self.device = self.codes.device   # with its index resolved
 
     @property
     def dense(self):
@@ -183,36 +188,40 @@ class LeapQuantState:
 
 def leapquant_quantize_state(state, S, stream=None):
     n, dk, dv = state.n, state.dk, state.dv
-    s = _ptr(S, _F32, (n, dk, dv), "S")
+    s = _ptr(S, _F32, (n, dk, dv), "S", state.device)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_quantize_state(ctypes.byref(prm), s, ctypes.byref(st),
-                                              _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_quantize_state(ctypes.byref(prm), s, ctypes.byref(st),
+                                                  _stream(stream, state.device)))
 
 
 def leapquant_decode_step(state, t, q, k, v, beta, alpha, o, stream=None):
     args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_decode_step(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
-                                           _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_step(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
+                                               _stream(stream, state.device)))
 
 
 def _token_args(state, q, k, v, beta, alpha, o):
     n, dk, dv = state.n, state.dk, state.dv
     ashape = (n,) if state.gate == L.LQ_GATE_GDN else (n, dk)
-    return [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
-            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
-            _ptr(o, _F32, (n, dv), "o")]
+    d = state.device
+    return [_ptr(q, _F32, (n, dk), "q", d), _ptr(k, _F32, (n, dk), "k", d), _ptr(v, _F32, (n, dv), "v", d),
+            _ptr(beta, _F32, (n,), "beta", d), _ptr(alpha, _F32, ashape, "alpha", d),
+            _ptr(o, _F32, (n, dv), "o", d)]
 
 
 def leapquant_decode_close(state, t, q, k, v, beta, alpha, o, stream=None):
     args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_decode_close(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
-                                            _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_close(ctypes.byref(prm), ctypes.byref(st), int(t), *args,
+                                                _stream(stream, state.device)))
 
 
-def _slots_ptr(x, n, name):
-    return _ptr(x, _I32, (n,), name)
+def _slots_ptr(x, state, name):
+    return _ptr(x, _I32, (state.n,), name, state.device)
 
 
 def leapquant_decode_step_slots(state, pos, q, k, v, beta, alpha, o, stream=None):
@@ -220,32 +229,35 @@ def leapquant_decode_step_slots(state, pos, q, k, v, beta, alpha, o, stream=None
     pos outside [0, p) are idle."""
     args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_decode_step_slots(ctypes.byref(prm), ctypes.byref(st),
-                                                 _slots_ptr(pos, state.n, "pos"), *args,
-                                                 _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_step_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                     _slots_ptr(pos, state, "pos"), *args,
+                                                     _stream(stream, state.device)))
 
 
 def leapquant_decode_close_slots(state, pos, q, k, v, beta, alpha, o, stream=None):
     args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_decode_close_slots(ctypes.byref(prm), ctypes.byref(st),
-                                                  _slots_ptr(pos, state.n, "pos"), *args,
-                                                  _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_close_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                      _slots_ptr(pos, state, "pos"), *args,
+                                                      _stream(stream, state.device)))
 
 
 def leapquant_window_close_slots(state, lengths, stream=None):
     """Close slot s with lengths[s] records (int32 [n] on the device) when
     1 <= lengths[s] <= p; other slots are left as they are."""
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_window_close_slots(ctypes.byref(prm), ctypes.byref(st),
-                                                  _slots_ptr(lengths, state.n, "lengths"),
-                                                  _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_window_close_slots(ctypes.byref(prm), ctypes.byref(st),
+                                                      _slots_ptr(lengths, state, "lengths"),
+                                                      _stream(stream, state.device)))
 
 
-def _list_ptr(slots):
+def _list_ptr(slots, state):
     if not isinstance(slots, torch.Tensor) or slots.dim() != 1:
         raise ValueError("slots must be a 1-D int32 tensor of slot ids")
-    return _ptr(slots, _I32, (slots.numel(),), "slots"), slots.numel()
+    return _ptr(slots, _I32, (slots.numel(),), "slots", state.device), slots.numel()
 
 
 def leapquant_decode_close_list(state, pos, slots, q, k, v, beta, alpha, o, stream=None):
@@ -253,26 +265,28 @@ def leapquant_decode_close_list(state, pos, slots, q, k, v, beta, alpha, o, stre
     an int32 tensor of distinct slot ids on the device (one workgroup each);
     slot s works as in leapquant_decode_close_slots with pos[s]."""
     args = _token_args(state, q, k, v, beta, alpha, o)
-    lp, count = _list_ptr(slots)
+    lp, count = _list_ptr(slots, state)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_decode_close_list(ctypes.byref(prm), ctypes.byref(st),
-                                                 _slots_ptr(pos, state.n, "pos"), lp, int(count), *args,
-                                                 _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_close_list(ctypes.byref(prm), ctypes.byref(st),
+                                                     _slots_ptr(pos, state, "pos"), lp, int(count), *args,
+                                                     _stream(stream, state.device)))
 
 
 def leapquant_window_close_list(state, lengths, slots, stream=None):
     """Window close of the listed slots only (distinct int32 slot ids on
     the device); slot s is closed with lengths[s] records as in
     leapquant_window_close_slots."""
-    lp, count = _list_ptr(slots)
+    lp, count = _list_ptr(slots, state)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_window_close_list(ctypes.byref(prm), ctypes.byref(st),
-                                                 _slots_ptr(lengths, state.n, "lengths"), lp, int(count),
-                                                 _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_window_close_list(ctypes.byref(prm), ctypes.byref(st),
+                                                     _slots_ptr(lengths, state, "lengths"), lp, int(count),
+                                                     _stream(stream, state.device)))
 
 
 def _bf16_ptr(state, B):
-    return _ptr(B, torch.bfloat16, (state.n, state.dk, state.dv), "B")
+    return _ptr(B, torch.bfloat16, (state.n, state.dk, state.dv), "B", state.device)
 
 
 def leapquant_bf16w_decode_step(state, B, t, q, k, v, beta, alpha, o, stream=None):
@@ -281,16 +295,18 @@ def leapquant_bf16w_decode_step(state, B, t, q, k, v, beta, alpha, o, stream=Non
     int8 boundary arrays are not used)."""
     args = _token_args(state, q, k, v, beta, alpha, o)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_bf16w_decode_step(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
-                                                 int(t), *args, _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_bf16w_decode_step(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
+                                                     int(t), *args, _stream(stream, state.device)))
 
 
 def leapquant_bf16w_window_close(state, B, length, stream=None):
     """"BF16 + per-window": B <- bf16(Gamma * B + K_w U) over `length`
     buffered records."""
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_bf16w_window_close(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
-                                                  int(length), _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_bf16w_window_close(ctypes.byref(prm), _bf16_ptr(state, B), ctypes.byref(st),
+                                                      int(length), _stream(stream, state.device)))
 
 
 def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0):
@@ -309,25 +325,29 @@ def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0)
     sp = _ptr(S, S.dtype, (n, dk, dv), "S")
     g = _gate_id(gate)
     ashape = (n,) if g == L.LQ_GATE_GDN else (n, dk)
-    args = [_ptr(q, _F32, (n, dk), "q"), _ptr(k, _F32, (n, dk), "k"), _ptr(v, _F32, (n, dv), "v"),
-            _ptr(beta, _F32, (n,), "beta"), _ptr(alpha, _F32, ashape, "alpha"),
-            _ptr(o, _F32, (n, dv), "o")]
+    d = S.device
+    args = [_ptr(q, _F32, (n, dk), "q", d), _ptr(k, _F32, (n, dk), "k", d), _ptr(v, _F32, (n, dv), "v", d),
+            _ptr(beta, _F32, (n,), "beta", d), _ptr(alpha, _F32, ashape, "alpha", d),
+            _ptr(o, _F32, (n, dv), "o", d)]
     prm = L.LqParams(n, dk, dv, 1, 0, g, int(flags))
-    L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
+    with torch.cuda.device(S.device):
+        L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
 
 
 def leapquant_window_close(state, length, stream=None):
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), int(length),
-                                            _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_window_close(ctypes.byref(prm), ctypes.byref(st), int(length),
+                                                _stream(stream, state.device)))
 
 
 def leapquant_dequantize_state(state, S_out, stream=None):
     n, dk, dv = state.n, state.dk, state.dv
-    s = _ptr(S_out, _F32, (n, dk, dv), "S_out")
+    s = _ptr(S_out, _F32, (n, dk, dv), "S_out", state.device)
     prm, st = state.params(), state.ptrs()
-    L.check(L.load().leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), s,
-                                                _stream(stream, state.device)))
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), s,
+                                                    _stream(stream, state.device)))
 
 
 def leapquant_status_string(status):
