@@ -39,7 +39,11 @@
  *     only during the call.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without waiting.  Device faults surface at the caller's next
- *     synchronization.
+ *     synchronization.  Every pointer is memory of the device the launch
+ *     runs on; call with that device current (hipSetDevice), since the
+ *     default stream belongs to the current device.  The library keeps no
+ *     state of its own: calls on different streams or host threads do not
+ *     interfere unless their arrays overlap.
  *   - Arrays are dense, row-major, in the shapes given below; n is the
  *     leading dimension of every per-state array.  The codes of one state
  *     are a 16 KiB block stored column-major in two 64-row halves: code
