@@ -42,8 +42,10 @@
  *     synchronization.  Every pointer is memory of the device the launch
  *     runs on; call with that device current (hipSetDevice), since the
  *     default stream belongs to the current device.  The library keeps no
- *     state of its own: calls on different streams or host threads do not
- *     interfere unless their arrays overlap.
+ *     state of its own and allocates no memory (the kernels use only the
+ *     caller's arrays, registers and LDS), so every call may be captured in
+ *     a graph; calls on different streams or host threads do not interfere
+ *     unless their arrays overlap.
  *   - Arrays are dense, row-major, in the shapes given below; n is the
  *     leading dimension of every per-state array.  The codes of one state
  *     are a 16 KiB block stored column-major in two 64-row halves: code
