@@ -196,7 +196,7 @@ def dense_keys(S64, start_rows, iters, ratios=None):
     return K
 
 
-def quantize(S, r, flags=0, iters=0, keys=None):
+def quantize(S, r, flags=0, iters=0, keys=None, rows=None):
     """Split an fp32 state into compensator tokens + smoothed int8 residual.
 
     S: [n, dk, dv], values taken as fp32 (the reconstructed FP32 state of
@@ -205,7 +205,11 @@ def quantize(S, r, flags=0, iters=0, keys=None):
     [n,r,dv]; with DENSE_COMP also comp_key fp32 [n,r,dk] (comp_idx then
     holds the rows the subspace iteration started from).  `keys` (fp32
     [n,r,dk], DENSE_COMP only) replaces the subspace iteration: the split
-    into values, residual and codes is then made with these keys.
+    into values, residual and codes is then made with these keys.  `rows`
+    (int [n,r]) replaces the top-r selection of step 2 by the given rows, in
+    the given order (the extraction is then forced; when two row norms are
+    within rounding of each other, either choice is a correct top-r, and a
+    test forces the oracle to the choice it checks).
     """
     S32 = np.asarray(S, dtype=_F32)
     n, dk, dv = S32.shape
@@ -216,6 +220,11 @@ def quantize(S, r, flags=0, iters=0, keys=None):
     norm2 = np.einsum("nij,nij->ni", S64, S64)
     # 2. top-r rows: descending norm, ties to the lower index (stable sort)
     comp_idx = np.argsort(-norm2, axis=1, kind="stable")[:, :r].astype(np.int32)
+    if rows is not None:
+        comp_idx = np.array(rows, dtype=np.int32).reshape(n, r)
+        if r and (comp_idx.min() < 0 or comp_idx.max() >= dk or
+                  any(len(set(c.tolist())) != r for c in comp_idx)):
+            raise ValueError("rows must be r distinct row indices per state")
     if flags & DENSE_COMP:
         # 3'. dense keys, values w_c = S^T k_c from the fp32 keys, and the
         # residual S - sum_c k_c w_c^T (fp64, rounded once to fp32)

@@ -65,16 +65,12 @@ int check_buffer(const lq_params *prm, const lq_state *st) {
   return LQ_OK;
 }
 
-// The arrays of one state must not overlap one another: a launch that writes
-// the state reads the same arrays (the boundary in the close, the buffer row
-// of the current token in the decode).  `boundary` and `buffer` select the
-// halves the call uses; NULL arrays of a half the call does not use are
-// skipped.
-int check_state_disjoint(const lq_params *prm, const lq_state *st, bool boundary, bool buffer) {
+// Byte ranges of the state's arrays: the boundary half and / or the buffer
+// half; arrays a call does not use give empty ranges.  Returns the count.
+int state_ranges(const lq_params *prm, const lq_state *st, bool boundary, bool buffer, Range *rs) {
   const size_t n = static_cast<size_t>(prm->n), p = static_cast<size_t>(prm->p);
   const size_t r = static_cast<size_t>(prm->r);
   const size_t vec = n * kDim * sizeof(float);
-  Range rs[9];
   int m = 0;
   if (boundary) {
     rs[m++] = span(st->codes, n * kDim * kDim);
@@ -92,10 +88,31 @@ int check_state_disjoint(const lq_params *prm, const lq_state *st, bool boundary
     rs[m++] = span(st->buf_k, n * p * kDim * sizeof(float));
     rs[m++] = span(st->buf_u, n * p * kDim * sizeof(float));
   }
+  return m;
+}
+
+// The arrays of one state must not overlap one another: a launch that writes
+// the state reads the same arrays (the boundary in the close, the buffer row
+// of the current token in the decode).  `boundary` and `buffer` select the
+// halves the call uses.
+int check_state_disjoint(const lq_params *prm, const lq_state *st, bool boundary, bool buffer) {
+  Range rs[9];
+  const int m = state_ranges(prm, st, boundary, buffer, rs);
   for (int i = 0; i < m; ++i)
     for (int j = i + 1; j < m; ++j)
       if (overlap(rs[i], rs[j])) return LQ_ERR_ALIAS;
   return LQ_OK;
+}
+
+// A caller array `x` must not overlap any array of the state: the token
+// calls write records (decode) or the whole boundary (fused close) while
+// their workgroups read the inputs, so any overlap is a race.
+bool overlaps_state(Range x, const lq_params *prm, const lq_state *st, bool boundary, bool buffer) {
+  Range rs[9];
+  const int m = state_ranges(prm, st, boundary, buffer, rs);
+  for (int i = 0; i < m; ++i)
+    if (overlap(x, rs[i])) return true;
+  return false;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_HIP; }
@@ -157,8 +174,9 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
 
 namespace {
 
-// Checks shared by the two token entry points: parameters, state, t, the
-// token inputs, and that o overlaps no input or state array.
+// Checks shared by the token entry points: parameters, state, t, the token
+// inputs, that o overlaps no input, and that no input or o overlaps an array
+// of the state.
 int check_token_call(const lq_params *prm, const lq_state *st, int32_t t, const float *q,
                      const float *k, const float *v, const float *beta, const float *alpha,
                      const float *o) {
@@ -176,19 +194,11 @@ int check_token_call(const lq_params *prm, const lq_state *st, int32_t t, const 
   const size_t n = static_cast<size_t>(prm->n);
   const size_t vec = n * kDim * sizeof(float);
   const Range out = span(o, vec);
-  const size_t gate_elems = kda ? n * prm->p * kDim : n * prm->p;
-  if (overlap(out, span(q, vec)) || overlap(out, span(k, vec)) || overlap(out, span(v, vec)) ||
-      overlap(out, span(beta, n * sizeof(float))) ||
-      overlap(out, span(alpha, kda ? vec : n * sizeof(float))) ||
-      overlap(out, span(st->codes, n * kDim * kDim)) ||
-      overlap(out, span(st->row_scale, vec)) || overlap(out, span(st->col_scale, vec)) ||
-      overlap(out, span(st->buf_gate, gate_elems * sizeof(float))) ||
-      overlap(out, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
-      overlap(out, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
-      (prm->r > 0 && (overlap(out, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(out, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
-      overlap(out, key_span(prm, st)))
-    return LQ_ERR_ALIAS;
+  const Range in[5] = {span(q, vec), span(k, vec), span(v, vec), span(beta, n * sizeof(float)),
+                       span(alpha, kda ? vec : n * sizeof(float))};
+  if (overlaps_state(out, prm, st, true, true)) return LQ_ERR_ALIAS;
+  for (const Range &x : in)
+    if (overlap(out, x) || overlaps_state(x, prm, st, true, true)) return LQ_ERR_ALIAS;
   return LQ_OK;
 }
 
@@ -291,17 +301,7 @@ static int check_slots(const lq_params *prm, const lq_state *st, const int32_t *
   if (!aligned(v, 4)) return LQ_ERR_ALIGN;
   const size_t n = static_cast<size_t>(prm->n);
   const Range in = span(v, n * sizeof(int32_t));
-  const size_t gate_elems = prm->gate == LQ_GATE_KDA ? n * prm->p * kDim : n * prm->p;
-  if ((o && overlap(in, span(o, n * kDim * sizeof(float)))) ||
-      overlap(in, span(st->codes, n * kDim * kDim)) ||
-      overlap(in, span(st->row_scale, n * kDim * sizeof(float))) ||
-      overlap(in, span(st->col_scale, n * kDim * sizeof(float))) ||
-      overlap(in, span(st->buf_gate, gate_elems * sizeof(float))) ||
-      overlap(in, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
-      overlap(in, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
-      (prm->r > 0 && (overlap(in, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(in, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
-      overlap(in, key_span(prm, st)))
+  if ((o && overlap(in, span(o, n * kDim * sizeof(float)))) || overlaps_state(in, prm, st, true, true))
     return LQ_ERR_ALIAS;
   return LQ_OK;
 }
@@ -407,17 +407,8 @@ static int check_list(const lq_params *prm, const lq_state *st, const int32_t *v
   if (!aligned(list, 4)) return LQ_ERR_ALIGN;
   const size_t n = static_cast<size_t>(prm->n);
   const Range in = span(list, static_cast<size_t>(count) * sizeof(int32_t));
-  const size_t gate_elems = prm->gate == LQ_GATE_KDA ? n * prm->p * kDim : n * prm->p;
   if ((o && overlap(in, span(o, n * kDim * sizeof(float)))) || overlap(in, span(v, n * sizeof(int32_t))) ||
-      overlap(in, span(st->codes, n * kDim * kDim)) ||
-      overlap(in, span(st->row_scale, n * kDim * sizeof(float))) ||
-      overlap(in, span(st->col_scale, n * kDim * sizeof(float))) ||
-      overlap(in, span(st->buf_gate, gate_elems * sizeof(float))) ||
-      overlap(in, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
-      overlap(in, span(st->buf_u, n * prm->p * kDim * sizeof(float))) ||
-      (prm->r > 0 && (overlap(in, span(st->comp_idx, n * prm->r * sizeof(int32_t))) ||
-                      overlap(in, span(st->comp_val, n * prm->r * kDim * sizeof(float))))) ||
-      overlap(in, key_span(prm, st)))
+      overlaps_state(in, prm, st, true, true))
     return LQ_ERR_ALIAS;
   return LQ_OK;
 }
@@ -555,16 +546,12 @@ int leapquant_bf16w_decode_step(const lq_params *prm, const void *B, const lq_st
     return LQ_ERR_ALIGN;
   const size_t n = static_cast<size_t>(prm->n);
   const size_t vec = n * kDim * sizeof(float);
-  const Range out = span(o, vec);
-  const size_t gate_elems = kda ? n * prm->p * kDim : n * prm->p;
-  if (overlap(out, span(q, vec)) || overlap(out, span(k, vec)) || overlap(out, span(v, vec)) ||
-      overlap(out, span(beta, n * sizeof(float))) ||
-      overlap(out, span(alpha, kda ? vec : n * sizeof(float))) ||
-      overlap(out, span(B, n * kDim * kDim * 2)) ||
-      overlap(out, span(st->buf_gate, gate_elems * sizeof(float))) ||
-      overlap(out, span(st->buf_k, n * prm->p * kDim * sizeof(float))) ||
-      overlap(out, span(st->buf_u, n * prm->p * kDim * sizeof(float))))
-    return LQ_ERR_ALIAS;
+  const Range out = span(o, vec), bs = span(B, n * kDim * kDim * 2);
+  const Range in[5] = {span(q, vec), span(k, vec), span(v, vec), span(beta, n * sizeof(float)),
+                       span(alpha, kda ? vec : n * sizeof(float))};
+  if (overlap(out, bs) || overlaps_state(out, prm, st, false, true)) return LQ_ERR_ALIAS;
+  for (const Range &x : in)
+    if (overlap(out, x) || overlap(bs, x) || overlaps_state(x, prm, st, false, true)) return LQ_ERR_ALIAS;
   lq::Bf16WinArgs a{};
   a.B = static_cast<uint16_t *>(const_cast<void *>(B));
   a.buf_gate = st->buf_gate;

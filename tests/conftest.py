@@ -9,3 +9,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running check")
+
+
+def pytest_sessionstart(session):
+    # a planted oracle mistake, set only by tests/test_oracle_mutants.py in
+    # the subprocesses it starts
+    name = os.environ.get("LQ_ORACLE_MUTANT")
+    if name:
+        from tests import oracle_mutants
+        oracle_mutants.apply(name)

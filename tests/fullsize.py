@@ -117,7 +117,8 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
     loc_t = [(torch.as_tensor([a for a, _ in lo], device=DEV, dtype=torch.long),
               torch.as_tensor([b for _, b in lo], device=DEV, dtype=torch.long)) for lo in loc]
     diverged = np.zeros(len(free), bool)
-    stats = {"flips": 0, "codes": 0, "ties": 0, "worst_free_rel": 0.0}
+    stats = {"flips": 0, "codes": 0, "ties": 0, "max_half_dist": 0.0, "worst_free_rel": 0.0,
+             "free_ties": 0, "free_parted": []}
     snaps, mse = {}, []
     if checkpoint_every:
         assert checkpoint_every % p == 0 and len(free)
@@ -134,11 +135,13 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
         ws = slice(w * p, (w + 1) * p)
         og = to_np(rec[ws])
         P.assert_close(og[:, :nf], o_f[ws], f"{cfg.name} window {w} forced outputs")
-        _, _, S_end, _ = O.window(b_f[w], tok_f, w * p, p, gate, cfg.r)
+        _, recs, S_end, _ = O.window(b_f[w], tok_f, w * p, p, gate, cfg.r)
         s = P.compare_boundary(_gather_boundary(slab, forced), b_f[w + 1],
-                               S_end.astype(np.float32), cfg.r, f"{cfg.name} boundary {w + 1}")
+                               S_end.astype(np.float32), cfg.r, f"{cfg.name} boundary {w + 1}",
+                               mag=P.rebuild_magnitude(b_f[w], recs))
         for k in ("flips", "codes", "ties"):
             stats[k] += s[k]
+        stats["max_half_dist"] = max(stats["max_half_dist"], s["max_half_dist"])
         if len(free):
             ofr, orr = og[:, nf:], o_r[ws]
             strict = ~diverged
@@ -149,9 +152,24 @@ def run(cfg, n_forced=8, n_free=8, steps=None, seed=None, log=None, checkpoint_e
                 stats["worst_free_rel"] = max(stats["worst_free_rel"], float(rel))
                 assert rel < 2e-2, f"{cfg.name} window {w}: diverged free states differ by {rel}"
             gb = _gather_boundary(slab, free)
+            if strict.any():
+                # free states still on the oracle's trajectory closed this
+                # window from the oracle's boundary: checked strictly, so a
+                # state parts only at a legitimate rounding flip or near tie
+                sel = np.nonzero(strict)[0]
+                _, rr, S_fr, _ = O.window(O.copy_boundary(b_r[w], sel), {k: v[:, sel] for k, v in tok_r.items()},
+                                          w * p, p, gate, cfg.r)
+                sf = P.compare_boundary({k: v[sel] for k, v in gb.items()}, O.copy_boundary(b_r[w + 1], sel),
+                                        S_fr.astype(np.float32), cfg.r, f"{cfg.name} free boundary {w + 1}",
+                                        mag=P.rebuild_magnitude(O.copy_boundary(b_r[w], sel), rr))
+                stats["free_ties"] += sf["ties"]
+                stats["max_half_dist"] = max(stats["max_half_dist"], sf["max_half_dist"])
             same = np.all(gb["codes"] == b_r[w + 1]["codes"], axis=(1, 2))
             if cfg.r:
                 same &= np.all(gb["comp_idx"] == b_r[w + 1]["comp_idx"], axis=1)
+            newly = strict & ~same
+            if newly.any():
+                stats["free_parted"].append((w + 1, int(newly.sum())))
             diverged |= ~same
         tt = (w + 1) * p
         if checkpoint_every and tt % checkpoint_every == 0:

@@ -4,13 +4,19 @@ Tolerances:
   * outputs o_t, buffered u_t, compensator rows, row and column scales:
     |gpu - ref| <= 1e-4 + 1e-3 |ref| elementwise;
   * int8 codes: identical, except entries off by one where the oracle's
-    pre-rounding value lies within HALF_BAND of a half-integer, at most 0.1%
+    pre-rounding value lies within a band of a half-integer, at most 0.1%
     of a slab's codes per boundary (a code at a rounding boundary is decided
     by the last bits of the fp32 rebuilt state, which the GPU sums in a
-    different order);
-  * compensator selection: identical row sets, unless the oracle's r-th and
-    (r+1)-th row norms are a near tie (relative gap < 1e-5), in which case
-    that state's boundary is reported as a tie and checked by invariants;
+    different order).  The band is HALF_BAND plus two measured or bounded
+    terms per code: the shift that the GPU's own row and column scales
+    (compared above) cause at that code, |x| (|da|/a + |ds|/s), and, when
+    the caller passes the magnitudes the fp32 rebuild sums (`mag`), that
+    rebuild's rounding error in code units, REBUILD_EPS mag / (a s);
+  * compensator selection: the GPU's rows must be a top-r of the oracle's
+    norms up to fp32 rounding of those norms (TIE_GAP relative).  Where
+    they differ from the oracle's own choice (a near tie), the oracle is
+    forced to the GPU's rows and the whole boundary is compared against
+    that split under the same rules: no state is left out;
   * dense compensator keys: the leading keys that the fp32 state determines
     (every Gram-Schmidt ratio of the oracle's iteration outside
     (RATIO_DROPPED, RATIO_OK)) within KEY_ATOL; every GPU key unit or zero
@@ -20,13 +26,28 @@ Tolerances:
     rank <= r, whose residual is rounding noise: those must reconstruct the
     state to NOISE_RESIDUAL of its largest entry.
 """
+import json
+import os
+
 import numpy as np
 
 from oracle import leapquant_oracle as O
 
 RTOL, ATOL = 1e-3, 1e-4
 FLIP_FRACTION = 1e-3
-HALF_BAND = 1e-2
+# Distance from a half-integer within which the oracle's fp32 pre-rounding
+# code value may round the other way on the GPU, before the per-code terms
+# below (scale shift, rebuild error) are added.
+HALF_BAND = 1e-3
+# fp32 error of the rebuilt state relative to the magnitudes it sums:
+# Gamma (a product of up to 64 fp32 gates), the dequantized code (two
+# products), the compensator add, the suffix products of the records' key
+# decays (up to 64 factors) and the fp32 MFMA / FMA accumulation over up to
+# 64 + 16 terms, each rounding at 2^-24: below 2^-16 in total.
+REBUILD_EPS = 2.0 ** -16
+# Relative gap within which two fp32 row norms (128 squares summed in a
+# different order) may order two rows differently: the sum of n = 128
+# non-negative terms carries at most (n - 1) 2^-24 = 7.6e-6 relative error.
 TIE_GAP = 1e-5
 # Dense compensator keys (unit vectors), fp32 iteration against fp64: a
 # relative perturbation of S by one ulp moves the oracle's keys by up to
@@ -65,48 +86,93 @@ def assert_close(gpu, ref, what, rtol=RTOL, atol=ATOL):
     return float(np.divide(err, lim, out=np.zeros_like(err), where=lim > 0).max()) if err.size else 0.0
 
 
-def near_tie(S32, r):
-    """Per state: True when two of the oracle's top r + 1 row norms differ,
-    but by less than TIE_GAP relative.  Exactly equal norms are not a near
-    tie: both sides break them by the lower row index."""
+def _log(stats, what):
+    """Append a comparison's statistics to $LQ_PARITY_LOG (JSON lines), if set."""
+    path = os.environ.get("LQ_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"what": what, **stats}) + "\n")
+
+
+def row_norms2(S32):
+    """Squared row norms of fp32 states, fp64 sums of exact fp32 squares."""
     S = np.asarray(S32, np.float32).astype(np.float64)
-    n2 = np.sort(np.einsum("nij,nij->ni", S, S), axis=1)[:, ::-1]
+    return np.einsum("nij,nij->ni", S, S)
+
+
+def check_selection(idx, S32, r, what):
+    """The GPU's compensator rows idx [n, r] must be a top-r selection of the
+    oracle's fp32 state up to fp32 rounding of the row norms: r distinct rows
+    in range, every chosen norm at least (1 - TIE_GAP) times every unchosen
+    one, stored in descending order up to the same gap.  Returns the mask of
+    states whose selection differs from the oracle's own (near ties)."""
+    n2 = row_norms2(S32)
+    n = n2.shape[0]
     if r == 0:
-        return np.zeros(S.shape[0], bool)
-    top = n2[:, :r + 1]
-    gaps = (top[:, :-1] - top[:, 1:]) / np.maximum(top[:, :-1], 1e-300)
-    return ((gaps > 0) & (gaps < 2 * TIE_GAP)).any(axis=1)
+        return np.zeros(n, bool)
+    idx = np.asarray(idx).astype(np.int64)
+    assert idx.shape == (n, r), (what, idx.shape)
+    assert idx.min() >= 0 and idx.max() < n2.shape[1], f"{what}: compensator row out of range"
+    for s in range(n):
+        assert len(set(idx[s].tolist())) == r, f"{what}: state {s} repeats a compensator row"
+    chosen = np.take_along_axis(n2, idx, axis=1)
+    mask = np.ones_like(n2, bool)
+    np.put_along_axis(mask, idx, False, axis=1)
+    rest_max = np.where(mask, n2, -np.inf).max(axis=1)
+    lo = chosen.min(axis=1)
+    bad = lo < (1 - TIE_GAP) * rest_max
+    assert not bad.any(), f"{what}: compensator rows are not a top-{r} in states {np.nonzero(bad)[0][:8]}"
+    dec = chosen[:, 1:] <= chosen[:, :-1] * (1 + TIE_GAP)
+    assert dec.all(), f"{what}: compensator rows not in descending-norm order"
+    own = np.argsort(-n2, axis=1, kind="stable")[:, :r]
+    return ~np.all(idx == own, axis=1)
 
 
-def compare_boundary(gpu, ref, S_ref, r, what, exact=False, band=None):
+def _infer_flags(ref, flags):
+    if flags is not None:
+        return flags
+    return O.NO_SMOOTH if np.all(np.asarray(ref["col_scale"]) == 1) else 0
+
+
+def compare_boundary(gpu, ref, S_ref, r, what, exact=False, band=None, flags=None, mag=None):
     """Compare a GPU boundary state with the oracle's.
 
     gpu, ref: dicts of arrays (codes, row_scale, col_scale, comp_idx,
     comp_val) for the same states; S_ref: the oracle's fp32 state that `ref`
-    quantizes (used to locate rounding boundaries).  exact=True demands
-    bit-identity (both sides quantized the same fp32 input).  band: optional
-    per-code widening of the rounding band (code units), for residuals whose
-    fp32 evaluation error is known to exceed the rebuilt state's.
-    Returns a dict of statistics.
+    quantizes (used to locate rounding boundaries and to re-split near
+    ties).  exact=True demands bit-identity (both sides quantized the same
+    fp32 input).  band: optional per-code widening of the rounding band
+    (code units).  flags: the quantizer flags `ref` was made with (None:
+    NO_SMOOTH when every column scale of `ref` is 1).  mag: optional
+    [n, dk, dv] magnitudes that the GPU's fp32 rebuild of S_ref summed
+    (Gamma |B| + sum_i |K_i| |u_i|), for the rebuild-error term of the band.
+    Every state is compared; states whose GPU rows differ from the oracle's
+    (a near tie, validated by check_selection) are compared against the
+    oracle's split under the GPU's rows.  Returns a dict of statistics,
+    also appended to $LQ_PARITY_LOG.
     """
     n = ref["codes"].shape[0]
-    ties = near_tie(S_ref, r)
-    ok = ~ties
-    stats = {"states": n, "ties": int(ties.sum()), "flips": 0, "codes": 0, "max_half_dist": 0.0}
-    if r:
-        same_sel = np.all(gpu["comp_idx"] == ref["comp_idx"], axis=1)
-        bad = ok & ~same_sel
-        assert not bad.any(), f"{what}: compensator rows differ without a near tie in states {np.nonzero(bad)[0][:8]}"
-    if not ok.any():
-        return stats
-    g = {k: np.asarray(v)[ok] for k, v in gpu.items()}
-    o = {k: np.asarray(v)[ok] for k, v in ref.items()}
+    S_ref = np.asarray(S_ref, np.float32)
+    gpu = {k: np.asarray(v) for k, v in gpu.items()}
+    ref = {k: np.asarray(v) for k, v in ref.items()}
+    ties = check_selection(gpu["comp_idx"], S_ref, r, what)
+    stats = {"states": n, "ties": int(ties.sum()), "flips": 0, "codes": 0, "max_half_dist": 0.0,
+             "max_band_use": 0.0}
+    if ties.any():
+        # the oracle's split of the same fp32 state under the GPU's rows
+        forced = O.quantize(S_ref[ties], r, _infer_flags(ref, flags), rows=gpu["comp_idx"][ties])
+        ref = {k: v.copy() for k, v in ref.items()}
+        for k in forced:
+            ref[k][ties] = forced[k]
+    np.testing.assert_array_equal(gpu["comp_idx"], ref["comp_idx"], err_msg=f"{what}: comp_idx")
     if exact:
         for k in ("codes", "row_scale", "col_scale", "comp_idx", "comp_val", "comp_key"):
-            if k in o:
-                np.testing.assert_array_equal(g[k], o[k], err_msg=f"{what}: {k}")
-        stats["codes"] = int(o["codes"].size)
+            if k in ref:
+                np.testing.assert_array_equal(gpu[k], ref[k], err_msg=f"{what}: {k}")
+        stats["codes"] = int(ref["codes"].size)
+        _log(stats, what)
         return stats
+    g, o = gpu, ref
     if r:
         assert_close(g["comp_val"], o["comp_val"], f"{what}: comp_val")
     assert_close(g["col_scale"], o["col_scale"], f"{what}: col_scale")
@@ -118,30 +184,52 @@ def compare_boundary(gpu, ref, S_ref, r, what, exact=False, band=None):
     stats["flips"] = nflip
     stats["codes"] = int(d.size)
     if nflip:
-        pre = O.prerounding_codes(np.asarray(S_ref)[ok], o)
+        pre = O.prerounding_codes(S_ref, o)
         x = pre[flips].astype(np.float64)
         dist = np.abs(np.abs(x - np.floor(x)) - 0.5)
         stats["max_half_dist"] = float(dist.max())
-        extra = 0.0 if band is None else np.asarray(band)[ok][flips]
-        assert np.all(dist <= HALF_BAND + extra), \
-            f"{what}: code flip away from a rounding boundary (distance {dist.max()})"
+        extra = np.zeros_like(x) if band is None else np.asarray(band, np.float64)[flips]
+        # the GPU's own scales shift every code of a row / column
+        a_g, a_o = g["row_scale"].astype(np.float64), o["row_scale"].astype(np.float64)
+        s_g, s_o = g["col_scale"].astype(np.float64), o["col_scale"].astype(np.float64)
+        ra = np.abs(a_g - a_o) / np.where(a_o > 0, a_o, 1.0)
+        rs = np.abs(s_g - s_o) / np.where(s_o > 0, s_o, 1.0)
+        extra = extra + np.abs(x) * (ra[flips[0], flips[1]] + rs[flips[0], flips[2]])
+        if mag is not None:
+            unit = a_o[flips[0], flips[1]] * s_o[flips[0], flips[2]]
+            m = np.asarray(mag, np.float64)[flips]
+            extra = extra + np.where(unit > 0, REBUILD_EPS * m / np.where(unit > 0, unit, 1.0), 0.0)
+        lim = HALF_BAND + extra
+        stats["max_band_use"] = float((dist / lim).max())
+        assert np.all(dist <= lim), \
+            f"{what}: code flip away from a rounding boundary (distance {dist.max()}, band {lim[np.argmax(dist / lim)]})"
         allowed = FLIP_FRACTION * d.size
         if band is not None:
             # codes whose value lies inside the widened band flip at most
             # with the band's width (uniform fractional parts), 4x margin
-            allowed += 4 * float(np.minimum(0.5, np.asarray(band)[ok]).sum())
+            allowed += 4 * float(np.minimum(0.5, np.asarray(band)).sum())
         assert nflip <= allowed, f"{what}: {nflip} flipped codes of {d.size}"
+    _log(stats, what)
     return stats
 
 
-def key_ratios(S32, r, iters):
+def rebuild_magnitude(boundary, records):
+    """Magnitudes that a rebuild of the state from `boundary` and the window's
+    records sums, |Gamma B| + sum_i |Gamma_p / Gamma_i k~_i| |u_i|: the replay
+    of the records on |B| with |k~| and |u| (decays are non-negative)."""
+    B = np.abs(O.dequantize(boundary))
+    return O.replay(B, [(d, np.abs(kt), np.abs(u)) for d, kt, u in records])
+
+
+def key_ratios(S32, r, iters, rows=None):
     """Gram-Schmidt ratios of the oracle's dense-key iteration: [n, iters, r]
-    (see oracle mgs), for the states S32 started from their top-r rows."""
+    (see oracle mgs), for the states S32 started from their top-r rows (or
+    from `rows` [n, r])."""
     S32 = np.asarray(S32, np.float32)
     out = np.ones((len(S32), iters, r))
     for s in range(len(S32)):
         S64 = S32[s].astype(np.float64)
-        start = np.argsort(-np.einsum("ij,ij->i", S64, S64), kind="stable")[:r]
+        start = np.argsort(-np.einsum("ij,ij->i", S64, S64), kind="stable")[:r] if rows is None else rows[s]
         ratios = []
         O.dense_keys(S64, start, iters, ratios)
         if iters:
@@ -178,20 +266,25 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     band plus that bound; the scales themselves are compared with the
     oracle's.  States of numerical rank <= r, whose residual is rounding
     noise, must reconstruct the state to NOISE_RESIDUAL of its largest entry.
-    Near ties of the starting rows are exempt, as for row extraction.
+    Near ties of the starting rows force the oracle to the GPU's rows, as
+    for row extraction.
     """
     S_ref = np.asarray(S_ref, np.float32)
     S64 = S_ref.astype(np.float64)
     g_all = {k: np.asarray(v) for k, v in gpu.items()}
-    ok = ~near_tie(S_ref, r)
-    ref = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters)
-    stats = {"states": len(S_ref), "ties": int((~ok).sum()), "flips": 0, "codes": 0, "low_rank": 0,
+    # the starting rows are a top-r selection; near ties force the oracle's
+    # iteration to start from the GPU's rows
+    ties = check_selection(g_all["comp_idx"], S_ref, r, what)
+    ok = np.ones(len(S_ref), bool)
+    rows = g_all["comp_idx"] if r else None
+    ref = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters, rows=rows)
+    stats = {"states": len(S_ref), "ties": int(ties.sum()), "flips": 0, "codes": 0, "low_rank": 0,
              "max_excess": 0.0, "keys_compared": 0, "keys_undetermined": 0}
     if r and ok.any():
         np.testing.assert_array_equal(g_all["comp_idx"][ok], ref["comp_idx"][ok], err_msg=f"{what}: start rows")
         # keys the fp32 state determines: against the oracle's; the rest:
         # unit or zero and orthogonal (checked below for every key)
-        rat = key_ratios(S_ref[ok], r, iters)
+        rat = key_ratios(S_ref[ok], r, iters, None if rows is None else rows[ok])
         det = determined_keys(rat)
         mask = np.arange(r)[None, :] < det[:, None]
         assert_close(g_all["comp_key"][ok][mask], ref["comp_key"][ok][mask], f"{what}: comp_key",
@@ -230,6 +323,7 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
         stats["low_rank"] = int(noise.sum())
     keep = ok & ~noise
     if not keep.any():
+        _log(stats, what)
         return stats
     g = {k: v[keep] for k, v in g_all.items()}
     o = {k: np.asarray(v)[keep] for k, v in ref_g.items()}
@@ -259,4 +353,5 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     stats["flips"] = off
     stats["differ_from_oracle_codes"] = int((g["codes"] != o["codes"]).sum())
     stats["codes"] = int(c.size)
+    _log(stats, what)
     return stats

@@ -157,6 +157,21 @@ def test_aliasing_rejected(lib, entry):
     assert lib.leapquant_dequantize_state(ctypes.byref(prm), ctypes.byref(st), st.row_scale, None) == L.LQ_ERR_ALIAS
 
 
+def test_inputs_overlapping_the_state_rejected(lib, entry):
+    """The token calls write records (decode) or the whole boundary (fused
+    close) while they read their inputs: an input inside any state array is
+    a race and is rejected before a launch."""
+    st, _ = _state()
+    prm = _params()
+    assert _decode(lib, prm, st, k=st.buf_k) == L.LQ_ERR_ALIAS             # k over the records
+    assert _decode(lib, prm, st, q=st.codes + 1024) == L.LQ_ERR_ALIAS      # q inside the codes
+    assert _decode(lib, prm, st, v=st.buf_u + 2048) == L.LQ_ERR_ALIAS      # v inside the buffer
+    assert _decode(lib, prm, st, beta=st.buf_gate + 8) == L.LQ_ERR_ALIAS   # beta inside the gates
+    assert _decode(lib, prm, st, alpha=st.row_scale) == L.LQ_ERR_ALIAS     # alpha over the row scales
+    assert _decode(lib, prm, st, q=st.comp_val + 16) == L.LQ_ERR_ALIAS     # q inside the compensators
+    assert _decode(lib, prm, st, beta=st.comp_idx) == L.LQ_ERR_ALIAS       # beta over the row indices
+
+
 def test_overlapping_state_arrays_rejected(lib, entry):
     """Every call that writes the state rejects a state whose own arrays
     overlap (the launch would read what it writes); arrays a call does not
