@@ -719,6 +719,298 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
 }
 
 // ---------------------------------------------------------------------------
+// Window close for windows of at most 16 records with compensator rows
+// (r <= 8): the form every full window of length 16 takes.  Same state
+// layout, split and results as close_kernel; the rebuild's contraction K_w U
+// runs on the bf16 matrix path instead of the fp32 one, which on gfx950
+// occupies the SIMD for 32 cycles per 16x16x4 step and does not overlap the
+// split's vector work.
+//
+// Each fp32 operand x is split into three bf16 parts, x = hi + mid + lo
+// (each part the round-to-nearest-even bf16 of what the previous parts leave;
+// the split is exact), and K_w U is accumulated in fp32 from the six cross
+// products whose size is at least 2^-16 of |K||U|: hh + mh + hm + mm + hl +
+// lh.  The dropped products mid.lo, lo.mid and lo.lo are below 2^-24 of
+// |K_i||U_i| each, the size of one fp32 rounding of the product.  16 records
+// of three parts fill the K = 32 slots of three v_mfma_f32_16x16x32_bf16 per
+// output tile:
+//   [Kh | Km] x [Uh ; Uh],   [Kh | Km] x [Um ; Um],   [Kh | Kl] x [Ul ; Uh]
+// (48 matrix instructions of 16 cycles per wave instead of 64 of 32).
+//
+// Staging: threads 0..127 own key row i = tid: they load k~_j[i] of every
+// record and the gates, fold the decays in registers (K_w[j][i] = rho_j[i]
+// k~_j[i], newest record first, the chain starting at alpha_t for the fused
+// last token) and write the row's parts; threads 128..255 own value column
+// c = tid - 128 and write the parts of u_j[c].  Parts are stored transposed,
+// [row][record] per part, so that each matrix operand is one 16-byte LDS
+// read per lane: lane (i, kb) of an operand holds records 8 (kb & 1) .. +7
+// of row (column) i of the part that k-block kb takes.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float fx2_t __attribute__((ext_vector_type(2)));
+
+// the bf16 pair nearest to (x, y) (ties to even), as one 32-bit word
+__device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
+  const bf16x2_t h = __builtin_convertvector((fx2_t){x, y}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+// three-part split of (x, y): hi, mid, lo pairs; x = hi.x + mid.x + lo.x exactly
+__device__ __forceinline__ void split3(float x, float y, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+  hi = bf16_pair(x, y);
+  x -= __uint_as_float(hi << 16);
+  y -= __uint_as_float(hi & 0xFFFF0000u);
+  mid = bf16_pair(x, y);
+  x -= __uint_as_float(mid << 16);
+  y -= __uint_as_float(mid & 0xFFFF0000u);
+  lo = bf16_pair(x, y);
+}
+
+constexpr int kSplitRecs = 16;  // records per row of a split operand
+
+template <bool KDA, bool FUSED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void close16_kernel(const CloseArgs A) {
+  int slot = blockIdx.x;
+  if (A.slots) {
+    slot = A.slots[blockIdx.x];
+    if ((unsigned)slot >= (unsigned)A.n) return;
+  }
+  const size_t s = slot;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int lr = lane >> 4, lc = lane & 15;
+  const int h = w & 1, ch = w >> 1;
+  const int rbase = 64 * h + 4 * lr;
+  const int col0 = 64 * ch + lc;
+  const int r = A.r, p = A.p;
+  const int len = A.lens ? A.lens[s] : A.len;
+  if (FUSED ? (len < 0 || len >= p) : (len < 1 || len > p)) return;
+  const size_t rec0 = s * p;
+
+  // split operands [part][row or column][record] (bf16); after the
+  // contraction the same space holds the fused decode's partial sums and
+  // the split's column maxima
+  __shared__ __attribute__((aligned(16))) uint16_t sh_kp[3][D][kSplitRecs];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_up[3][D][kSplitRecs];
+  __shared__ __attribute__((aligned(16))) float sh_ag[D];   // a_i * Gamma_i
+  __shared__ __attribute__((aligned(16))) float sh_gam[D];  // Gamma_i
+  __shared__ __attribute__((aligned(16))) float sh_s[D];
+  __shared__ __attribute__((aligned(16))) int sh_cslot[D];
+  __shared__ __attribute__((aligned(16))) float sh_comp[8 * D];
+  __shared__ __attribute__((aligned(16))) float sh_tk[FUSED ? D : 4], sh_tq[FUSED ? D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_tkt[FUSED ? D : 4], sh_tu[FUSED ? D : 4];
+  __shared__ float sh_kq[2];
+  __shared__ float sh_part[2 * D], sh_sig[D];
+  __shared__ __attribute__((aligned(16))) float sh_inv[D];
+  __shared__ __attribute__((aligned(16))) int sh_sel[D];
+  static_assert(sizeof(sh_kp) + sizeof(sh_up) >= 8 * D * sizeof(float2), "scratch for the fused partials");
+
+  // ---- every load first: codes, then the thread's row or column of records
+  const int8_t *csrc = A.codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;
+  uint4 cw[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
+  const bool krow = tid < D;       // waves 0, 1: key row i = tid
+  const int ic = krow ? tid : tid - D;  // row or column index
+  float x[kSplitRecs];
+#pragma unroll
+  for (int j = 0; j < kSplitRecs; ++j) {
+    x[j] = 0.f;
+    if (j < len) x[j] = krow ? A.buf_k[(rec0 + j) * D + ic] : A.buf_u[(rec0 + j) * D + ic];
+  }
+  float g[KDA ? kSplitRecs : 1];
+  float gl = 1.f;  // GDN: lane j holds gate j
+  if (KDA) {
+#pragma unroll
+    for (int j = 0; j < kSplitRecs; ++j) g[j] = (krow && j < len) ? A.buf_gate[(rec0 + j) * D + ic] : 1.f;
+  } else {
+    if (krow && lane < len) gl = A.buf_gate[rec0 + lane];
+  }
+  const float scale = krow ? A.row_scale[s * D + ic] : A.col_scale[s * D + ic];
+  // compensator rows (r <= 8: at most one float4 per thread) and indices
+  float4 cv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < r * (D / 4)) cv = ld4(A.comp_val + s * r * D + 4 * tid);
+  int cidx = -1;
+  if (tid < r) cidx = A.comp_idx[s * r + tid];
+  // FUSED: the last token's k, q (rows), v (columns), beta and alpha
+  float tk = 0.f, tq = 0.f, tv = 0.f, tx = 0.f, ta = 1.f;
+  if (FUSED) {
+    if (krow) {
+      tk = A.k[s * D + ic];
+      tq = A.q[s * D + ic];
+      // beta_t in even lanes, GDN's alpha_t in odd lanes (lane-indexed
+      // vector load, broadcast below); KDA reads alpha_t per row
+      tx = *((lane & 1) ? A.alpha + (KDA ? s * D + ic : s) : A.beta + s);
+      if (KDA) ta = A.alpha[s * D + ic];
+    } else {
+      tv = A.v[s * D + ic];
+    }
+  }
+
+  // ---- decays (key rows), parts, side data to LDS
+  if (tid < D) sh_cslot[tid] = -1;
+  if (krow) {
+    float P = 1.f;
+    if (FUSED) P = KDA ? ta : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 1));
+#pragma unroll
+    for (int j = kSplitRecs - 1; j >= 0; --j) {
+      if (j < len) {
+        x[j] *= P;
+        P *= KDA ? g[j] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), j));
+      }
+    }
+    sh_gam[ic] = P;
+    sh_ag[ic] = scale * P;
+    if (FUSED) {
+      const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 0));
+      sh_tk[ic] = (A.flags & 2u) ? 0.f : tk;  // b_t = 0 without the delta correction
+      sh_tq[ic] = tq;
+      sh_tkt[ic] = tb * tk;
+    }
+  } else {
+    sh_s[ic] = scale;
+    if (FUSED) sh_tu[ic] = tv;  // v_t; replaced by u_t after the decode
+  }
+  {
+    uint32_t ph[8], pm[8], pl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3(x[2 * e], x[2 * e + 1], ph[e], pm[e], pl[e]);
+    uint16_t (*dst)[D][kSplitRecs] = krow ? sh_kp : sh_up;
+    uint4 *d0 = reinterpret_cast<uint4 *>(&dst[0][ic][0]);
+    uint4 *d1 = reinterpret_cast<uint4 *>(&dst[1][ic][0]);
+    uint4 *d2 = reinterpret_cast<uint4 *>(&dst[2][ic][0]);
+    d0[0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+    d0[1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
+    d1[0] = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+    d1[1] = make_uint4(pm[4], pm[5], pm[6], pm[7]);
+    d2[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+    d2[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
+  }
+  if (tid < r * (D / 4)) reinterpret_cast<float4 *>(sh_comp)[tid] = cv;
+  __syncthreads();
+  // comp_idx entries outside [0, dk) are ignored
+  if (tid < r && (unsigned)cidx < (unsigned)D) sh_cslot[cidx] = tid;
+  if (FUSED && tid < D) {
+    const float kq = wave_sum(sh_tkt[tid] * sh_tq[tid]);  // waves 0 and 1, all lanes active
+    if (lane == 0) sh_kq[w] = kq;
+  }
+  __syncthreads();
+
+  // ---- acc = Gamma ((c (a Gamma)) s + compensator rows)
+  floatx4 acc[4][4];
+  {
+    float sv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) sv[ct] = sh_s[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 ag4 = *reinterpret_cast<const float4 *>(sh_ag + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float ag = f4get(ag4, v);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct][v] = (float)(int8_t)(u4get(cw[ct], rt) >> (8 * v)) * (ag * sv[ct]);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int4 cs4 = *reinterpret_cast<const int4 *>(sh_cslot + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = v == 0 ? cs4.x : v == 1 ? cs4.y : v == 2 ? cs4.z : cs4.w;
+        if (c >= 0) {
+          const float G = sh_gam[rbase + 16 * rt + v];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            acc[rt][ct][v] = fmaf(G, sh_comp[c * D + col0 + 16 * ct], acc[rt][ct][v]);
+        }
+      }
+    }
+  }
+
+  // ---- acc += K_w U on the bf16 matrix path (three instructions per tile)
+  {
+    const int kb = lr;                 // k-block of this lane's operand values
+    const int rec = 8 * (kb & 1);      // first record of the block
+    const bool lowk = kb < 2;          // k-blocks 0, 1: first part; 2, 3: second
+    bf16x8_t a1[4], a2[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int row = 64 * h + 16 * rt + lc;
+      a1[rt] = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 1][row][rec]);
+      a2[rt] = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 2][row][rec]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int col = col0 + 16 * ct;
+      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t *>(&sh_up[0][col][rec]);
+      const bf16x8_t b2 = *reinterpret_cast<const bf16x8_t *>(&sh_up[1][col][rec]);
+      const bf16x8_t b3 = *reinterpret_cast<const bf16x8_t *>(&sh_up[lowk ? 2 : 0][col][rec]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b1, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b2, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[rt], b3, acc[rt][ct], 0, 0, 0);
+      }
+    }
+  }
+
+  if (FUSED) {
+    // z = acc^T k_t and acc^T q_t, u_t = v_t - z_b, o_t = z_q + (k~_t . q_t) u_t
+    float zb[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(sh_tk + rbase + 16 * rt);
+      const float4 q4 = *reinterpret_cast<const float4 *>(sh_tq + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          zb[ct] = fmaf(acc[rt][ct][v], f4get(k4, v), zb[ct]);
+          zq[ct] = fmaf(acc[rt][ct][v], f4get(q4, v), zq[ct]);
+        }
+    }
+    __syncthreads();  // every wave is done with the split operands
+    float2 *zp = reinterpret_cast<float2 *>(&sh_kp[0][0][0]);  // [8][D]
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) zp[(4 * h + lr) * D + col0 + 16 * ct] = make_float2(zb[ct], zq[ct]);
+    __syncthreads();
+    if (tid < D) {
+      float b = 0.f, q = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < 8; ++gi) {
+        const float2 z = zp[gi * D + tid];
+        b += z.x;
+        q += z.y;
+      }
+      const float u = sh_tu[tid] - b;
+      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + tid);
+      sh_tu[tid] = u;
+    }
+    __syncthreads();
+    float uu[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) uu[ct] = sh_tu[col0 + 16 * ct];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 kt4 = *reinterpret_cast<const float4 *>(sh_tkt + rbase + 16 * rt);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(f4get(kt4, v), uu[ct], acc[rt][ct][v]);
+    }
+  }
+  // every read of the compensator rows and split operands is done before
+  // the split overwrites them
+  __syncthreads();
+  float *cmx = reinterpret_cast<float *>(&sh_up[0][0][0]);  // [8][D] column-max partials
+  const SplitLds L{sh_part, sh_sel, cmx, sh_sig, sh_inv, nullptr, nullptr, nullptr};
+  split_state<false>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, nullptr, s, r, 0,
+                     A.flags);
+}
+
+// ---------------------------------------------------------------------------
 // Dequantize: S_out = deQ(codes, a, s) + compensator rows (fp32).  Thread
 // (half hh, column j) reads the 64 code bytes of its column segment and
 // writes column j of rows 64hh .. 64hh+63; the row scales and compensator
@@ -781,6 +1073,15 @@ template <bool FUSED>
 hipError_t launch_close(const CloseArgs &a, bool kda, hipStream_t stream) {
   const dim3 grid(a.slots ? a.n_launch : a.n);
   const bool dense = a.comp_key != nullptr;
+  // windows of at most 16 records with at most 8 compensator rows: the
+  // bf16-split contraction (every record count of such a window is <= 16)
+  if (!dense && a.p <= kSplitRecs && a.r <= 8) {
+    if (kda)
+      hipLaunchKernelGGL((close16_kernel<true, FUSED>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((close16_kernel<false, FUSED>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (kda && dense)
     hipLaunchKernelGGL((close_kernel<true, FUSED, true>), grid, dim3(256), 0, stream, a);
   else if (kda)

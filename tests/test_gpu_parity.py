@@ -311,6 +311,7 @@ def test_free_running(name, n, steps, fused):
     out = torch.empty((steps, n, 128), device=DEV)
     diverged = np.zeros(n, bool)
     worst_rel = 0.0
+    on_track = parted = 0
     for w in range(steps // cfg.p):
         run_window(st, tokd, w * cfg.p, cfg.p, out, fused=fused)
         torch.cuda.synchronize()
@@ -338,11 +339,16 @@ def test_free_running(name, n, steps, fused):
         if cfg.r:
             same &= np.all(gb["comp_idx"] == bounds[w + 1]["comp_idx"], axis=1)
         newly = strict & ~same
-        # a flip needs a code within rounding of a half-integer: at most a
-        # few per boundary, so most states stay on the trajectory per window
-        assert newly.sum() <= max(1, n // 4), f"{name} window {w}: {newly.sum()} of {strict.sum()} states parted"
+        on_track += int(strict.sum())
+        parted += int(newly.sum())
         diverged |= ~same
-    print(f"{name}: diverged states {diverged.sum()}/{n}, worst diverged rel err {worst_rel:.2e}")
+    # a state parts at a code within fp32 rounding of a half-integer (a few in
+    # 10^5 codes, each checked above), so over the run most closes of a state
+    # on the trajectory keep it there; a kernel error would flip codes far from
+    # a rounding boundary in every state
+    assert parted <= max(2, on_track // 2), f"{name}: {parted} of {on_track} closes parted a state"
+    print(f"{name}: diverged states {diverged.sum()}/{n} ({parted} of {on_track} closes parted one), "
+          f"worst diverged rel err {worst_rel:.2e}")
 
 
 # ---------------------------------------------------------------------------
@@ -688,3 +694,89 @@ def test_degenerate_tokens(gate, fused):
     o_ref, _, S_end, b_next = O.window(b, t64, 0, p, _gate(gate), r)
     P.assert_close(to_np(out), o_ref, "degenerate outputs")
     P.compare_boundary(boundary_np(st), b_next, S_end.astype(np.float32), r, "degenerate boundary")
+
+
+# ---------------------------------------------------------------------------
+# Near ties in the top-r selection: two rows holding the same values in a
+# different order have the same norm; the fp32 sums on the GPU (in the
+# kernel's order) rank them either way.  Each such state is compared with
+# the oracle forced to the GPU's rows (tests/parity.py), and every case must
+# produce some near ties, so that path is exercised.
+# ---------------------------------------------------------------------------
+def _tie_states(rng, n, r, n_old=0):
+    """States whose r-th and (r+1)-th largest rows (after `n_old` larger
+    rows) are permutations of one vector of wide dynamic range."""
+    S = (0.02 * rng.standard_normal((n, 128, 128))).astype(np.float32)
+    rows = np.zeros((n, n_old + r + 1), np.int64)
+    for s in range(n):
+        perm = rng.permutation(128)
+        rows[s] = perm[:n_old + r + 1]
+        for j in range(n_old):            # distinct, largest
+            S[s, perm[j]] = (30.0 - 0.5 * j) * rng.standard_normal(128)
+        for j in range(r - 1):            # distinct, above the tie
+            S[s, perm[n_old + j]] = (15.0 - 0.25 * j) * rng.standard_normal(128)
+        base = (rng.standard_normal(128) * 10.0 ** rng.uniform(-3, 0, 128)).astype(np.float32)
+        base *= np.float32(40.0 / np.linalg.norm(base))
+        S[s, perm[n_old + r - 1]] = base
+        S[s, perm[n_old + r]] = base[rng.permutation(128)]
+    return S, rows
+
+
+@pytest.mark.parametrize("r", [1, 4, 8, 16])
+def test_quantize_near_tie_rows(r):
+    rng = np.random.default_rng(7100 + r)
+    n = 64
+    S, _ = _tie_states(rng, n, r)
+    st = lq.LeapQuantState(n, 16, r, "gdn", DEV)
+    lq.leapquant_quantize_state(st, _dev(S))
+    torch.cuda.synchronize()
+    stats = P.compare_boundary(boundary_np(st), O.quantize(S, r), S, r, "quantize near ties", exact=True)
+    print(f"r={r}: {stats['ties']} of {n} states ranked the tied rows the other way")
+    assert stats["ties"] > 0, "no near tie was exercised"
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+@pytest.mark.parametrize("r", [4, 8, 16])
+@pytest.mark.parametrize("fused", [False, True])
+def test_close_near_tie_rows(gate, r, fused):
+    """The boundary's compensator rows are erased by the window's records
+    (unit key on the row, u = -w_c, gate 1: the delta rule's exact erase),
+    so the new top r come from the residual, where the tied pair sits."""
+    rng = np.random.default_rng(7200 + 10 * r + 3 * fused + (gate == "kda"))
+    n = 48
+    p = 16 if r < 16 else 32
+    S, rows = _tie_states(rng, n, r, n_old=r)
+    b = O.quantize(S, r, O.NO_SMOOTH)
+    np.testing.assert_array_equal(np.sort(b["comp_idx"], axis=1), np.sort(rows[:, :r], axis=1))
+    kda = gate == "kda"
+    recs = []
+    for c in range(r):
+        kt = np.zeros((n, 128), np.float32)
+        kt[np.arange(n), b["comp_idx"][:, c]] = 1.0
+        a = np.ones((n, 128) if kda else (n,), np.float32)
+        recs.append((a, kt, -b["comp_val"][:, c].astype(np.float32)))
+    st = lq.LeapQuantState(n, p, r, gate, DEV, lq.LQ_NO_SMOOTH)
+    upload_boundary(st, b)
+    _upload_records(st, recs, gate)
+    S_prev = O.replay(O.dequantize(b), _oracle_records(recs, gate))
+    mag_recs = _oracle_records(recs, gate)
+    if fused:
+        tok = _token(rng, n, gate)
+        tok["beta"][:] = 0.0
+        tok["alpha"][:] = 1.0
+        o = torch.empty((n, 128), device=DEV)
+        lq.leapquant_decode_close(st, r, *[_dev(tok[x]) for x in ("q", "k", "v", "beta", "alpha")], o)
+        t64 = {k: v.astype(np.float64) for k, v in tok.items()}
+        o_ref, S_end, rec_t = O.step(S_prev, t64["q"], t64["k"], t64["v"], t64["beta"], t64["alpha"],
+                                     _gate(gate))
+        mag_recs = mag_recs + [rec_t]
+    else:
+        lq.leapquant_window_close(st, r)
+        S_end = S_prev
+    torch.cuda.synchronize()
+    if fused:
+        P.assert_close(to_np(o), o_ref, "o_t")
+    stats = P.compare_boundary(boundary_np(st), O.quantize(S_end, r, O.NO_SMOOTH), S_end.astype(np.float32), r,
+                               "close near ties", flags=O.NO_SMOOTH, mag=P.rebuild_magnitude(b, mag_recs))
+    print(f"{gate} r={r} fused={fused}: {stats['ties']} of {n} states ranked the tied rows the other way")
+    assert stats["ties"] > 0, "no near tie was exercised"
