@@ -140,7 +140,7 @@ def parse():
     ap.add_argument("--ablation-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-states", type=int, default=64)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0)
     return ap.parse_args()
 
 
@@ -572,10 +572,54 @@ def copy_calibration(dev, nbytes=1 << 31, reps=5):
     return gbs
 
 
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_group(job):
+    """One worker's share of the all-core oracle run: free-running decode of
+    its group of states over all tokens (inputs memory-mapped from a .npz
+    written by the parent).  Returns (head-tokens, seconds of compute)."""
+    path, g, p, r, gate, flags, iters, barrier_path = job
+    import numpy as np
+
+    from oracle import leapquant_oracle as O
+    d = np.load(path, mmap_mode="r")
+    S0 = np.array(d[f"S{g}"])
+    tk = {k: np.array(d[f"{k}{g}"]).astype(np.float64) for k in ("q", "k", "v", "beta", "alpha")}
+    # start together: wait until every worker has loaded its inputs
+    open(f"{barrier_path}.{g}", "w").close()
+    while len([f for f in os.listdir(os.path.dirname(barrier_path))
+               if f.startswith(os.path.basename(barrier_path) + ".")]) < int(d["workers"]):
+        time.sleep(0.005)
+    t0 = time.perf_counter()
+    b = O.quantize(S0, r, flags, iters)
+    T = tk["q"].shape[0]
+    for t in range(0, T, p):
+        _, _, _, b = O.window(b, tk, t, p, gate, r, flags, iters=iters)
+    return S0.shape[0] * T, time.perf_counter() - t0
+
+
 def cpu_baseline(args, cfg, S_init, tok, comp_flags=0, iters=0):
-    """The CPU oracle, free-running on a bounded sample of the same inputs:
-    groups of `cpu_sample_states` states of layer 0, each decoded over all
-    tokens, until about `cpu_seconds` of wall time have been spent."""
+    """The CPU oracle, free-running on bounded samples of the same inputs.
+
+    All cores: one worker process per host core (at most 16, the box's share
+    for one GPU), each decoding its own group of `cpu_sample_states` states
+    of layer 0 over all tokens; the rate is the groups' head-tokens over the
+    wall time from the common start to the last worker's end.  One process:
+    groups decoded one after another until about `cpu_seconds` have passed.
+    Inputs are copied to the host before either timed region."""
+    import multiprocessing as mp
+    import tempfile
+
     import numpy as np
     import torch
 
@@ -584,27 +628,70 @@ def cpu_baseline(args, cfg, S_init, tok, comp_flags=0, iters=0):
     ns = min(args.cpu_sample_states, cfg.states_per_layer)
     T = tok["q"].shape[0]
     gate = O.GATE_GDN if cfg.gate == "gdn" else O.GATE_KDA
-    c0, t0 = os.times(), time.perf_counter()
-    head_tokens, groups = 0, 0
-    # groups of ns states of layer 0, each decoded over all tokens
-    while time.perf_counter() - t0 < args.cpu_seconds and (groups + 1) * ns <= cfg.states_per_layer:
-        idx = torch.arange(groups * ns, (groups + 1) * ns, device=S_init.device)
+    flags = O.DENSE_COMP if comp_flags else 0
+
+    def group(gi):
+        idx = torch.arange(gi * ns, (gi + 1) * ns, device=S_init.device)
         S0 = S_init.index_select(0, idx).cpu().numpy()
-        tk = {k: v.index_select(1, idx).cpu().numpy().astype(np.float64) for k, v in tok.items()}
-        flags = O.DENSE_COMP if comp_flags else 0
+        tk = {k: v.index_select(1, idx).cpu().numpy() for k, v in tok.items()}
+        return S0, tk
+
+    # ---- one process
+    t0 = time.perf_counter()
+    head_tokens, groups, busy = 0, 0, 0.0
+    while busy < args.cpu_seconds and (groups + 1) * ns <= cfg.states_per_layer:
+        S0, tk = group(groups)
+        tk = {k: v.astype(np.float64) for k, v in tk.items()}
+        c0 = time.perf_counter()
         b = O.quantize(S0, cfg.r, flags, iters)
-        for t0_ in range(0, T, cfg.p):
-            _, _, _, b = O.window(b, tk, t0_, cfg.p, gate, cfg.r, flags, iters=iters)
+        for t_ in range(0, T, cfg.p):
+            _, _, _, b = O.window(b, tk, t_, cfg.p, gate, cfg.r, flags, iters=iters)
+        busy += time.perf_counter() - c0
         head_tokens += ns * T
         groups += 1
-    wall = time.perf_counter() - t0
-    c1 = os.times()
-    cpu = (c1.user + c1.system) - (c0.user + c0.system)
-    return {"value": round(head_tokens / wall, 1), "unit": UNIT, "cores": max(1, round(cpu / wall)),
-            "kind": "oracle",
-            "sample": f"{groups} groups of {ns} states of layer 0 x {T} tokens, free-running, fp64 numpy "
-                      "(includes copying the sampled inputs to the host)",
-            "wall_s": round(wall, 2), "host_cpus": os.cpu_count()}
+    single = head_tokens / busy
+
+    # ---- all cores: one group per worker, started together
+    workers = max(1, min(16, os.cpu_count() or 1, cfg.states_per_layer // ns))
+    with tempfile.TemporaryDirectory(dir="/dev/shm" if os.path.isdir("/dev/shm") else None) as tmp:
+        path = os.path.join(tmp, "inputs.npz")
+        arrays = {"workers": np.array(workers)}
+        for gi in range(workers):
+            S0, tk = group(gi)
+            arrays[f"S{gi}"] = S0
+            for k, v in tk.items():
+                arrays[f"{k}{gi}"] = v
+        np.savez(path, **arrays)
+        del arrays
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in env:
+            os.environ[k] = "1"  # one thread per worker process
+        try:
+            jobs = [(path, gi, cfg.p, cfg.r, gate, flags, iters, os.path.join(tmp, "ready"))
+                    for gi in range(workers)]
+            ctx = mp.get_context("spawn")
+            w0 = time.perf_counter()
+            with ctx.Pool(workers) as pool:
+                res = pool.map(_oracle_group, jobs)
+            wall_pool = time.perf_counter() - w0
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    total = sum(h for h, _ in res)
+    # every worker started at the common barrier: the slowest one's compute
+    # time is the parallel run's wall time
+    wall = max(sec for _, sec in res)
+    return {"value": round(total / wall, 1), "unit": UNIT, "cores": workers, "kind": "oracle",
+            "sample": f"{workers} groups of {ns} states of layer 0 x {T} tokens, one group per worker process, "
+                      "free-running, fp64 numpy; inputs copied to the host before timing",
+            "wall_s": round(wall, 2),
+            "single_process": {"value": round(single, 1), "unit": UNIT, "cores": 1,
+                               "sample": f"{groups} groups of {ns} states x {T} tokens", "busy_s": round(busy, 2)},
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "total_s": round(time.perf_counter() - t0, 2), "pool_s": round(wall_pool, 2)}
 
 
 if __name__ == "__main__":

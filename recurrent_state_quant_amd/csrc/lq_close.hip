@@ -57,6 +57,28 @@ __device__ __forceinline__ void pack_code(uint32_t &word, float x) {
 __device__ __forceinline__ float f4get(const float4 &x, int i) {
   return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
 }
+
+// Signed byte B of `word` as a float: one SDWA convert (the compiler
+// otherwise extracts the byte with a shift or bit-field extract first).
+template <int B>
+__device__ __forceinline__ float sbyte_to_f32(uint32_t word) {
+  static_assert(B >= 0 && B < 4, "byte index");
+  float r;
+  if (B == 0)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(word));
+  else if (B == 1)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(word));
+  else if (B == 2)
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(word));
+  else
+    asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(word));
+  return r;
+}
+// signed byte v of `word` (v a constant once loops are unrolled)
+__device__ __forceinline__ float sbyte_to_f32(uint32_t word, int v) {
+  return v == 0 ? sbyte_to_f32<0>(word) : v == 1 ? sbyte_to_f32<1>(word) : v == 2 ? sbyte_to_f32<2>(word)
+                                                                        : sbyte_to_f32<3>(word);
+}
 __device__ __forceinline__ uint32_t u4get(const uint4 &x, int i) {
   return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
 }
@@ -341,7 +363,12 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
     float4 iv[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) iv[rt] = *reinterpret_cast<const float4 *>(L.inv + rbase + 16 * rt);
-    int8_t *cdst = codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;  // + 1024 ct
+    // the store offset from a fresh copy of the thread index: derived
+    // values kept live from the kernel's start would cost registers
+    int t2 = threadIdx.x;
+    asm volatile("" : "+v"(t2));
+    const int coff = ((t2 >> 6) & 1) * 8192 + (64 * (t2 >> 7) + (t2 & 15)) * 64 + 16 * ((t2 >> 4) & 3);
+    int8_t *cdst = codes + s * D * D + coff;  // + 1024 ct
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma clang fp contract(off)
@@ -806,7 +833,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   static_assert(sizeof(sh_kp) + sizeof(sh_up) >= 8 * D * sizeof(float2), "scratch for the fused partials");
 
   // ---- every load first: codes, then the thread's row or column of records
-  const int8_t *csrc = A.codes + s * D * D + h * 8192 + col0 * 64 + 16 * lr;
+  // (the lane offset is opaque here so that the split recomputes the store
+  // address instead of keeping this one live across the kernel)
+  int coff = h * 8192 + col0 * 64 + 16 * lr;
+  asm volatile("" : "+v"(coff));
+  const int8_t *csrc = A.codes + s * D * D + coff;
   uint4 cw[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
@@ -909,8 +940,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
       for (int v = 0; v < 4; ++v) {
         const float ag = f4get(ag4, v);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          acc[rt][ct][v] = (float)(int8_t)(u4get(cw[ct], rt) >> (8 * v)) * (ag * sv[ct]);
+        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = sbyte_to_f32(u4get(cw[ct], rt), v) * (ag * sv[ct]);
       }
     }
 #pragma unroll
@@ -934,13 +964,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     const int kb = lr;                 // k-block of this lane's operand values
     const int rec = 8 * (kb & 1);      // first record of the block
     const bool lowk = kb < 2;          // k-blocks 0, 1: first part; 2, 3: second
-    bf16x8_t a1[4], a2[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int row = 64 * h + 16 * rt + lc;
-      a1[rt] = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 1][row][rec]);
-      a2[rt] = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 2][row][rec]);
-    }
+    // operands of one column tile held, the row tiles' reloaded (LDS reads
+    // are cheap here; registers are not)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const int col = col0 + 16 * ct;
@@ -949,9 +974,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
       const bf16x8_t b3 = *reinterpret_cast<const bf16x8_t *>(&sh_up[lowk ? 2 : 0][col][rec]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b1, acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b2, acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[rt], b3, acc[rt][ct], 0, 0, 0);
+        const int row = 64 * h + 16 * rt + lc;
+        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 1][row][rec]);
+        const bf16x8_t a2 = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 2][row][rec]);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b2, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b3, acc[rt][ct], 0, 0, 0);
       }
     }
   }
