@@ -85,6 +85,7 @@ __device__ __forceinline__ uint32_t u4get(const uint4 &x, int i) {
 
 struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
   float *part;       // [2][D] per column half: row norms^2, later row absmax
+                     // (with red: [D], the rows' totals)
   int *sel;          // [D] compensator slot of a row or -1
   float *cmx;        // [8][D] column-max partials
   float *sig;        // [D] 1 / s_j
@@ -93,7 +94,14 @@ struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
   float *dq;         // keys K (row c: k_c)
   float *dw;         // W = K S (row c: w_c)
   float *dy;         // Y = S W^T (row c: column c of Y)
+  // optional [D][kRedRow]: every lane's row partials, reduced by one thread
+  // per row (in place of a DPP reduction chain per row and lane group)
+  float *red;
 };
+// Row stride of the transposed partials: column half ch and lane lc at
+// ch * 16 + lc; 36 puts the four rows 4 apart that one store instruction
+// writes in distinct banks.
+constexpr int kRedRow = 36;
 
 constexpr float kMgsDrop = 1e-3f;  // relative projected norm at or below which a key is dropped
 
@@ -216,7 +224,7 @@ __device__ __forceinline__ void dense_comp_split(floatx4 (&acc)[4][4], const Spl
 // comp_idx, comp_val; with DENSE the dense tokens started from those rows,
 // also comp_key), smoothing scales (col_scale), row scales (row_scale) and
 // int8 codes, all for state s.  Ends with every LDS array consumed.
-template <bool DENSE>
+template <bool DENSE, bool TRED = false>
 __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds &L, int8_t *codes,
                                             float *row_scale, float *col_scale, int32_t *comp_idx,
                                             float *comp_val, float *comp_key, size_t s, int r, int iters,
@@ -227,7 +235,8 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
   const int h = w & 1, ch = w >> 1;
   const int rbase = 64 * h + 4 * lr;  // row of (rt, v) = rbase + 16 rt + v
   const int col0 = 64 * ch + lc;  // column of ct = col0 + 16 ct
-  // ---- a6 row L2 norms (squared, fp32; two column-half partials)
+  // ---- a6 row L2 norms (squared, fp32; two column-half partials, or with
+  // L.red every lane's partials summed by one thread per row)
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -235,9 +244,26 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
       float q = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) q = fmaf(acc[rt][ct][v], acc[rt][ct][v], q);
-      q = row16_sum(q);
-      if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = q;
+      if (TRED) {
+        L.red[(rbase + 16 * rt + v) * kRedRow + 16 * ch + lc] = q;
+      } else {
+        q = row16_sum(q);
+        if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = q;
+      }
     }
+  if (TRED) {
+    __syncthreads();
+    if (tid < D) {
+      const float4 *pr = reinterpret_cast<const float4 *>(L.red + tid * kRedRow);
+      float4 x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = pr[e];
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = (x[e].x + x[e].y) + (x[e].z + x[e].w);
+      L.part[tid] = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    }
+  }
   if (tid < D) L.sel[tid] = -1;
   if (DENSE)
     for (int e = tid; e < r * D; e += 256) L.dq[e] = 0.f;
@@ -245,8 +271,8 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
   if (w == 0 && r > 0) {
     // iterative argmax on wave 0: lane l holds rows 2l and 2l+1; each round
     // takes the largest remaining norm, ties to the lower row index
-    float n0 = L.part[2 * lane] + L.part[D + 2 * lane];
-    float n1 = L.part[2 * lane + 1] + L.part[D + 2 * lane + 1];
+    float n0 = TRED ? L.part[2 * lane] : L.part[2 * lane] + L.part[D + 2 * lane];
+    float n1 = TRED ? L.part[2 * lane + 1] : L.part[2 * lane + 1] + L.part[D + 2 * lane + 1];
     for (int c = 0; c < r; ++c) {
       const bool pick1 = n1 > n0;  // equal norms keep the lower row
       const float best = pick1 ? n1 : n0;
@@ -340,14 +366,29 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
           acc[rt][ct][v] = acc[rt][ct][v] * sig[ct];
           m = fmaxf(m, fabsf(acc[rt][ct][v]));
         }
-        m = row16_max_nn(m);
-        if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = m;
+        if (TRED) {
+          L.red[(rbase + 16 * rt + v) * kRedRow + 16 * ch + lc] = m;
+        } else {
+          m = row16_max_nn(m);
+          if (lc == 0) L.part[ch * D + rbase + 16 * rt + v] = m;
+        }
       }
   }
   __syncthreads();
   if (tid < D) {
     // row scale and its reciprocal, once per row (correctly rounded)
-    const float m = fmaxf(L.part[tid], L.part[D + tid]);
+    float m;
+    if (TRED) {
+      const float4 *pr = reinterpret_cast<const float4 *>(L.red + tid * kRedRow);
+      m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 x = pr[e];
+        m = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+      }
+    } else {
+      m = fmaxf(L.part[tid], L.part[D + tid]);
+    }
     float a = 0.f, inv = 0.f;
     if (m > 0.f && L.sel[tid] < 0) {
       a = m / 127.f;
@@ -402,6 +443,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
   __shared__ __attribute__((aligned(16))) float sh_dq[DENSE ? 16 * D : 4];
   __shared__ __attribute__((aligned(16))) float sh_dw[DENSE ? 16 * D : 4];
   __shared__ __attribute__((aligned(16))) float sh_dy[DENSE ? 16 * D : 4];
+  __shared__ __attribute__((aligned(16))) float sh_red[DENSE ? 4 : D * kRedRow];
   floatx4 acc[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -412,9 +454,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const CloseArgs A) {
       for (int ct = 0; ct < 4; ++ct)
         acc[rt][ct][v] = __builtin_nontemporal_load(A.S_in + (s * D + row) * D + 64 * ch + 16 * ct + lc);
     }
-  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv, sh_dq, sh_dw, sh_dy};
-  split_state<DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s,
-                     A.r, A.iters, A.flags);
+  const SplitLds L{sh_part, sh_sel, sh_cmx, sh_sig, sh_inv, sh_dq, sh_dw, sh_dy, DENSE ? nullptr : sh_red};
+  split_state<DENSE, !DENSE>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, A.comp_key, s,
+                             A.r, A.iters, A.flags);
 }
 
 // ---- a5-a8: window close, one workgroup per state.  With FUSED the
@@ -817,8 +859,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   // split operands [part][row or column][record] (bf16); after the
   // contraction the same space holds the fused decode's partial sums and
   // the split's column maxima
-  __shared__ __attribute__((aligned(16))) uint16_t sh_kp[3][D][kSplitRecs];
-  __shared__ __attribute__((aligned(16))) uint16_t sh_up[3][D][kSplitRecs];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_ops[2][3][D][kSplitRecs];
+  uint16_t (*sh_kp)[D][kSplitRecs] = sh_ops[0];
+  uint16_t (*sh_up)[D][kSplitRecs] = sh_ops[1];
   __shared__ __attribute__((aligned(16))) float sh_ag[D];   // a_i * Gamma_i
   __shared__ __attribute__((aligned(16))) float sh_gam[D];  // Gamma_i
   __shared__ __attribute__((aligned(16))) float sh_s[D];
@@ -830,7 +873,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   __shared__ float sh_part[2 * D], sh_sig[D];
   __shared__ __attribute__((aligned(16))) float sh_inv[D];
   __shared__ __attribute__((aligned(16))) int sh_sel[D];
-  static_assert(sizeof(sh_kp) + sizeof(sh_up) >= 8 * D * sizeof(float2), "scratch for the fused partials");
+  static_assert(sizeof(sh_ops) >= (D * kRedRow + 8 * D) * sizeof(float), "scratch for the split's partials");
 
   // ---- every load first: codes, then the thread's row or column of records
   // (the lane offset is opaque here so that the split recomputes the store
@@ -1032,9 +1075,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
   // every read of the compensator rows and split operands is done before
   // the split overwrites them
   __syncthreads();
-  float *cmx = reinterpret_cast<float *>(&sh_up[0][0][0]);  // [8][D] column-max partials
-  const SplitLds L{sh_part, sh_sel, cmx, sh_sig, sh_inv, nullptr, nullptr, nullptr};
-  split_state<false>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, nullptr, s, r, 0,
+  float *red = reinterpret_cast<float *>(&sh_ops[0][0][0][0]);  // [D][kRedRow] row partials
+  float *cmx = red + D * kRedRow;                                 // [8][D] column-max partials
+  const SplitLds L{sh_part, sh_sel, cmx, sh_sig, sh_inv, nullptr, nullptr, nullptr, red};
+  split_state<false, true>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, nullptr, s, r, 0,
                      A.flags);
 }
 
