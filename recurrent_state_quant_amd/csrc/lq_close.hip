@@ -341,13 +341,19 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) L.cmx[(4 * h + lr) * D + col0 + 16 * ct] = cm[ct];
   __syncthreads();
-  if (tid < D) {
+  // per-column and per-row finishing work: with TRED on waves 2 and 3 (the
+  // row norms and the top-r selection ran on waves 0 and 1), so that every
+  // SIMD gets a share
+  int fin = threadIdx.x;  // a fresh copy: values derived earlier would be kept live
+  asm volatile("" : "+v"(fin));
+  if (TRED) fin -= D;
+  if ((unsigned)fin < (unsigned)D) {
     float m = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) m = fmaxf(m, L.cmx[g * D + tid]);
+    for (int g = 0; g < 8; ++g) m = fmaxf(m, L.cmx[g * D + fin]);
     const float sc = (flags & 1u) ? 1.f : (m > 0.f ? m : 1.f);
-    col_scale[s * D + tid] = sc;
-    L.sig[tid] = 1.f / sc;  // sigma_j, correctly rounded
+    col_scale[s * D + fin] = sc;
+    L.sig[fin] = 1.f / sc;  // sigma_j, correctly rounded
   }
   __syncthreads();
 
@@ -375,11 +381,11 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
       }
   }
   __syncthreads();
-  if (tid < D) {
+  if ((unsigned)fin < (unsigned)D) {
     // row scale and its reciprocal, once per row (correctly rounded)
     float m;
     if (TRED) {
-      const float4 *pr = reinterpret_cast<const float4 *>(L.red + tid * kRedRow);
+      const float4 *pr = reinterpret_cast<const float4 *>(L.red + fin * kRedRow);
       m = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -387,15 +393,15 @@ __device__ __forceinline__ void split_state(floatx4 (&acc)[4][4], const SplitLds
         m = fmaxf(m, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
       }
     } else {
-      m = fmaxf(L.part[tid], L.part[D + tid]);
+      m = fmaxf(L.part[fin], L.part[D + fin]);
     }
     float a = 0.f, inv = 0.f;
-    if (m > 0.f && L.sel[tid] < 0) {
+    if (m > 0.f && L.sel[fin] < 0) {
       a = m / 127.f;
       inv = 127.f / m;
     }
-    row_scale[s * D + tid] = a;
-    L.inv[tid] = inv;
+    row_scale[s * D + fin] = a;
+    L.inv[fin] = inv;
   }
   __syncthreads();
   // codes: rne(q * inv), one v_add_f32 per code (see pack_code); the
@@ -1047,17 +1053,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) zp[(4 * h + lr) * D + col0 + 16 * ct] = make_float2(zb[ct], zq[ct]);
     __syncthreads();
-    if (tid < D) {
+    // the column threads (waves 2, 3); the index is recomputed from a fresh
+    // copy of the thread index rather than kept live from the start
+    int col = threadIdx.x;
+    asm volatile("" : "+v"(col));
+    col -= D;
+    if (col >= 0) {
       float b = 0.f, q = 0.f;
 #pragma unroll
       for (int gi = 0; gi < 8; ++gi) {
-        const float2 z = zp[gi * D + tid];
+        const float2 z = zp[gi * D + col];
         b += z.x;
         q += z.y;
       }
-      const float u = sh_tu[tid] - b;
-      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + tid);
-      sh_tu[tid] = u;
+      const float u = sh_tu[col] - b;
+      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + col);
+      sh_tu[col] = u;
     }
     __syncthreads();
     float uu[4];
