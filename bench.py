@@ -28,6 +28,7 @@ METRIC = "decode head-tokens/s (dk=dv=128, int8 state, p=16) + % of HBM BW roofl
 UNIT = "head-tokens/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def _comp_read(dk, dv, r, dense):
@@ -139,51 +140,30 @@ def parse():
                          "per-window, compensators) and Table 3 (window length p, compensator count r) on this workload")
     ap.add_argument("--ablation-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the short separate-close and KDA-workload runs reported beside the headline")
     ap.add_argument("--cpu-sample-states", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=6.0)
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the states shard across GPUs with no exchange)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def run_schedule(cfg, S_init, tok, T, fused, mode, steps, warmup, dev, comp_flags=0, comp_iters=2):
+    """Time one decode schedule of workload `cfg` over the first T tokens of
+    `tok` (inputs resident in HBM): per step, quantize the initial states,
+    then T / p windows of p tokens x L per-layer launches (fused: p - 1 decode
+    steps and one decode_close per layer; separate: p decode steps per layer
+    and one window close over the whole slab).  HIP events on the launch
+    stream bracket every window's decode launches and its closing launches.
+    Returns the wall time per step and the average launch times."""
     import torch
 
     import recurrent_state_quant_amd as lq
-    from workloads import generators as G
-    from workloads.configs import WORKLOADS
 
-    cfg = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.ablations:
-        print(json.dumps(ablations(args, cfg, dev)), flush=True)
-        return
-    kda = cfg.gate == "kda"
-    T = args.tokens or cfg.steps
-    assert T % cfg.p == 0
-    L, nl = cfg.layers, cfg.states_per_layer
-    n = cfg.n_states
+    L, nl, n = cfg.layers, cfg.states_per_layer, cfg.n_states
     windows = T // cfg.p
-
-    # ---- inputs, resident in HBM (untimed)
-    t_gen = time.time()
-    g = G.make_generator(cfg.seed, dev)
-    S_init = G.initial_state(cfg, n, g, dev)
-    tok = G.token_inputs(cfg, n, T, g, dev)
-    torch.cuda.synchronize()
-    print(f"[bench] generated {n} states x {T} tokens in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
-
     # the layers' states live in one slab: decoded layer by layer through
     # views, quantized and window-closed together in one launch each
-    dense = args.comp == "dense" and cfg.r > 0
-    comp_flags = lq.LQ_DENSE_COMP if dense else 0
-    slab = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, dev, comp_flags, comp_iters=args.comp_iters)
+    slab = lq.LeapQuantState(n, cfg.p, cfg.r, cfg.gate, dev, comp_flags, comp_iters=comp_iters)
     slabs = [slab.view(l * nl, nl) for l in range(L)]
     outs = [torch.empty((nl, cfg.dv), device=dev) for _ in range(L)]
 
@@ -193,7 +173,6 @@ def main():
     def quantize_phase():
         lq.leapquant_quantize_state(slab, S_init)
 
-    fused = args.close == "fused"
     n_steps = cfg.p - 1 if fused else cfg.p  # decode-step launches per layer and window
 
     def token_args(t, l):
@@ -214,7 +193,7 @@ def main():
         else:
             lq.leapquant_window_close(slab, cfg.p)
 
-    if args.mode == "graph":
+    if mode == "graph":
         stream = torch.cuda.Stream(device=dev)
         # one warm eager pass on the capture stream before capturing
         with torch.cuda.stream(stream):
@@ -242,7 +221,6 @@ def main():
         run_q, run_d, run_c = quantize_phase, decode_phase, close_phase
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(windows)]
-    copy_gbs = copy_calibration(dev)
 
     def one_step(record):
         run_q()
@@ -257,39 +235,123 @@ def main():
                 ev[w][2].record(stream)
 
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             one_step(False)
         torch.cuda.synchronize()
         dec_ms = close_ms = 0.0
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             one_step(True)
             torch.cuda.synchronize()   # events are reused per step: read them now
             dec_ms += sum(e[0].elapsed_time(e[1]) for e in ev)
             close_ms += sum(e[1].elapsed_time(e[2]) for e in ev)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    close_launches = L if fused else 1
+    return {"wall_per_step": wall / steps, "value": n * T / (wall / steps),
+            "dec_avg_ms": dec_ms / (steps * windows * n_steps * L),
+            "close_avg_ms": close_ms / (steps * windows * close_launches), "n_steps": n_steps,
+            "close_launches": close_launches}
 
-    ms_per_step = 1e3 * wall / args.steps
-    head_tokens = n * T
-    value = head_tokens / (wall / args.steps)
+
+def context_runs(dev, tokens=256, steps=2, warmup=1):
+    """Short measurements beside the headline (about 10-20 s in all): the
+    headline workload in the separate-close schedule, and the KDA workload
+    (per-channel gates, r = 8) in the fused schedule, each over its first
+    `tokens` tokens.  Reported as head-tokens/s and % of 8 TB/s under each
+    schedule's own byte model."""
+    import torch
+
+    from workloads import generators as G
+    from workloads.configs import WORKLOADS
+
+    out = {}
+    for key, name, fused in (("separate_close", "gdn_b256_h32_4layers", False),
+                             ("kda_h32_b128", "kda_h32_b128", True)):
+        cfg = WORKLOADS[name]
+        kda = cfg.gate == "kda"
+        g = G.make_generator(cfg.seed, dev)
+        S_init = G.initial_state(cfg, cfg.n_states, g, dev)
+        tok = G.token_inputs(cfg, cfg.n_states, tokens, g, dev)
+        r = run_schedule(cfg, S_init, tok, tokens, fused, "graph", steps, warmup, dev)
+        bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, fused)
+        out[key] = {"workload": name, "close": "fused" if fused else "separate", "states": cfg.n_states,
+                    "r": cfg.r, "tokens": tokens, "value": round(r["value"], 1), "unit": UNIT,
+                    "frac": round(r["value"] * bpht / 1e9 / HBM_PEAK_GBS, 4),
+                    "bytes_per_head_token": round(bpht, 1),
+                    "decode_avg_launch_us": round(r["dec_avg_ms"] * 1e3, 2),
+                    "close_avg_launch_us": round(r["close_avg_ms"] * 1e3, 2)}
+        del S_init, tok
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the states shard across GPUs with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import recurrent_state_quant_amd as lq
+    from workloads import generators as G
+    from workloads.configs import WORKLOADS
+
+    cfg = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.ablations:
+        print(json.dumps(ablations(args, cfg, dev)), flush=True)
+        return
+    kda = cfg.gate == "kda"
+    T = args.tokens or cfg.steps
+    assert T % cfg.p == 0
+    L, nl = cfg.layers, cfg.states_per_layer
+    n = cfg.n_states
+
+    # ---- inputs, resident in HBM (untimed)
+    t_gen = time.time()
+    g = G.make_generator(cfg.seed, dev)
+    S_init = G.initial_state(cfg, n, g, dev)
+    tok = G.token_inputs(cfg, n, T, g, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] generated {n} states x {T} tokens in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    dense = args.comp == "dense" and cfg.r > 0
+    comp_flags = lq.LQ_DENSE_COMP if dense else 0
+    fused = args.close == "fused"
+    copy_gbs = copy_calibration(dev)
+    run = run_schedule(cfg, S_init, tok, T, fused, args.mode, args.steps, args.warmup, dev, comp_flags,
+                       args.comp_iters)
+    n_steps = run["n_steps"]
+    ms_per_step = 1e3 * run["wall_per_step"]
+    value = run["value"]
     bpht = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, fused, dense)
     bpht_unfused = bytes_per_head_token(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, dense=dense)
-    n_dec = args.steps * windows * n_steps * L
-    dec_avg_ms = dec_ms / n_dec
+    dec_avg_ms = run["dec_avg_ms"]
     dec_bytes = nl * sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda, dense) for t in range(n_steps)) / n_steps
     dec_gbs = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    close_launches = L if fused else 1          # per window
     close_states = nl if fused else n           # per launch
     close_state_bytes = (fused_bytes(cfg.p - 1, cfg.dk, cfg.dv, cfg.r, kda, dense) if fused
                          else close_bytes(cfg.p, cfg.dk, cfg.dv, cfg.r, kda, dense))
-    close_avg_ms = close_ms / (args.steps * windows * close_launches)
+    close_avg_ms = run["close_avg_ms"]
     close_gbs = close_states * close_state_bytes / (close_avg_ms * 1e-3) / 1e9
-    # issued MFMA flops of the rebuild: 2 dk dv per record slot, the records
-    # (plus dense tokens) padded to a multiple of 4
+    # matrix-path work of the rebuild as issued: windows of up to 16 records
+    # (row compensators, r <= 8) run three bf16 16x16x32 steps per 16 x 16
+    # output tile (the six cross products of a three-part split); other
+    # shapes run fp32 16x16x4 steps over the records padded to a multiple
+    # of 4 (dense tokens add r records)
     slots = (cfg.p - 1 if fused else cfg.p) + (cfg.r if dense else 0)
-    close_flops = close_states * 2 * cfg.dk * cfg.dv * ((slots + 3) // 4 * 4)
-    close_mfma_util = close_flops / (close_avg_ms * 1e-3) / (MFMA_FP32_PEAK_TFLOPS * 1e12)
+    bf16_path = not dense and cfg.p <= 16 and cfg.r <= 8
+    if bf16_path:
+        close_flops = close_states * 64 * 3 * 2 * 16 * 16 * 32
+        mfma_peak, mfma_dtype = MFMA_BF16_PEAK_TFLOPS, "bf16 (three-part split of fp32 operands)"
+    else:
+        close_flops = close_states * 2 * cfg.dk * cfg.dv * ((slots + 3) // 4 * 4)
+        mfma_peak, mfma_dtype = MFMA_FP32_PEAK_TFLOPS, "fp32"
+    close_mfma_util = close_flops / (close_avg_ms * 1e-3) / (mfma_peak * 1e12)
     whole_gbs = value * bpht / 1e9
     traffic = {} if dense else measured_traffic(cfg)
     dkey = "decode_fused" if fused else "decode_separate"
@@ -306,25 +368,30 @@ def main():
                    "layers": L, "states": n, "dk": cfg.dk, "dv": cfg.dv, "p": cfg.p, "r": cfg.r,
                    "tokens": T, "state_storage": "int8 codes + fp32 scales, fp32 compensators",
                    "launch": args.mode, "close": args.close},
+        "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
+                       "bytes_per_head_token": round(bpht, 1),
+                       "unfused_bytes_per_head_token": round(bpht_unfused, 1),
+                       "frac_of_unfused_model": round(value * bpht_unfused / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dec_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": dec_traffic, "bytes_per_launch": round(dec_bytes),
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "window_close": {"kernel": "decode_close (fused)" if fused else "window_close",
                          "avg_launch_us": round(close_avg_ms * 1e3, 2), "achieved_GBs": round(close_gbs, 1),
+                         "frac": round(close_gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": close_states * close_state_bytes,
-                         "states_per_launch": close_states, "launches_per_window": close_launches,
-                         "traffic": close_traffic, "mfma_flops_per_launch": close_flops,
-                         "mfma_util": round(close_mfma_util, 4)},
-        "whole_step": {"algorithmic_GBs": round(whole_gbs, 1), "frac": round(whole_gbs / HBM_PEAK_GBS, 4),
-                       "bytes_per_head_token": round(bpht, 1),
-                       "unfused_bytes_per_head_token": round(bpht_unfused, 1),
-                       "frac_of_unfused_model": round(value * bpht_unfused / 1e9 / HBM_PEAK_GBS, 4)},
+                         "states_per_launch": close_states, "launches_per_window": run["close_launches"],
+                         "traffic": close_traffic, "mfma_dtype": mfma_dtype,
+                         "mfma_flops_per_launch": close_flops, "mfma_util": round(close_mfma_util, 4)},
         "hbm_copy_GBs": round(copy_gbs, 1),
     }
 
     if dense:
         result["config"]["compensators"] = f"dense tokens, {args.comp_iters} subspace iterations"
+    if not args.no_context and args.workload == "gdn_b256_h32_4layers" and not dense and T == cfg.steps:
+        t_ctx = time.perf_counter()
+        result["context"] = context_runs(dev)
+        result["context"]["wall_s"] = round(time.perf_counter() - t_ctx, 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, cfg, S_init, tok, comp_flags, args.comp_iters)
     print(json.dumps(result), flush=True)
