@@ -121,7 +121,7 @@ enum {
  * contraction (K = len + r).  The split finds the keys by comp_iters rounds
  * of subspace iteration on S S^T started from the one-hot keys of the r
  * largest-norm rows: K <- MGS(S S^T K), modified Gram-Schmidt in compensator
- * order, a key whose projected norm is zero or at most 1e-3 of its norm
+ * order, a key whose projected norm is zero or at most 2e-2 of its norm
  * before projection becoming the zero key.  Then w_c = S^T k_c and the
  * residual S - sum_c k_c w_c^T is smoothed and quantized as usual; comp_idx
  * receives the starting rows.  With comp_iters = 0 the keys are the one-hot

@@ -45,7 +45,9 @@ What is computed (all floating point in fp64 unless a step says fp32):
   the compensators): subspace iteration started from the one-hot keys of the
   r largest-norm rows, `iters` rounds of Y = S S^T K, K = MGS(Y) (modified
   Gram-Schmidt in compensator order; a column whose projected norm is at
-  most 1e-3 of its norm before projection, or zero, becomes the zero key).
+  most 2e-2 of its norm before projection, or zero, becomes the zero key: a
+  column kept with less would carry the rounding of S S^T K amplified by
+  more than 50).
   Values w_c = S^T k_c from the fp32 keys, residual R = S - sum_c k_c w_c^T.
   With iters = 0 this is exactly the row extraction above.
 
@@ -81,7 +83,7 @@ NO_SMOOTH = 1  # flag: s_j = 1 (ablation of residual smoothing)
 NO_DELTA = 2   # flag: b_t = 0, so u_t = v_t (the rows of Table 4 without the
                # delta correction: linear attention, RetNet, Mamba2, GLA family)
 DENSE_COMP = 4  # flag: compensator tokens with dense keys (subspace iteration)
-MGS_DROP = 1e-3  # relative projected norm at or below which a key is dropped
+MGS_DROP = 2e-2  # relative projected norm at or below which a key is dropped
 
 _F32 = np.float32
 
@@ -159,13 +161,16 @@ def sequential_exact(S0, tokens, gate, keep_every=0, flags=0):
 # --------------------------------------------------------------------------
 # Quantized boundary state ([EL] Abstract, Figure 4; [TM])
 # --------------------------------------------------------------------------
-def mgs(Y, ratios=None):
+def mgs(Y, ratios=None, keep=None):
     """Modified Gram-Schmidt on the columns of Y [dk, r] (fp64), in column
     order.  A column whose norm after projection is zero or at most MGS_DROP
     times its norm before projection gives a zero column.  If `ratios` is a
     list, the ratio (norm after projection) / (norm before) of every column
     is appended to it (0 for a zero column): a diagnostic only, the result
-    does not depend on it."""
+    does not depend on it.  `keep` ({column: bool}) overrides the decision
+    for the columns it names (a nonzero projected column only): a test
+    forces it where the ratio lies within rounding of the threshold, so
+    either decision is correct."""
     dk, r = Y.shape
     K = np.zeros((dk, r))
     for c in range(r):
@@ -176,27 +181,32 @@ def mgs(Y, ratios=None):
         nv = np.sqrt(v @ v)
         if ratios is not None:
             ratios.append(nv / n0 if n0 > 0 else 0.0)
-        if nv > 0 and nv > MGS_DROP * n0:
+        kept = nv > 0 and nv > MGS_DROP * n0
+        if keep is not None and c in keep and nv > 0:
+            kept = bool(keep[c])
+        if kept:
             K[:, c] = v / nv
     return K
 
 
-def dense_keys(S64, start_rows, iters, ratios=None):
+def dense_keys(S64, start_rows, iters, ratios=None, keep=None):
     """Keys of the dense compensator tokens of one state: subspace iteration
     on S S^T from the one-hot keys of `start_rows` (fp64, [dk, r]).  With a
-    list `ratios`, each round appends its list of MGS ratios (see mgs)."""
+    list `ratios`, each round appends its list of MGS ratios (see mgs).
+    `keep` ({(round, column): bool}) forces keep / drop decisions of mgs."""
     dk = S64.shape[0]
     K = np.zeros((dk, len(start_rows)))
     K[start_rows, np.arange(len(start_rows))] = 1.0
-    for _ in range(iters):
+    for it in range(iters):
         rr = None if ratios is None else []
-        K = mgs(S64 @ (S64.T @ K), rr)
+        kk = None if keep is None else {c: v for (i, c), v in keep.items() if i == it}
+        K = mgs(S64 @ (S64.T @ K), rr, kk)
         if ratios is not None:
             ratios.append(rr)
     return K
 
 
-def quantize(S, r, flags=0, iters=0, keys=None, rows=None):
+def quantize(S, r, flags=0, iters=0, keys=None, rows=None, keep=None):
     """Split an fp32 state into compensator tokens + smoothed int8 residual.
 
     S: [n, dk, dv], values taken as fp32 (the reconstructed FP32 state of
@@ -209,7 +219,9 @@ def quantize(S, r, flags=0, iters=0, keys=None, rows=None):
     (int [n,r]) replaces the top-r selection of step 2 by the given rows, in
     the given order (the extraction is then forced; when two row norms are
     within rounding of each other, either choice is a correct top-r, and a
-    test forces the oracle to the choice it checks).
+    test forces the oracle to the choice it checks).  `keep` (a list of one
+    {(round, column): bool} per state, DENSE_COMP only) forces keep / drop
+    decisions of the key iteration in the same way (see mgs).
     """
     S32 = np.asarray(S, dtype=_F32)
     n, dk, dv = S32.shape
@@ -235,7 +247,8 @@ def quantize(S, r, flags=0, iters=0, keys=None, rows=None):
             if keys is not None:
                 K32 = np.asarray(keys[s], _F32).T
             else:
-                K32 = dense_keys(S64[s], comp_idx[s], iters).astype(_F32)
+                K32 = dense_keys(S64[s], comp_idx[s], iters,
+                                 keep=None if keep is None else keep[s]).astype(_F32)
             K = K32.astype(np.float64)
             W32 = (K.T @ S64[s]).astype(_F32)
             comp_key[s] = K32.T

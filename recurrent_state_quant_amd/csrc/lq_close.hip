@@ -103,7 +103,7 @@ struct SplitLds {    // LDS used by the split (a6-a8), shared by both kernels
 // writes in distinct banks.
 constexpr int kRedRow = 36;
 
-constexpr float kMgsDrop = 1e-3f;  // relative projected norm at or below which a key is dropped
+constexpr float kMgsDrop = 2e-2f;  // relative projected norm at or below which a key is dropped
 
 // Dense compensator tokens of the state in acc (r >= 1), after the top-r
 // rows have set one-hot keys in L.dq: `iters` rounds of subspace iteration

@@ -36,11 +36,11 @@ MUTANTS = {
     # windows ([EL] Figure 2)
     "window_one_token_long": ("run_windowed", "length = min(p, T - t0)", "length = min(p + 1, T - t0)"),
     # dense compensator tokens (second reading of [EL] Figure 4)
-    "iteration_on_wrong_side": ("dense_keys", "K = mgs(S64 @ (S64.T @ K), rr)", "K = mgs(S64.T @ (S64 @ K), rr)"),
+    "iteration_on_wrong_side": ("dense_keys", "K = mgs(S64 @ (S64.T @ K), rr, kk)", "K = mgs(S64.T @ (S64 @ K), rr, kk)"),
     "keys_not_normalized": ("mgs", "K[:, c] = v / nv", "K[:, c] = v"),
     "keys_not_projected": ("mgs", "v = v - (K[:, c2] @ v) * K[:, c2]", "v = v"),
-    "no_drop_threshold": ("mgs", "if nv > 0 and nv > MGS_DROP * n0:", "if nv > 0:"),
-    "one_iteration_too_many": ("dense_keys", "for _ in range(iters):", "for _ in range(iters + 1):"),
+    "no_drop_threshold": ("mgs", "kept = nv > 0 and nv > MGS_DROP * n0", "kept = nv > 0"),
+    "one_iteration_too_many": ("dense_keys", "for it in range(iters):", "for it in range(iters + 1):"),
     "values_from_rows": ("quantize", "W32 = (K.T @ S64[s])", "W32 = (K.T @ S64[s].T)"),
     "residual_sign": ("quantize", "R[s] = (S64[s] - K @ W32", "R[s] = (S64[s] + K @ W32"),
     "residual_outer_transposed": ("quantize", "R[s] = (S64[s] - K @ W32.astype(np.float64))",

@@ -17,14 +17,16 @@ Tolerances:
     they differ from the oracle's own choice (a near tie), the oracle is
     forced to the GPU's rows and the whole boundary is compared against
     that split under the same rules: no state is left out;
-  * dense compensator keys: the leading keys that the fp32 state determines
-    (every Gram-Schmidt ratio of the oracle's iteration outside
-    (RATIO_DROPPED, RATIO_OK)) within KEY_ATOL; every GPU key unit or zero
-    and orthogonal to the others within a bound scaled by the keys'
-    conditioning; the rest of a dense boundary is compared with the
-    oracle's split under the GPU's keys, except for states of numerical
-    rank <= r, whose residual is rounding noise: those must reconstruct the
-    state to NOISE_RESIDUAL of its largest entry.
+  * dense compensator keys: every key within KEY_ATOL of the oracle's.  A
+    key is kept only if its Gram-Schmidt ratio exceeds the drop threshold
+    (2e-2), which bounds the amplification of fp32 rounding; a keep / drop
+    decision may differ only where the oracle's ratio lies within
+    DECISION_BAND of the threshold, and the oracle is then forced to the
+    GPU's decision.  Every GPU key is unit or zero and orthogonal to the
+    others; the rest of a dense boundary is compared with the oracle's
+    split under the GPU's keys, except for states of numerical rank <= r,
+    whose residual is rounding noise: those must reconstruct the state to
+    NOISE_RESIDUAL of its largest entry.
 """
 import json
 import os
@@ -52,22 +54,19 @@ TIE_GAP = 1e-5
 # Dense compensator keys (unit vectors), fp32 iteration against fp64: a
 # relative perturbation of S by one ulp moves the oracle's keys by up to
 # ~2.5e-6 (r = 16, the last keys in the noise bulk, measured); the fp32
-# products and Gram-Schmidt sums amount to tens of ulps.  An algorithmic
-# mistake moves keys by O(0.1).
+# products and Gram-Schmidt sums amount to tens of ulps, amplified at most
+# 1 / MGS_DROP = 50-fold in a kept key (simulated fp32 iterations: below
+# 1e-5).  An algorithmic mistake moves keys by O(0.1).
 KEY_ATOL = 1e-3
 NOISE_RESIDUAL = 1e-4  # residual / state magnitude below which a dense split is rank-exhausted
-# A Gram-Schmidt step that leaves a fraction rho of a column's norm amplifies
-# the error of that column by 1/rho.  The fp32 evaluation of S S^T K carries
-# up to about 1.5e-5 of |S S^T k| (two 128-term sums); below RATIO_OK that
-# error can exceed KEY_ATOL in the normalized key, and later keys inherit it
-# through their projections.  Columns below RATIO_DROPPED (a tenth of the
-# drop threshold) are dropped on both sides with margin.
-RATIO_OK = 2e-2
-RATIO_DROPPED = 1e-4
-# Loss of orthogonality between the GPU's nonzero keys c < d: the same
-# error, amplified by 1 / (the smallest ratio, at least the drop threshold,
-# among the kept keys 0..d, which key d was projected against), with a
-# floor for well-conditioned keys.
+# A keep / drop decision is taken in fp32 on the GPU: the ratio carries an
+# absolute error of about 1e-5 (1.5e-5 of |S S^T k| through the projected
+# norm), i.e. 5e-4 of the threshold; decisions whose oracle ratio lies within
+# this relative band of the threshold may go either way.
+DECISION_BAND = 1e-2
+# Loss of orthogonality between the GPU's nonzero keys: the same error,
+# amplified by 1 / (the smallest ratio among the kept keys a key was
+# projected against, at least the drop threshold), with a floor.
 KEY_ORTHO_EPS = 1.5e-5
 KEY_ORTHO_FLOOR = 1e-4
 
@@ -221,40 +220,47 @@ def rebuild_magnitude(boundary, records):
     return O.replay(B, [(d, np.abs(kt), np.abs(u)) for d, kt, u in records])
 
 
-def key_ratios(S32, r, iters, rows=None):
-    """Gram-Schmidt ratios of the oracle's dense-key iteration: [n, iters, r]
-    (see oracle mgs), for the states S32 started from their top-r rows (or
-    from `rows` [n, r])."""
-    S32 = np.asarray(S32, np.float32)
-    out = np.ones((len(S32), iters, r))
-    for s in range(len(S32)):
-        S64 = S32[s].astype(np.float64)
-        start = np.argsort(-np.einsum("ij,ij->i", S64, S64), kind="stable")[:r] if rows is None else rows[s]
-        ratios = []
-        O.dense_keys(S64, start, iters, ratios)
-        if iters:
-            out[s] = np.array(ratios)
-    return out
+def oracle_keys(S32, rows, iters, keep=None):
+    """The oracle's keys [r, dk] and Gram-Schmidt ratios [iters, r] of one
+    state started from `rows`, with keep / drop decisions forced by `keep`
+    ({(round, key): bool})."""
+    ratios = []
+    K = O.dense_keys(np.asarray(S32, np.float32).astype(np.float64), rows, iters, ratios, keep)
+    return K.T, (np.array(ratios) if iters else np.ones((0, len(rows))))
 
 
-def determined_keys(ratios):
-    """Per state, the number of leading dense keys that the fp32 state
-    determines to KEY_ATOL: keys up to the first one whose ratio, in any
-    round, lies between RATIO_DROPPED and RATIO_OK (key c depends only on
-    keys 0..c of this and earlier rounds)."""
-    bad = ((ratios > RATIO_DROPPED) & (ratios < RATIO_OK)).any(axis=1)  # [n, r]
-    r = ratios.shape[2]
-    return np.where(bad.any(axis=1), bad.argmax(axis=1), r)
+def match_decisions(K_gpu, S32, rows, iters, what):
+    """Force the oracle's keep / drop decisions to the GPU's where the GPU
+    kept a key the oracle dropped, or dropped one it kept; each such
+    decision must sit within DECISION_BAND of the threshold in some round.
+    Returns (forced decisions, oracle keys, ratios)."""
+    r = len(rows)
+    nz_g = np.linalg.norm(np.asarray(K_gpu, np.float64), axis=1) > 0.5
+    keep = {}
+    for _ in range(r + 1):
+        K, rat = oracle_keys(S32, rows, iters, keep)
+        nz_o = np.linalg.norm(K, axis=1) > 0.5
+        diff = np.nonzero(nz_o != nz_g)[0]
+        if not len(diff):
+            return keep, K, rat
+        c = int(diff[0])
+        near = [it for it in range(iters)
+                if rat[it, c] > 0 and abs(rat[it, c] / O.MGS_DROP - 1) <= DECISION_BAND and (it, c) not in keep]
+        assert near, (f"{what}: GPU {'kept' if nz_g[c] else 'dropped'} key {c} away from the threshold "
+                      f"(oracle ratios {rat[:, c]})")
+        keep[(near[0], c)] = bool(nz_g[c])
+    raise AssertionError(f"{what}: keep / drop decisions do not settle")
 
 
 def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     """Dense compensator tokens.
 
     The keys come from an fp32 iteration on the GPU and an fp64 one in the
-    oracle.  A key that survives a Gram-Schmidt step with a small fraction
-    of its norm carries the fp32 error amplified by the inverse of that
-    fraction, and so do the keys after it; the leading keys up to the first
-    such one agree to KEY_ATOL and are compared, every GPU key is checked
+    oracle.  A key that survives a Gram-Schmidt step with a fraction rho of
+    its norm carries the fp32 error amplified by 1 / rho; keys are kept only
+    with rho above the drop threshold, so every key agrees to KEY_ATOL and
+    is compared, after forcing the oracle's keep / drop decisions that lie
+    within rounding of the threshold to the GPU's.  Every GPU key is checked
     for unit norm (or zero) and orthogonality to the others.  Given the
     keys, the values follow.
     The residual S - sum_c k_c w_c^T is evaluated in fp32 on the GPU; in rows
@@ -272,37 +278,37 @@ def compare_dense_boundary(gpu, S_ref, r, iters, flags, what):
     S_ref = np.asarray(S_ref, np.float32)
     S64 = S_ref.astype(np.float64)
     g_all = {k: np.asarray(v) for k, v in gpu.items()}
+    n = len(S_ref)
     # the starting rows are a top-r selection; near ties force the oracle's
     # iteration to start from the GPU's rows
     ties = check_selection(g_all["comp_idx"], S_ref, r, what)
-    ok = np.ones(len(S_ref), bool)
-    rows = g_all["comp_idx"] if r else None
-    ref = O.quantize(S_ref, r, flags | O.DENSE_COMP, iters, rows=rows)
-    stats = {"states": len(S_ref), "ties": int(ties.sum()), "flips": 0, "codes": 0, "low_rank": 0,
-             "max_excess": 0.0, "keys_compared": 0, "keys_undetermined": 0}
+    ok = np.ones(n, bool)
+    stats = {"states": n, "ties": int(ties.sum()), "flips": 0, "codes": 0, "low_rank": 0,
+             "max_excess": 0.0, "keys_compared": 0, "decisions_forced": 0, "max_key_err": 0.0}
     if r and ok.any():
-        np.testing.assert_array_equal(g_all["comp_idx"][ok], ref["comp_idx"][ok], err_msg=f"{what}: start rows")
-        # keys the fp32 state determines: against the oracle's; the rest:
-        # unit or zero and orthogonal (checked below for every key)
-        rat = key_ratios(S_ref[ok], r, iters, None if rows is None else rows[ok])
-        det = determined_keys(rat)
-        mask = np.arange(r)[None, :] < det[:, None]
-        assert_close(g_all["comp_key"][ok][mask], ref["comp_key"][ok][mask], f"{what}: comp_key",
-                     rtol=0, atol=KEY_ATOL)
-        stats["keys_compared"] = int(mask.sum())
-        stats["keys_undetermined"] = int((~mask).sum())
-        Kg = g_all["comp_key"][ok].astype(np.float64)
+        # every key against the oracle's, with keep / drop decisions at the
+        # threshold forced to the GPU's
+        Ko = np.zeros((n, r, 128))
+        rat = np.ones((n, iters, r))
+        for s_ in range(n):
+            keep, Ko[s_], rat[s_] = match_decisions(g_all["comp_key"][s_], S_ref[s_], g_all["comp_idx"][s_],
+                                                    iters, f"{what} state {s_}")
+            stats["decisions_forced"] += len(keep)
+        Kg = g_all["comp_key"].astype(np.float64)
+        assert_close(Kg, Ko.astype(np.float32), f"{what}: comp_key", rtol=0, atol=KEY_ATOL)
+        stats["keys_compared"] = int(n * r)
+        stats["max_key_err"] = float(np.abs(Kg - Ko.astype(np.float32)).max())
         G = np.einsum("nci,ndi->ncd", Kg, Kg)
         nz = np.linalg.norm(Kg, axis=2) > 0.5
         both = nz[:, :, None] & nz[:, None, :]
         dev = np.abs(G - np.eye(r)[None])
         if iters:
-            # per key, its smallest ratio over the rounds in which it was kept
-            kept = rat > RATIO_DROPPED
-            rk = np.where(kept, np.maximum(rat, O.MGS_DROP), 1.0).min(axis=1)
+            # per key, its smallest ratio over the rounds (at least the
+            # threshold: a kept key's ratio is above it up to the band)
+            rk = np.where(nz, np.maximum(rat, O.MGS_DROP * (1 - DECISION_BAND)).min(axis=1), 1.0)
             cum = np.minimum.accumulate(rk, axis=1)          # over keys 0..d
         else:
-            cum = np.ones((len(Kg), r))
+            cum = np.ones((n, r))
         later = np.maximum(np.arange(r)[:, None], np.arange(r)[None, :])
         tol = np.maximum(KEY_ORTHO_FLOOR, KEY_ORTHO_EPS / cum[:, later])
         if not np.all(dev[both] <= tol[both]):

@@ -55,7 +55,10 @@ def test_keys_orthonormal_and_residual_orthogonal(r, iters):
     b = O.quantize(S, r, DENSE, iters=iters)
     for s in range(4):
         K = b["comp_key"][s].astype(np.float64)          # [r, dk]
-        np.testing.assert_allclose(K @ K.T, np.eye(r), atol=2e-6)
+        # kept keys orthonormal, dropped keys exactly zero
+        kept = np.linalg.norm(K, axis=1) > 0.5
+        assert kept[0] and np.all(K[~kept] == 0)
+        np.testing.assert_allclose(K @ K.T, np.diag(kept.astype(np.float64)), atol=2e-6)
         W = b["comp_val"][s].astype(np.float64)
         S64 = S[s].astype(np.float64)
         np.testing.assert_allclose(W, K @ S64, rtol=1e-6, atol=1e-6 * np.abs(S64).max())
