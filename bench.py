@@ -87,7 +87,8 @@ def bytes_per_head_token(p, dk, dv, r, kda, fused=False, dense=False):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gdn_b256_4layers.txt")
 KERNEL_SRCS = [os.path.join(ROOT, "recurrent_state_quant_amd", "csrc", f)
-               for f in ("lq_device.h", "lq_decode.hip", "lq_close.hip", "lq_baselines.hip")]
+               for f in ("lq_device.h", "lq_decode_one.h", "lq_decode_body.inc", "lq_close16_body.inc",
+                         "lq_decode.hip", "lq_close.hip", "lq_baselines.hip")]
 
 
 def kernel_source_sha256():
@@ -139,6 +140,8 @@ def parse():
                          "analogues of the pages' Table 2 (per-step fp32 / bf16 / int8 baselines, "
                          "per-window, compensators) and Table 3 (window length p, compensator count r) on this workload")
     ap.add_argument("--ablation-tokens", type=int, default=64)
+    ap.add_argument("--ablation-set", choices=("all", "continuous_batching"), default="all",
+                    help="with --ablations: every table, or only the continuous-batching one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the short separate-close and KDA-workload runs reported beside the headline")
@@ -501,7 +504,7 @@ def ablations(args, cfg, dev, reps=3):
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True,
                                            dense=bool(flags & lq.LQ_DENSE_COMP) and r > 0)
 
-    def slots(p, r, compact=False):
+    def slots(p, r, compact=False, mixed=False, grouped=False):
         # continuous batching: every slot has its own window phase (seeded,
         # uniform), so about 1/p of the slots close at every token; the
         # positions live on the device.  (Phases strided by a multiple of 8
@@ -511,7 +514,13 @@ def ablations(args, cfg, dev, reps=3):
         lq.leapquant_quantize_state(slab, S_init)
         views = [slab.view(l * nl, nl) for l in range(L)]
         gp = torch.Generator(device=dev).manual_seed(cfg.seed + 1)
-        phase = torch.randint(0, p, (nl,), generator=gp, device=dev, dtype=torch.int32)
+        if grouped:
+            # four consecutive slots share a phase (a decode workgroup's four
+            # waves then decode at one window position)
+            phase = torch.randint(0, p, ((nl + 3) // 4,), generator=gp, device=dev,
+                                  dtype=torch.int32).repeat_interleave(4)[:nl]
+        else:
+            phase = torch.randint(0, p, (nl,), generator=gp, device=dev, dtype=torch.int32)
         pos = [(phase + t) % p for t in range(T)]
         step_pos = [torch.where(x == p - 1, -1, x).to(torch.int32) for x in pos]
         close_pos = [torch.where(x == p - 1, x, -1).to(torch.int32) for x in pos]
@@ -521,6 +530,9 @@ def ablations(args, cfg, dev, reps=3):
         def run():
             for t in range(T):
                 for l in range(L):
+                    if mixed:
+                        lq.leapquant_decode_step_close_list(views[l], pos[t], close_list[t], *targs(t, l))
+                        continue
                     lq.leapquant_decode_step_slots(views[l], step_pos[t], *targs(t, l))
                     if compact:
                         lq.leapquant_decode_close_list(views[l], pos[t], close_list[t], *targs(t, l))
@@ -554,11 +566,19 @@ def ablations(args, cfg, dev, reps=3):
     rows_cb = [("lockstep windows (all slots at the same position)", lambda: windowed(cfg.p, cfg.r, 0)),
                ("continuous batching (slot phases spread over the window)", lambda: slots(cfg.p, cfg.r)),
                ("continuous batching, closes launched for the closing slots only (slot list)",
-                lambda: slots(cfg.p, cfg.r, compact=True))]
+                lambda: slots(cfg.p, cfg.r, compact=True)),
+               ("continuous batching, one launch per token (closing slots' workgroups spread among the decode steps)",
+                lambda: slots(cfg.p, cfg.r, mixed=True)),
+               ("continuous batching, one launch per token, four consecutive slots sharing a phase",
+                lambda: slots(cfg.p, cfg.r, mixed=True, grouped=True))]
     DC = lq.LQ_DENSE_COMP
     rows_dc = [("row compensators", lambda: windowed(cfg.p, cfg.r, 0))] + \
         [(f"dense tokens, {i} subspace iteration{'s' if i != 1 else ''}", (lambda i=i: windowed(cfg.p, cfg.r, DC, i)))
          for i in (0, 1, 2)]
+    if args.ablation_set == "continuous_batching":
+        tcb, _ = table(rows_cb, None)
+        return {"metric": "continuous batching throughput (head-tokens/s; ratio to lockstep windows)",
+                "workload": cfg.name, "tokens": T, "reps": reps, "launch": "graph", "continuous_batching": tcb}
     t2, ref = table(rows2, None)
     t3, _ = table(rows3, ref)
     t3r, _ = table(rows3r, ref)

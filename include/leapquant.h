@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define LEAPQUANT_ABI_VERSION 4
+#define LEAPQUANT_ABI_VERSION 5
 
 typedef enum lq_status {
   LQ_OK = 0,
@@ -264,6 +264,27 @@ int leapquant_decode_close_list(const lq_params *prm, const lq_state *st, const 
                                 const float *alpha, float *o, hipStream_t stream);
 int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const int32_t *len,
                                 const int32_t *list, int32_t count, hipStream_t stream);
+
+/* One continuous-batching token in one launch ([EL] Figure 2: each slot
+ * decodes against its fixed boundary state and closes its own window after
+ * its p-th token).  Slot s with 0 <= pos[s] < p - 1 decodes its token
+ * exactly as leapquant_decode_step_slots does; listed slot s with
+ * pos[s] == p - 1 decodes its token and closes its window exactly as
+ * leapquant_decode_close_list does.  Slots at position p - 1 that are not
+ * listed, listed slots at any other position, ids outside [0, n) and slots
+ * outside [0, p) are left as they are.  The result equals
+ * leapquant_decode_step_slots over the positions with p - 1 replaced by -1
+ * followed by leapquant_decode_close_list over the listed slots at p - 1,
+ * bit for bit.  For slabs of more than 4,096 slots with p <= 16 and at
+ * most 8 compensator rows (no dense compensator tokens) it is a single
+ * launch: the closing slots' workgroups run among the decode steps, which
+ * keep memory busy around them, so the closes no longer cost a launch of
+ * their own; other shapes run the two launches.  Arguments, list rules
+ * and error codes are those of leapquant_decode_close_list. */
+int leapquant_decode_step_close_list(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                     const int32_t *list, int32_t count, const float *q,
+                                     const float *k, const float *v, const float *beta,
+                                     const float *alpha, float *o, hipStream_t stream);
 
 /* ---- Uncompressed baselines ([EL] Table 2, rows "FP32 per-step" and
  * "BF16 per-step"): the same token update on a dense state that is read

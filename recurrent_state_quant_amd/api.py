@@ -273,6 +273,21 @@ def leapquant_decode_close_list(state, pos, slots, q, k, v, beta, alpha, o, stre
                                                      _stream(stream, state.device)))
 
 
+def leapquant_decode_step_close_list(state, pos, slots, q, k, v, beta, alpha, o, stream=None):
+    """One continuous-batching token in one launch: slots at positions
+    0 .. p-2 decode their token (as leapquant_decode_step_slots), listed
+    slots at position p-1 decode their token and close their window (as
+    leapquant_decode_close_list); slots is an int32 tensor of distinct slot
+    ids on the device."""
+    args = _token_args(state, q, k, v, beta, alpha, o)
+    lp, count = _list_ptr(slots, state)
+    prm, st = state.params(), state.ptrs()
+    with torch.cuda.device(state.device):
+        L.check(L.load().leapquant_decode_step_close_list(ctypes.byref(prm), ctypes.byref(st),
+                                                          _slots_ptr(pos, state, "pos"), lp, int(count), *args,
+                                                          _stream(stream, state.device)))
+
+
 def leapquant_window_close_list(state, lengths, slots, stream=None):
     """Window close of the listed slots only (distinct int32 slot ids on
     the device); slot s is closed with lengths[s] records as in

@@ -450,6 +450,71 @@ int leapquant_decode_close_list(const lq_params *prm, const lq_state *st, const 
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
+int leapquant_decode_step_close_list(const lq_params *prm, const lq_state *st, const int32_t *pos,
+                                     const int32_t *list, int32_t count, const float *q, const float *k,
+                                     const float *v, const float *beta, const float *alpha, float *o,
+                                     hipStream_t stream) {
+  int rc = check_token_call(prm, st, 0, q, k, v, beta, alpha, o);
+  if (rc) return rc;
+  if ((rc = check_slots(prm, st, pos, o))) return rc;
+  if ((rc = check_list(prm, st, pos, list, count, o))) return rc;
+  lq::MixedArgs m{};
+  lq::DecodeArgs &d = m.d;
+  d.codes = st->codes;
+  d.row_scale = st->row_scale;
+  d.col_scale = st->col_scale;
+  d.comp_idx = st->comp_idx;
+  d.comp_val = st->comp_val;
+  d.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  d.buf_gate = st->buf_gate;
+  d.buf_k = st->buf_k;
+  d.buf_u = st->buf_u;
+  d.q = q;
+  d.k = k;
+  d.v = v;
+  d.beta = beta;
+  d.alpha = alpha;
+  d.o = o;
+  d.pos = pos;
+  d.n = prm->n;
+  d.p = prm->p;
+  d.r = prm->r;
+  d.t = 0;
+  d.flags = prm->flags;
+  d.skip_last = true;
+  lq::CloseArgs &c = m.c;
+  c.codes = st->codes;
+  c.row_scale = st->row_scale;
+  c.col_scale = st->col_scale;
+  c.comp_idx = st->comp_idx;
+  c.comp_val = st->comp_val;
+  c.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  c.buf_gate = st->buf_gate;
+  c.buf_k = st->buf_k;
+  c.buf_u = st->buf_u;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.beta = beta;
+  c.alpha = alpha;
+  c.o = o;
+  c.lens = pos;
+  c.slots = list;
+  c.n_launch = count;
+  c.n = prm->n;
+  c.p = prm->p;
+  c.r = prm->r;
+  c.len = 0;
+  c.flags = prm->flags;
+  c.iters = prm->comp_iters;
+  c.only_last = true;
+  const bool kda = prm->gate == LQ_GATE_KDA;
+  if (lq::mixed_supported(c)) return hip_status(lq::launch_mixed(m, kda, stream));
+  // other shapes: the same work as two launches, the closes first
+  if (count > 0 && (rc = hip_status(lq::launch_decode_close(c, kda, stream)))) return rc;
+  return hip_status(lq::launch_decode_step(d, kda, stream));
+}
+
 int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const int32_t *len,
                                 const int32_t *list, int32_t count, hipStream_t stream) {
   int rc = check_params(prm);

@@ -1,6 +1,6 @@
 // LeapQuant window close, fused last-token close, initial split and
 // dequantize for gfx950: one 256-thread workgroup per state.
-#include "lq_device.h"
+#include "lq_decode_one.h"
 
 namespace lq {
 
@@ -494,6 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA && !DEN
   // range is left untouched.  FUSED: len is the last token's position t.
   const int len = A.lens ? A.lens[s] : A.len;
   if (FUSED ? (len < 0 || len >= p) : (len < 1 || len > p)) return;
+  if (A.only_last && len != p - 1) return;
   const size_t rec0 = s * p;
 
   __shared__ __attribute__((aligned(16))) float sh_K[kChunk * D];
@@ -843,6 +844,60 @@ __device__ __forceinline__ void split3(float x, float y, uint32_t &hi, uint32_t 
 
 constexpr int kSplitRecs = 16;  // records per row of a split operand
 
+// LDS of one close16 workgroup, carved from one buffer (byte offsets)
+template <bool FUSED>
+struct Close16Lds {
+  static constexpr int kOps = 0;                                  // [2][3][D][16] bf16 split operands
+  static constexpr int kAg = kOps + 2 * 3 * D * kSplitRecs * 2;   // [D] a_i * Gamma_i
+  static constexpr int kGam = kAg + D * 4;                        // [D] Gamma_i
+  static constexpr int kS = kGam + D * 4;                         // [D] s_j
+  static constexpr int kCslot = kS + D * 4;                       // [D] compensator slot of a row or -1
+  static constexpr int kComp = kCslot + D * 4;                    // [8][D] compensator rows
+  static constexpr int kTok = kComp + 8 * D * 4;                  // FUSED: tk, tq, tkt, tu [D] each
+  static constexpr int kKq = kTok + (FUSED ? 4 * D : 16) * 4;     // [2] (padded to 16 bytes)
+  static constexpr int kPart = kKq + 16;                          // [2][D]
+  static constexpr int kSig = kPart + 2 * D * 4;                  // [D]
+  static constexpr int kInv = kSig + D * 4;                       // [D]
+  static constexpr int kSel = kInv + D * 4;                       // [D]
+  static constexpr int kBytes = kSel + D * 4;
+  static_assert(2 * 3 * D * kSplitRecs * 2 >= (D * kRedRow + 8 * D) * 4, "scratch for the split's partials");
+};
+
+// The LDS arrays of one close16 workgroup
+struct Close16Ptrs {
+  uint16_t (*ops)[3][D][kSplitRecs];
+  float *ag, *gam, *s;
+  int *cslot;
+  float *comp, *tk, *tq, *tkt, *tu, *kq, *part, *sig, *inv;
+  int *sel;
+};
+
+// The arrays carved from one buffer of Close16Lds<FUSED>::kBytes
+template <bool FUSED>
+__device__ __forceinline__ Close16Ptrs close16_carve(uint8_t *smem) {
+  using Lo = Close16Lds<FUSED>;
+  Close16Ptrs P;
+  P.ops = reinterpret_cast<uint16_t (*)[3][D][kSplitRecs]>(smem + Lo::kOps);
+  P.ag = reinterpret_cast<float *>(smem + Lo::kAg);
+  P.gam = reinterpret_cast<float *>(smem + Lo::kGam);
+  P.s = reinterpret_cast<float *>(smem + Lo::kS);
+  P.cslot = reinterpret_cast<int *>(smem + Lo::kCslot);
+  P.comp = reinterpret_cast<float *>(smem + Lo::kComp);
+  P.tk = reinterpret_cast<float *>(smem + Lo::kTok);
+  P.tq = P.tk + (FUSED ? D : 4);
+  P.tkt = P.tq + (FUSED ? D : 4);
+  P.tu = P.tkt + (FUSED ? D : 4);
+  P.kq = reinterpret_cast<float *>(smem + Lo::kKq);
+  P.part = reinterpret_cast<float *>(smem + Lo::kPart);
+  P.sig = reinterpret_cast<float *>(smem + Lo::kSig);
+  P.inv = reinterpret_cast<float *>(smem + Lo::kInv);
+  P.sel = reinterpret_cast<int *>(smem + Lo::kSel);
+  return P;
+}
+
+// One workgroup per state (or listed slot): the close of p <= 16 records
+// (FUSED: decoding the window's last token first), body in
+// lq_close16_body.inc.
 template <bool KDA, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void close16_kernel(const CloseArgs A) {
   int slot = blockIdx.x;
@@ -850,247 +905,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
     slot = A.slots[blockIdx.x];
     if ((unsigned)slot >= (unsigned)A.n) return;
   }
+  const int len = A.lens ? A.lens[slot] : A.len;
+  if (FUSED ? (len < 0 || len >= A.p) : (len < 1 || len > A.p)) return;
+  if (A.only_last && len != A.p - 1) return;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Close16Lds<FUSED>::kBytes];
   const size_t s = slot;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
-  const int lr = lane >> 4, lc = lane & 15;
-  const int h = w & 1, ch = w >> 1;
-  const int rbase = 64 * h + 4 * lr;
-  const int col0 = 64 * ch + lc;
-  const int r = A.r, p = A.p;
-  const int len = A.lens ? A.lens[s] : A.len;
-  if (FUSED ? (len < 0 || len >= p) : (len < 1 || len > p)) return;
-  const size_t rec0 = s * p;
+  const Close16Ptrs P = close16_carve<FUSED>(smem);
+#include "lq_close16_body.inc"
+}
 
-  // split operands [part][row or column][record] (bf16); after the
-  // contraction the same space holds the fused decode's partial sums and
-  // the split's column maxima
-  __shared__ __attribute__((aligned(16))) uint16_t sh_ops[2][3][D][kSplitRecs];
-  uint16_t (*sh_kp)[D][kSplitRecs] = sh_ops[0];
-  uint16_t (*sh_up)[D][kSplitRecs] = sh_ops[1];
-  __shared__ __attribute__((aligned(16))) float sh_ag[D];   // a_i * Gamma_i
-  __shared__ __attribute__((aligned(16))) float sh_gam[D];  // Gamma_i
-  __shared__ __attribute__((aligned(16))) float sh_s[D];
-  __shared__ __attribute__((aligned(16))) int sh_cslot[D];
-  __shared__ __attribute__((aligned(16))) float sh_comp[8 * D];
-  __shared__ __attribute__((aligned(16))) float sh_tk[FUSED ? D : 4], sh_tq[FUSED ? D : 4];
-  __shared__ __attribute__((aligned(16))) float sh_tkt[FUSED ? D : 4], sh_tu[FUSED ? D : 4];
-  __shared__ float sh_kq[2];
-  __shared__ float sh_part[2 * D], sh_sig[D];
-  __shared__ __attribute__((aligned(16))) float sh_inv[D];
-  __shared__ __attribute__((aligned(16))) int sh_sel[D];
-  static_assert(sizeof(sh_ops) >= (D * kRedRow + 8 * D) * sizeof(float), "scratch for the split's partials");
-
-  // ---- every load first: codes, then the thread's row or column of records
-  // (the lane offset is opaque here so that the split recomputes the store
-  // address instead of keeping this one live across the kernel)
-  int coff = h * 8192 + col0 * 64 + 16 * lr;
-  asm volatile("" : "+v"(coff));
-  const int8_t *csrc = A.codes + s * D * D + coff;
-  uint4 cw[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) cw[ct] = ldu4(csrc + ct * 1024);
-  const bool krow = tid < D;       // waves 0, 1: key row i = tid
-  const int ic = krow ? tid : tid - D;  // row or column index
-  float x[kSplitRecs];
-#pragma unroll
-  for (int j = 0; j < kSplitRecs; ++j) {
-    x[j] = 0.f;
-    if (j < len) x[j] = krow ? A.buf_k[(rec0 + j) * D + ic] : A.buf_u[(rec0 + j) * D + ic];
-  }
-  float g[KDA ? kSplitRecs : 1];
-  float gl = 1.f;  // GDN: lane j holds gate j
-  if (KDA) {
-#pragma unroll
-    for (int j = 0; j < kSplitRecs; ++j) g[j] = (krow && j < len) ? A.buf_gate[(rec0 + j) * D + ic] : 1.f;
+// ---------------------------------------------------------------------------
+// A continuous-batching token in one launch: count workgroups decode and
+// close the listed slots whose window ends at this token (the fused close
+// above, one workgroup per slot), the others decode four slots each (one
+// wave per slot, the one-wave decode step with its own LDS) for every slot
+// at positions 0 .. p-2.  The closes no longer form a launch of their own
+// whose length is one workgroup's lifetime; they run among the decode
+// steps, which keep memory busy around them.
+// ---------------------------------------------------------------------------
+template <bool KDA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mixed_kernel(const MixedArgs M) {
+  constexpr int kBytes = Close16Lds<true>::kBytes > 4 * kDecodeLdsBytes ? Close16Lds<true>::kBytes
+                                                                          : 4 * kDecodeLdsBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes];
+  // The close workgroups are spread evenly through the grid (dispatch
+  // order): close i sits at position floor(i T / nc) of the T workgroups, so
+  // at any time about nc / T of the resident workgroups are closes (VALU
+  // work) and the rest decode steps (memory streams).  Workgroup b is a
+  // close iff ceil((b + 1) nc / T) > ceil(b nc / T); closes before it:
+  // ceil(b nc / T).
+  const long long nc = M.c.n_launch;
+  const long long T = gridDim.x, b = blockIdx.x;
+  const long long before = (b * nc + T - 1) / T;
+  const long long upto = ((b + 1) * nc + T - 1) / T;
+  if (upto > before) {
+    const int slot = M.c.slots[before];
+    if ((unsigned)slot >= (unsigned)M.c.n) return;
+    const int len = M.c.lens[slot];
+    if (len != M.c.p - 1) return;
+    const CloseArgs &A = M.c;
+    const size_t s = slot;
+    constexpr bool FUSED = true;
+    const Close16Ptrs P = close16_carve<true>(smem);
+#include "lq_close16_body.inc"
   } else {
-    if (krow && lane < len) gl = A.buf_gate[rec0 + lane];
+    // whole waves leave here; the wave-local decode has no workgroup barrier
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int s = 4 * (int)(b - before) + w;
+    if (s >= M.d.n) return;
+    const int t = M.d.pos[s];
+    if (t < 0 || t >= M.d.p - 1) return;
+    uint8_t *base = smem + w * kDecodeLdsBytes;
+    float2 *gy = reinterpret_cast<float2 *>(base);
+    float2 *hh = gy + D;
+    float2 *hc = hh + 64;
+    float2 *zz = hc + 16;
+    uint8_t *dig = reinterpret_cast<uint8_t *>(zz + D);
+    float *red = reinterpret_cast<float *>(dig + 8 * 2 * 64);
+    const DecodeLds Ls{gy, hh, hc, zz, dig, red};
+    const DecodeArgs &A = M.d;
+    const int lane = threadIdx.x & 63;
+    constexpr bool DENSE = false, WAVE = true;
+#include "lq_decode_body.inc"
   }
-  const float scale = krow ? A.row_scale[s * D + ic] : A.col_scale[s * D + ic];
-  // compensator rows (r <= 8: at most one float4 per thread) and indices
-  float4 cv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < r * (D / 4)) cv = ld4(A.comp_val + s * r * D + 4 * tid);
-  int cidx = -1;
-  if (tid < r) cidx = A.comp_idx[s * r + tid];
-  // FUSED: the last token's k, q (rows), v (columns), beta and alpha
-  float tk = 0.f, tq = 0.f, tv = 0.f, tx = 0.f, ta = 1.f;
-  if (FUSED) {
-    if (krow) {
-      tk = A.k[s * D + ic];
-      tq = A.q[s * D + ic];
-      // beta_t in even lanes, GDN's alpha_t in odd lanes (lane-indexed
-      // vector load, broadcast below); KDA reads alpha_t per row
-      tx = *((lane & 1) ? A.alpha + (KDA ? s * D + ic : s) : A.beta + s);
-      if (KDA) ta = A.alpha[s * D + ic];
-    } else {
-      tv = A.v[s * D + ic];
-    }
-  }
+}
 
-  // ---- decays (key rows), parts, side data to LDS
-  if (tid < D) sh_cslot[tid] = -1;
-  if (krow) {
-    float P = 1.f;
-    if (FUSED) P = KDA ? ta : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 1));
-#pragma unroll
-    for (int j = kSplitRecs - 1; j >= 0; --j) {
-      if (j < len) {
-        x[j] *= P;
-        P *= KDA ? g[j] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), j));
-      }
-    }
-    sh_gam[ic] = P;
-    sh_ag[ic] = scale * P;
-    if (FUSED) {
-      const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx), 0));
-      sh_tk[ic] = (A.flags & 2u) ? 0.f : tk;  // b_t = 0 without the delta correction
-      sh_tq[ic] = tq;
-      sh_tkt[ic] = tb * tk;
-    }
-  } else {
-    sh_s[ic] = scale;
-    if (FUSED) sh_tu[ic] = tv;  // v_t; replaced by u_t after the decode
-  }
-  {
-    uint32_t ph[8], pm[8], pl[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split3(x[2 * e], x[2 * e + 1], ph[e], pm[e], pl[e]);
-    uint16_t (*dst)[D][kSplitRecs] = krow ? sh_kp : sh_up;
-    uint4 *d0 = reinterpret_cast<uint4 *>(&dst[0][ic][0]);
-    uint4 *d1 = reinterpret_cast<uint4 *>(&dst[1][ic][0]);
-    uint4 *d2 = reinterpret_cast<uint4 *>(&dst[2][ic][0]);
-    d0[0] = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-    d0[1] = make_uint4(ph[4], ph[5], ph[6], ph[7]);
-    d1[0] = make_uint4(pm[0], pm[1], pm[2], pm[3]);
-    d1[1] = make_uint4(pm[4], pm[5], pm[6], pm[7]);
-    d2[0] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-    d2[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
-  }
-  if (tid < r * (D / 4)) reinterpret_cast<float4 *>(sh_comp)[tid] = cv;
-  __syncthreads();
-  // comp_idx entries outside [0, dk) are ignored
-  if (tid < r && (unsigned)cidx < (unsigned)D) sh_cslot[cidx] = tid;
-  if (FUSED && tid < D) {
-    const float kq = wave_sum(sh_tkt[tid] * sh_tq[tid]);  // waves 0 and 1, all lanes active
-    if (lane == 0) sh_kq[w] = kq;
-  }
-  __syncthreads();
+// The single launch covers slabs above kSmallSlab, where the decode steps
+// it runs are the ones leapquant_decode_step_slots runs (the one-wave
+// kernel), so that both give identical results.
+bool mixed_supported(const CloseArgs &c) {
+  return c.comp_key == nullptr && c.p <= kSplitRecs && c.r <= 8 && c.n > kSmallSlab;
+}
 
-  // ---- acc = Gamma ((c (a Gamma)) s + compensator rows)
-  floatx4 acc[4][4];
-  {
-    float sv[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) sv[ct] = sh_s[col0 + 16 * ct];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float4 ag4 = *reinterpret_cast<const float4 *>(sh_ag + rbase + 16 * rt);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float ag = f4get(ag4, v);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = sbyte_to_f32(u4get(cw[ct], rt), v) * (ag * sv[ct]);
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int4 cs4 = *reinterpret_cast<const int4 *>(sh_cslot + rbase + 16 * rt);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = v == 0 ? cs4.x : v == 1 ? cs4.y : v == 2 ? cs4.z : cs4.w;
-        if (c >= 0) {
-          const float G = sh_gam[rbase + 16 * rt + v];
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            acc[rt][ct][v] = fmaf(G, sh_comp[c * D + col0 + 16 * ct], acc[rt][ct][v]);
-        }
-      }
-    }
-  }
-
-  // ---- acc += K_w U on the bf16 matrix path (three instructions per tile)
-  {
-    const int kb = lr;                 // k-block of this lane's operand values
-    const int rec = 8 * (kb & 1);      // first record of the block
-    const bool lowk = kb < 2;          // k-blocks 0, 1: first part; 2, 3: second
-    // operands of one column tile held, the row tiles' reloaded (LDS reads
-    // are cheap here; registers are not)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int col = col0 + 16 * ct;
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t *>(&sh_up[0][col][rec]);
-      const bf16x8_t b2 = *reinterpret_cast<const bf16x8_t *>(&sh_up[1][col][rec]);
-      const bf16x8_t b3 = *reinterpret_cast<const bf16x8_t *>(&sh_up[lowk ? 2 : 0][col][rec]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int row = 64 * h + 16 * rt + lc;
-        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 1][row][rec]);
-        const bf16x8_t a2 = *reinterpret_cast<const bf16x8_t *>(&sh_kp[lowk ? 0 : 2][row][rec]);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b2, acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b3, acc[rt][ct], 0, 0, 0);
-      }
-    }
-  }
-
-  if (FUSED) {
-    // z = acc^T k_t and acc^T q_t, u_t = v_t - z_b, o_t = z_q + (k~_t . q_t) u_t
-    float zb[4] = {0.f, 0.f, 0.f, 0.f}, zq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float4 k4 = *reinterpret_cast<const float4 *>(sh_tk + rbase + 16 * rt);
-      const float4 q4 = *reinterpret_cast<const float4 *>(sh_tq + rbase + 16 * rt);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          zb[ct] = fmaf(acc[rt][ct][v], f4get(k4, v), zb[ct]);
-          zq[ct] = fmaf(acc[rt][ct][v], f4get(q4, v), zq[ct]);
-        }
-    }
-    __syncthreads();  // every wave is done with the split operands
-    float2 *zp = reinterpret_cast<float2 *>(&sh_kp[0][0][0]);  // [8][D]
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) zp[(4 * h + lr) * D + col0 + 16 * ct] = make_float2(zb[ct], zq[ct]);
-    __syncthreads();
-    // the column threads (waves 2, 3); the index is recomputed from a fresh
-    // copy of the thread index rather than kept live from the start
-    int col = threadIdx.x;
-    asm volatile("" : "+v"(col));
-    col -= D;
-    if (col >= 0) {
-      float b = 0.f, q = 0.f;
-#pragma unroll
-      for (int gi = 0; gi < 8; ++gi) {
-        const float2 z = zp[gi * D + col];
-        b += z.x;
-        q += z.y;
-      }
-      const float u = sh_tu[col] - b;
-      __builtin_nontemporal_store(fmaf(sh_kq[0] + sh_kq[1], u, q), A.o + s * D + col);
-      sh_tu[col] = u;
-    }
-    __syncthreads();
-    float uu[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) uu[ct] = sh_tu[col0 + 16 * ct];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float4 kt4 = *reinterpret_cast<const float4 *>(sh_tkt + rbase + 16 * rt);
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rt][ct][v] = fmaf(f4get(kt4, v), uu[ct], acc[rt][ct][v]);
-    }
-  }
-  // every read of the compensator rows and split operands is done before
-  // the split overwrites them
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(&sh_ops[0][0][0][0]);  // [D][kRedRow] row partials
-  float *cmx = red + D * kRedRow;                                 // [8][D] column-max partials
-  const SplitLds L{sh_part, sh_sel, cmx, sh_sig, sh_inv, nullptr, nullptr, nullptr, red};
-  split_state<false, true>(acc, L, A.codes, A.row_scale, A.col_scale, A.comp_idx, A.comp_val, nullptr, s, r, 0,
-                     A.flags);
+hipError_t launch_mixed(const MixedArgs &a, bool kda, hipStream_t stream) {
+  const int nd = (a.d.n + 3) / 4;
+  const dim3 grid(a.c.n_launch + nd);
+  if (kda)
+    hipLaunchKernelGGL(mixed_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mixed_kernel<false>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -26,6 +26,7 @@ struct DecodeArgs {
   const int32_t *pos;  // per-state window position (nullptr: t for all)
   int n, p, r, t;
   unsigned flags;      // bit 1: b_t = 0 (no delta correction)
+  bool skip_last;      // states at position p - 1 are left to a fused close
 };
 
 struct CloseArgs {
@@ -52,7 +53,19 @@ struct CloseArgs {
   int n, p, r, len;  // len: buffered records the rebuild replays
   int iters;         // dense compensators: subspace iterations of the split
   unsigned flags;
+  bool only_last;    // decode_close over a slot list: listed slots not at position p - 1 are skipped
 };
+
+// One launch for a continuous-batching token: the fused decode_close of the
+// listed slots at their window's last position (the first workgroups), and
+// the decode step of every slot at positions 0 .. p-2 (four slots per
+// workgroup after those).  Supported for windows of up to 16 records with
+// at most 8 compensator rows (row compensators).
+struct MixedArgs {
+  DecodeArgs d;   // pos = the per-slot positions, skip_last = true
+  CloseArgs c;    // lens = the same positions, slots = the list, only_last = true
+};
+bool mixed_supported(const CloseArgs &c);
 
 struct DequantArgs {
   const int8_t *codes;
@@ -97,5 +110,6 @@ hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream)
 hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t stream);
+hipError_t launch_mixed(const MixedArgs &a, bool kda, hipStream_t stream);
 
 }  // namespace lq

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.leapquant_abi_version() == L.ABI_VERSION == 4
+    assert lib.leapquant_abi_version() == L.ABI_VERSION == 5
     for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
                  L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
         assert lib.leapquant_status_string(code)
@@ -170,6 +170,30 @@ def test_inputs_overlapping_the_state_rejected(lib, entry):
     assert _decode(lib, prm, st, alpha=st.row_scale) == L.LQ_ERR_ALIAS     # alpha over the row scales
     assert _decode(lib, prm, st, q=st.comp_val + 16) == L.LQ_ERR_ALIAS     # q inside the compensators
     assert _decode(lib, prm, st, beta=st.comp_idx) == L.LQ_ERR_ALIAS       # beta over the row indices
+
+
+def test_step_close_list_checks(lib):
+    """The one-launch continuous-batching token validates like
+    decode_close_list."""
+    st, base = _state()
+    prm = _params()
+    vec = 4 * 512
+    a = dict(q=base, k=base + vec, v=base + 2 * vec, beta=base + 3 * vec, alpha=base + 3 * vec + 64,
+             o=base + 4 * vec)
+    pos, lst = base + 5 * vec, base + 5 * vec + 64
+    f = lib.leapquant_decode_step_close_list
+
+    def call(pos_=pos, lst_=lst, count=2, **kw):
+        x = dict(a, **kw)
+        return f(ctypes.byref(prm), ctypes.byref(st), pos_, lst_, count, x["q"], x["k"], x["v"],
+                 x["beta"], x["alpha"], x["o"], None)
+    assert call(pos_=None) == L.LQ_ERR_NULL
+    assert call(lst_=None) == L.LQ_ERR_NULL
+    assert call(count=-1) == L.LQ_ERR_SHAPE and call(count=5) == L.LQ_ERR_SHAPE
+    assert call(pos_=pos + 2) == L.LQ_ERR_ALIGN
+    assert call(lst_=st.codes + 64) == L.LQ_ERR_ALIAS              # list inside the codes
+    assert call(lst_=pos + 4) == L.LQ_ERR_ALIAS                    # list over the positions
+    assert call(k=st.buf_k) == L.LQ_ERR_ALIAS                      # input over the records
 
 
 def test_overlapping_state_arrays_rejected(lib, entry):

@@ -35,6 +35,8 @@ hipError_t launch_window_close(const CloseArgs &, bool, hipStream_t) { return re
 hipError_t launch_decode_close(const CloseArgs &, bool, hipStream_t) { return reached("decode_close"); }
 hipError_t launch_quantize_state(const CloseArgs &, hipStream_t) { return reached("quantize_state"); }
 hipError_t launch_dequantize(const DequantArgs &, hipStream_t) { return reached("dequantize"); }
+hipError_t launch_mixed(const MixedArgs &, bool, hipStream_t) { return reached("mixed"); }
+bool mixed_supported(const CloseArgs &) { return true; }
 }  // namespace lq
 """
 
