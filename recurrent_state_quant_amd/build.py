@@ -21,6 +21,11 @@ def hipcc_command(out=LIB_PATH, extra=()):
             # MFMA accumulators in VGPRs: the close kernel post-processes them
             # on the VALU, and AGPR copies would double its register footprint
             "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+            # products fused into adds only within one expression (a*b + c
+            # becomes one fma, as written): the fusion the default mode leaves
+            # to the back end picks an operand by the shape of the code around
+            # it, so one body included in two kernels could round differently
+            "-ffp-contract=on",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG_DIR, "csrc"),
             *extra, "-o", out, *SOURCES]
 

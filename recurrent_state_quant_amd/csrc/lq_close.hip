@@ -965,7 +965,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     const DecodeLds Ls{gy, hh, hc, zz, dig, red};
     const DecodeArgs &A = M.d;
     const int lane = threadIdx.x & 63;
-    constexpr bool DENSE = false, WAVE = true;
+    constexpr bool DENSE = false, WAVE = true, LONG = false;  // p <= 16
 #include "lq_decode_body.inc"
   }
 }

@@ -4,7 +4,7 @@
 
 namespace lq {
 
-template <bool KDA, bool DENSE>
+template <bool KDA, bool DENSE, bool LONG>
 __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   // per-slot positions (continuous batching): out-of-range slots are idle;
@@ -340,8 +340,10 @@ template <bool KDA, bool DENSE>
 void launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   if (a.n <= kSmallSlab)
     hipLaunchKernelGGL((decode_step2_kernel<KDA, DENSE>), dim3(a.n), dim3(128), 0, stream, a);
+  else if (a.p > kRecChunk + 1)
+    hipLaunchKernelGGL((decode_step_kernel<KDA, DENSE, true>), dim3(a.n), dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_step_kernel<KDA, DENSE>), dim3(a.n), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_step_kernel<KDA, DENSE, false>), dim3(a.n), dim3(64), 0, stream, a);
 }
 
 // Dense compensator tokens are on when the caller passes their keys.

@@ -68,6 +68,26 @@ __device__ __forceinline__ uint2 ldu2(const void *p) {
   const vu2 t = __builtin_nontemporal_load(reinterpret_cast<const vu2 *>(p));
   return make_uint2(t.x, t.y);
 }
+// Count-guarded loads through a raw buffer resource: a buffer over the
+// first `bytes` bytes at p returns zero for loads at byte offsets at or
+// beyond `bytes` without touching memory, so a loop of loads guarded by a
+// run-time count becomes straight-line code.  The compiler then knows
+// exactly which loads are outstanding at each use and waits for those only;
+// with branches around the loads it waits for every load in flight
+// (the state's whole code stream included).  Dword 3 holds the gfx9 raw
+// buffer format (32-bit data, no swizzle, no stride); nontemporal like ld2.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void *p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+constexpr int kBufNt = 2;  // cache policy bits of the buffer loads: nt
+__device__ __forceinline__ float2 bld2(BufRsrc r, int off) {
+  const vu2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufNt);
+  return make_float2(__uint_as_float(t.x), __uint_as_float(t.y));
+}
+__device__ __forceinline__ uint32_t bld1(BufRsrc r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kBufNt);
+}
 __device__ __forceinline__ void st2(float *p, float2 v) {
   __builtin_nontemporal_store(vf2{v.x, v.y}, reinterpret_cast<vf2 *>(p));
 }
