@@ -355,6 +355,13 @@ def main():
         close_flops = close_states * 2 * cfg.dk * cfg.dv * ((slots + 3) // 4 * 4)
         mfma_peak, mfma_dtype = MFMA_FP32_PEAK_TFLOPS, "fp32"
     close_mfma_util = close_flops / (close_avg_ms * 1e-3) / (mfma_peak * 1e12)
+    # a plain stream with the decode step's mean bytes per state, one wave
+    # per state and as many waves as one decode launch: the rows it writes
+    # (record t, o_t, u_t) at the end of the wave, the rest read (to the
+    # nearest KiB)
+    wr = 512 * (3 + (1 if kda else 0))
+    stream_ref = stream_reference(dev, max(1, round((dec_bytes / nl - wr) / 1024)) * 1024, wr, nl)
+    stream_ref["decode_frac_of_stream"] = round(dec_gbs / stream_ref["GBs"], 4)
     whole_gbs = value * bpht / 1e9
     traffic = {} if dense else measured_traffic(cfg)
     dkey = "decode_fused" if fused else "decode_separate"
@@ -387,6 +394,7 @@ def main():
                          "traffic": close_traffic, "mfma_dtype": mfma_dtype,
                          "mfma_flops_per_launch": close_flops, "mfma_util": round(close_mfma_util, 4)},
         "hbm_copy_GBs": round(copy_gbs, 1),
+        "stream_reference": stream_ref,
     }
 
     if dense:
@@ -657,6 +665,35 @@ def copy_calibration(dev, nbytes=1 << 31, reps=5):
     gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     return gbs
+
+
+def stream_reference(dev, read_bytes, write_bytes, waves, slabs=4, reps=24):
+    """Rate of a plain stream in the decode step's launch shape: waves waves
+    per launch, each reading its own read_bytes bytes and then writing
+    write_bytes bytes (leapquant_stream_reference), over `slabs` buffers
+    cycled like layers so that no launch finds its bytes in a cache.  HIP
+    events on the launch stream bracket the timed launches."""
+    import torch
+    import recurrent_state_quant_amd as lq
+    stream = torch.cuda.Stream(device=dev)
+    srcs = [torch.empty(read_bytes * waves, dtype=torch.uint8, device=dev) for _ in range(slabs)]
+    dsts = [torch.empty(write_bytes * waves, dtype=torch.uint8, device=dev) if write_bytes else None
+            for _ in range(slabs)]
+    out = torch.empty((waves, 64), dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        for x, y in zip(srcs, dsts):
+            x.fill_(1)
+            lq.leapquant_stream_reference(x, read_bytes, y, write_bytes, out, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            lq.leapquant_stream_reference(srcs[i % slabs], read_bytes, dsts[i % slabs], write_bytes, out, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del srcs, dsts, out
+    return {"read_bytes_per_wave": read_bytes, "write_bytes_per_wave": write_bytes, "waves": waves,
+            "avg_launch_us": round(us, 2), "GBs": round((read_bytes + write_bytes) * waves / (us * 1e-6) / 1e9, 1)}
 
 
 def _cpu_model():

@@ -14,7 +14,7 @@ from .api import (LeapQuantState, code_offsets, codes_from_matrix, codes_to_matr
                   leapquant_decode_close_slots, leapquant_decode_step_slots, leapquant_dense_step,
                   leapquant_window_close_slots, leapquant_decode_close_list, leapquant_window_close_list,
                   leapquant_decode_step_close_list, leapquant_dequantize_state, leapquant_quantize_state,
-                  leapquant_status_string, leapquant_window_close)
+                  leapquant_stream_reference, leapquant_status_string, leapquant_window_close)
 
 __all__ = [
     "LQ_DENSE_BF16", "LQ_DENSE_COMP", "LQ_DENSE_FP32", "LQ_GATE_GDN", "LQ_GATE_KDA", "LQ_NO_DELTA", "LQ_NO_SMOOTH",
@@ -24,6 +24,6 @@ __all__ = [
     "leapquant_decode_close", "leapquant_decode_step",
     "leapquant_decode_close_slots", "leapquant_decode_step_slots", "leapquant_dense_step",
     "leapquant_window_close_slots", "leapquant_decode_close_list", "leapquant_window_close_list",
-    "leapquant_decode_step_close_list", "leapquant_dequantize_state", "leapquant_quantize_state", "leapquant_status_string",
-    "leapquant_window_close",
+    "leapquant_decode_step_close_list", "leapquant_dequantize_state", "leapquant_quantize_state",
+    "leapquant_stream_reference", "leapquant_status_string", "leapquant_window_close",
 ]

@@ -8,7 +8,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libleapquant.so")
 
-ABI_VERSION = 5  # the lq_params / lq_state layout and entry points this binding mirrors
+ABI_VERSION = 6  # the lq_params / lq_state layout and entry points this binding mirrors
 
 LQ_OK = 0
 LQ_ERR_NULL = -1
@@ -41,6 +41,7 @@ EXPORTED = (
     "leapquant_dequantize_state",
     "leapquant_bf16w_decode_step",
     "leapquant_bf16w_window_close",
+    "leapquant_stream_reference",
     "leapquant_status_string",
     "leapquant_abi_version",
 )
@@ -93,12 +94,13 @@ def load():
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     lib.leapquant_bf16w_decode_step.argtypes = [P, vp, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_bf16w_window_close.argtypes = [P, vp, S, i32, vp]
+    lib.leapquant_stream_reference.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64, i32, vp, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
               "leapquant_decode_close", "leapquant_dense_step", "leapquant_decode_step_slots",
               "leapquant_decode_close_slots", "leapquant_window_close_slots",
               "leapquant_decode_close_list", "leapquant_window_close_list", "leapquant_decode_step_close_list",
               "leapquant_dequantize_state", "leapquant_bf16w_decode_step",
-              "leapquant_bf16w_window_close"):
+              "leapquant_bf16w_window_close", "leapquant_stream_reference"):
         getattr(lib, f).restype = ctypes.c_int
     lib.leapquant_status_string.argtypes = [ctypes.c_int]
     lib.leapquant_status_string.restype = ctypes.c_char_p

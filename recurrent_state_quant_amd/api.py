@@ -349,6 +349,27 @@ def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0)
         L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
 
 
+def leapquant_stream_reference(src, read_bytes_per_wave, dst, write_bytes_per_wave, out, stream=None):
+    """Measurement reference: a plain stream in the decode step's launch
+    shape, one wave per read_bytes_per_wave block of src (uint8, 16-byte
+    aligned, a whole number of blocks), each wave then writing
+    write_bytes_per_wave bytes of dst (uint8, waves * write_bytes_per_wave
+    bytes; None when 0); out (int32 [waves, 64]) receives a checksum per
+    lane."""
+    if not isinstance(src, torch.Tensor) or src.dtype != torch.uint8 or src.dim() != 1:
+        raise ValueError("src must be a 1-d uint8 tensor")
+    if read_bytes_per_wave <= 0 or src.numel() % read_bytes_per_wave:
+        raise ValueError("src must hold a whole number of read_bytes_per_wave blocks")
+    waves = src.numel() // read_bytes_per_wave
+    d = src.device
+    sp = _ptr(src, torch.uint8, (src.numel(),), "src", d)
+    dp = None if write_bytes_per_wave == 0 else _ptr(dst, torch.uint8, (waves * write_bytes_per_wave,), "dst", d)
+    op = _ptr(out, torch.int32, (waves, 64), "out", d)
+    with torch.cuda.device(d):
+        L.check(L.load().leapquant_stream_reference(sp, int(read_bytes_per_wave), dp, int(write_bytes_per_wave),
+                                                    int(waves), op, _stream(stream, d)))
+
+
 def leapquant_window_close(state, length, stream=None):
     prm, st = state.params(), state.ptrs()
     with torch.cuda.device(state.device):

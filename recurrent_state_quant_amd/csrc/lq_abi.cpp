@@ -580,6 +580,29 @@ int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const flo
   return hip_status(lq::launch_dense_step(a, kda, bf16, stream));
 }
 
+// ---- stream reference (measurement aid)
+int leapquant_stream_reference(const void *src, int64_t read_bytes_per_wave, void *dst,
+                               int64_t write_bytes_per_wave, int32_t waves, uint32_t *out,
+                               hipStream_t stream) {
+  if (!src || !out || (write_bytes_per_wave > 0 && !dst)) return LQ_ERR_NULL;
+  const int64_t kMax = int64_t(1) << 30;
+  if (read_bytes_per_wave < 1024 || read_bytes_per_wave > kMax || read_bytes_per_wave % 1024 != 0 ||
+      write_bytes_per_wave < 0 || write_bytes_per_wave > kMax || write_bytes_per_wave % 512 != 0 || waves < 1)
+    return LQ_ERR_SHAPE;
+  if (!aligned(src, 16) || !aligned(out, 4) || (write_bytes_per_wave > 0 && !aligned(dst, 16)))
+    return LQ_ERR_ALIGN;
+  const size_t w = static_cast<size_t>(waves);
+  const Range rd = span(src, static_cast<size_t>(read_bytes_per_wave) * w);
+  const Range ck = span(out, w * 64 * sizeof(uint32_t));
+  if (overlap(rd, ck)) return LQ_ERR_ALIAS;
+  if (write_bytes_per_wave > 0) {
+    const Range wr = span(dst, static_cast<size_t>(write_bytes_per_wave) * w);
+    if (overlap(wr, rd) || overlap(wr, ck)) return LQ_ERR_ALIAS;
+  }
+  return hip_status(lq::launch_stream_ref(src, static_cast<uint32_t>(read_bytes_per_wave), dst,
+                                          static_cast<uint32_t>(write_bytes_per_wave), waves, out, stream));
+}
+
 // ---- "BF16 + per-window": dense bf16 boundary state, fp32 window buffer
 static int check_bf16w(const lq_params *prm, const void *B, const lq_state *st) {
   int rc = check_params(prm);

@@ -395,6 +395,42 @@ hipError_t launch_bf16w_decode(const Bf16WinArgs &a, bool kda, hipStream_t strea
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Stream reference for the decode step's launch shape (a measurement aid,
+// no arithmetic of the method): one 64-lane wave per block of per_wave
+// bytes, read with 16-byte nontemporal loads in batches of 16 per lane
+// (16 KiB per wave, every load of a batch issued before any is used, as
+// the decode issues its code stream; loads past the block's end return
+// zero without a memory access), then write_bytes bytes written per wave at
+// its end (8 bytes per lane per 512-byte row, as the decode stores its
+// output rows).  Each lane also writes one checksum word.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void stream_ref_kernel(const uint8_t *src, uint32_t per_wave, float *dst,
+                                                        uint32_t write_bytes, uint32_t *out) {
+  const int lane = threadIdx.x;
+  const BufRsrc rs = buf_rsrc(src + (size_t)blockIdx.x * per_wave, (int)per_wave);
+  uint32_t acc = 0;
+  for (uint32_t off = 0; off < per_wave; off += 16384) {
+    vu4 x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      x[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 1024 * j + 16 * lane), 0, kBufNt);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += x[j].x ^ x[j].y ^ x[j].z ^ x[j].w;
+  }
+  const float f = __uint_as_float(acc);
+  float *row = dst + (size_t)blockIdx.x * (write_bytes / 4) + 2 * lane;
+  for (uint32_t b = 0; b < write_bytes; b += 512, row += 128) st2(row, make_float2(f, f));
+  out[(size_t)blockIdx.x * 64 + lane] = acc;
+}
+
+hipError_t launch_stream_ref(const void *src, uint32_t per_wave, void *dst, uint32_t write_bytes, int waves,
+                             uint32_t *out, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_ref_kernel, dim3(waves), dim3(64), 0, stream, static_cast<const uint8_t *>(src),
+                     per_wave, static_cast<float *>(dst), write_bytes, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_bf16w_close(const Bf16WinArgs &a, bool kda, hipStream_t stream) {
   if (kda)
     hipLaunchKernelGGL(bf16w_close_kernel<true>, dim3(a.n), dim3(256), 0, stream, a);

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.leapquant_abi_version() == L.ABI_VERSION == 5
+    assert lib.leapquant_abi_version() == L.ABI_VERSION == 6
     for code in (L.LQ_OK, L.LQ_ERR_NULL, L.LQ_ERR_SHAPE, L.LQ_ERR_UNSUPPORTED, L.LQ_ERR_ALIGN,
                  L.LQ_ERR_ALIAS, L.LQ_ERR_HIP, 12345):
         assert lib.leapquant_status_string(code)
@@ -374,3 +374,24 @@ def test_bf16_window_validation(lib):
     assert close(n_=0) == L.LQ_ERR_SHAPE and close(n_=17) == L.LQ_ERR_SHAPE
     assert dec(q=0) == L.LQ_ERR_NULL
     assert close(prm_=_params(dk=64)) == L.LQ_ERR_UNSUPPORTED
+
+
+def test_stream_reference_validation(lib):
+    """The stream reference: read blocks a multiple of 1 KiB, written blocks
+    a multiple of 512 bytes, at least one wave, aligned pointers, outputs
+    outside the bytes read and apart from each other."""
+    f = lib.leapquant_stream_reference
+    src, dst, out = FAKE, FAKE + (1 << 24), FAKE + (1 << 25)
+    assert f(None, 1024, dst, 512, 4, out, None) == L.LQ_ERR_NULL
+    assert f(src, 1024, dst, 512, 4, None, None) == L.LQ_ERR_NULL
+    assert f(src, 1024, None, 512, 4, out, None) == L.LQ_ERR_NULL
+    for rb, wb, waves in ((0, 0, 4), (1000, 0, 4), (1536, 0, 4), ((1 << 30) + 1024, 0, 1), (1024, 0, 0),
+                          (1024, 0, -1), (1024, 256, 4), (1024, -512, 4), (1024, (1 << 30) + 512, 1)):
+        assert f(src, rb, dst, wb, waves, out, None) == L.LQ_ERR_SHAPE, (rb, wb, waves)
+    assert f(src + 8, 1024, dst, 512, 4, out, None) == L.LQ_ERR_ALIGN
+    assert f(src, 1024, dst + 8, 512, 4, out, None) == L.LQ_ERR_ALIGN
+    assert f(src, 1024, dst, 512, 4, out + 2, None) == L.LQ_ERR_ALIGN
+    assert f(src, 1024, dst, 512, 4, src + 4096 - 4, None) == L.LQ_ERR_ALIAS        # checksums over the last block
+    assert f(src, 1024, dst, 512, 4, src - 4 * 64 * 4 + 4, None) == L.LQ_ERR_ALIAS  # ... ending inside the first
+    assert f(src, 1024, src + 1024, 512, 4, out, None) == L.LQ_ERR_ALIAS            # writes over the reads
+    assert f(src, 1024, out - 16, 512, 4, out, None) == L.LQ_ERR_ALIAS              # writes over the checksums
