@@ -112,7 +112,7 @@ def measured_traffic(cfg):
         return {}
     names = {"decode_fused": "decode_step_kernel<GDN> (fused schedule)",
              "decode_separate": "decode_step_kernel<GDN> (separate schedule)",
-             "close": "close_kernel<GDN, window close>", "fused": "close_kernel<GDN, fused decode_close>"}
+             "close": "close16_kernel<GDN, window close>", "fused": "close16_kernel<GDN, fused decode_close>"}
     return {key: doc["kernels"][nm]["traffic_bytes_per_state"]
             for key, nm in names.items() if nm in doc["kernels"]}
 
@@ -142,6 +142,10 @@ def parse():
     ap.add_argument("--ablation-tokens", type=int, default=64)
     ap.add_argument("--ablation-set", choices=("all", "continuous_batching"), default="all",
                     help="with --ablations: every table, or only the continuous-batching one")
+    ap.add_argument("--stream-lab", action="store_true",
+                    help="instead of the headline line, print one line with the stream reference at the "
+                         "decode step's launch shape: the rate against an idle phase per wave after its "
+                         "loads, and against waves per launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the short separate-close and KDA-workload runs reported beside the headline")
@@ -307,6 +311,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.ablations:
         print(json.dumps(ablations(args, cfg, dev)), flush=True)
+        return
+    if args.stream_lab:
+        print(json.dumps(stream_lab(cfg, dev)), flush=True)
         return
     kda = cfg.gate == "kda"
     T = args.tokens or cfg.steps
@@ -667,7 +674,7 @@ def copy_calibration(dev, nbytes=1 << 31, reps=5):
     return gbs
 
 
-def stream_reference(dev, read_bytes, write_bytes, waves, slabs=4, reps=24):
+def stream_reference(dev, read_bytes, write_bytes, waves, slabs=4, reps=24, idle=0):
     """Rate of a plain stream in the decode step's launch shape: waves waves
     per launch, each reading its own read_bytes bytes and then writing
     write_bytes bytes (leapquant_stream_reference), over `slabs` buffers
@@ -683,17 +690,42 @@ def stream_reference(dev, read_bytes, write_bytes, waves, slabs=4, reps=24):
     with torch.cuda.stream(stream):
         for x, y in zip(srcs, dsts):
             x.fill_(1)
-            lq.leapquant_stream_reference(x, read_bytes, y, write_bytes, out, stream)
+            lq.leapquant_stream_reference(x, read_bytes, y, write_bytes, out, stream, idle)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(reps):
-            lq.leapquant_stream_reference(srcs[i % slabs], read_bytes, dsts[i % slabs], write_bytes, out, stream)
+            lq.leapquant_stream_reference(srcs[i % slabs], read_bytes, dsts[i % slabs], write_bytes, out, stream,
+                                          idle)
         e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
     del srcs, dsts, out
     return {"read_bytes_per_wave": read_bytes, "write_bytes_per_wave": write_bytes, "waves": waves,
             "avg_launch_us": round(us, 2), "GBs": round((read_bytes + write_bytes) * waves / (us * 1e-6) / 1e9, 1)}
+
+
+def stream_lab(cfg, dev):
+    """The stream reference at the decode step's shape on `cfg` (mean bytes
+    per state read and the rows written, one wave per state): the rate with
+    an idle phase of 0 .. 32 x 512 cycles per wave between its loads and its
+    stores (a stand-in for the work a decode wave does once its loads have
+    returned), and the rate for 1/2 .. 4x the waves of one launch."""
+    kda = cfg.gate == "kda"
+    nl = cfg.states_per_layer
+    dec = sum(step_bytes(t, cfg.dk, cfg.dv, cfg.r, kda) for t in range(cfg.p - 1)) / (cfg.p - 1)
+    wr = 512 * (3 + (1 if kda else 0))
+    rd = max(1, round((dec - wr) / 1024)) * 1024
+    idle = []
+    for k in (0, 4, 8, 16, 32):
+        r = stream_reference(dev, rd, wr, nl, idle=k)
+        idle.append({"idle_cycles_per_wave": 512 * k, "avg_launch_us": r["avg_launch_us"], "GBs": r["GBs"]})
+    waves = []
+    for m in (0.5, 1, 2, 4):
+        r = stream_reference(dev, rd, wr, int(nl * m))
+        waves.append({"waves": int(nl * m), "avg_launch_us": r["avg_launch_us"], "GBs": r["GBs"]})
+    return {"metric": "stream reference at the decode step's launch shape (GB/s, read + write)",
+            "workload": cfg.name, "read_bytes_per_wave": rd, "write_bytes_per_wave": wr,
+            "idle_phase": idle, "waves_per_launch": waves}
 
 
 def _cpu_model():

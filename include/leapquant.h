@@ -338,21 +338,25 @@ int leapquant_bf16w_window_close(const lq_params *prm, void *B, const lq_state *
 /* ---- Measurement reference, no part of the method: a plain stream in
  * the decode step's launch shape.  One 64-lane wave per block of
  * read_bytes_per_wave bytes at src reads its block with 16-byte nontemporal
- * loads, 16 KiB per wave issued at a time, then writes write_bytes_per_wave
- * bytes at dst + wave * write_bytes_per_wave (8 bytes per lane per 512-byte
- * row, as the decode step stores its output rows).  Timed beside the decode
- * step, it gives the rate the device reaches for the same bytes per wave,
- * read/write mix and waves per launch with no arithmetic between.  Also
+ * loads, 16 KiB per wave issued at a time, then sleeps idle_sleeps times
+ * 512 cycles with nothing in flight (a stand-in for the work a decode wave
+ * does after its loads return), then writes write_bytes_per_wave bytes at
+ * dst + wave * write_bytes_per_wave (8 bytes per lane per 512-byte row, as
+ * the decode step stores its output rows).  Timed beside the decode step
+ * with idle_sleeps = 0, it gives the rate the device reaches for the same
+ * bytes per wave, read/write mix and waves per launch with no arithmetic
+ * between.  Also
  * writes waves * 64 checksum words to out (each the sum over the lane's
  * 16-byte loads of the XOR of their four 32-bit words).
  * read_bytes_per_wave a positive multiple of 1024, write_bytes_per_wave a
  * multiple of 512 (0 allowed, then dst may be NULL), both at most 2^30;
- * waves >= 1 (LQ_ERR_SHAPE otherwise); src and dst 16-byte aligned, out
+ * 0 <= idle_sleeps <= 4096; waves >= 1 (LQ_ERR_SHAPE otherwise); src and
+ * dst 16-byte aligned, out
  * 4-byte aligned (LQ_ERR_ALIGN); dst and out must not overlap each other
  * or the bytes read (LQ_ERR_ALIAS). */
 int leapquant_stream_reference(const void *src, int64_t read_bytes_per_wave, void *dst,
-                               int64_t write_bytes_per_wave, int32_t waves, uint32_t *out,
-                               hipStream_t stream);
+                               int64_t write_bytes_per_wave, int32_t idle_sleeps, int32_t waves,
+                               uint32_t *out, hipStream_t stream);
 
 /* LEAPQUANT_ABI_VERSION of the loaded library. */
 int leapquant_abi_version(void);

@@ -94,7 +94,7 @@ def load():
     lib.leapquant_dequantize_state.argtypes = [P, S, vp, vp]
     lib.leapquant_bf16w_decode_step.argtypes = [P, vp, S, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.leapquant_bf16w_window_close.argtypes = [P, vp, S, i32, vp]
-    lib.leapquant_stream_reference.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64, i32, vp, vp]
+    lib.leapquant_stream_reference.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64, i32, i32, vp, vp]
     for f in ("leapquant_quantize_state", "leapquant_decode_step", "leapquant_window_close",
               "leapquant_decode_close", "leapquant_dense_step", "leapquant_decode_step_slots",
               "leapquant_decode_close_slots", "leapquant_window_close_slots",

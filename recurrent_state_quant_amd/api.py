@@ -349,13 +349,14 @@ def leapquant_dense_step(S, gate, q, k, v, beta, alpha, o, stream=None, flags=0)
         L.check(L.load().leapquant_dense_step(ctypes.byref(prm), sp, dtype, *args, _stream(stream, S.device)))
 
 
-def leapquant_stream_reference(src, read_bytes_per_wave, dst, write_bytes_per_wave, out, stream=None):
+def leapquant_stream_reference(src, read_bytes_per_wave, dst, write_bytes_per_wave, out, stream=None,
+                               idle_sleeps=0):
     """Measurement reference: a plain stream in the decode step's launch
     shape, one wave per read_bytes_per_wave block of src (uint8, 16-byte
-    aligned, a whole number of blocks), each wave then writing
-    write_bytes_per_wave bytes of dst (uint8, waves * write_bytes_per_wave
-    bytes; None when 0); out (int32 [waves, 64]) receives a checksum per
-    lane."""
+    aligned, a whole number of blocks), each wave then idling idle_sleeps x
+    512 cycles and writing write_bytes_per_wave bytes of dst (uint8, waves *
+    write_bytes_per_wave bytes; None when 0); out (int32 [waves, 64])
+    receives a checksum per lane."""
     if not isinstance(src, torch.Tensor) or src.dtype != torch.uint8 or src.dim() != 1:
         raise ValueError("src must be a 1-d uint8 tensor")
     if read_bytes_per_wave <= 0 or src.numel() % read_bytes_per_wave:
@@ -367,7 +368,7 @@ def leapquant_stream_reference(src, read_bytes_per_wave, dst, write_bytes_per_wa
     op = _ptr(out, torch.int32, (waves, 64), "out", d)
     with torch.cuda.device(d):
         L.check(L.load().leapquant_stream_reference(sp, int(read_bytes_per_wave), dp, int(write_bytes_per_wave),
-                                                    int(waves), op, _stream(stream, d)))
+                                                    int(idle_sleeps), int(waves), op, _stream(stream, d)))
 
 
 def leapquant_window_close(state, length, stream=None):

@@ -582,12 +582,13 @@ int leapquant_dense_step(const lq_params *prm, void *S, int32_t dtype, const flo
 
 // ---- stream reference (measurement aid)
 int leapquant_stream_reference(const void *src, int64_t read_bytes_per_wave, void *dst,
-                               int64_t write_bytes_per_wave, int32_t waves, uint32_t *out,
-                               hipStream_t stream) {
+                               int64_t write_bytes_per_wave, int32_t idle_sleeps, int32_t waves,
+                               uint32_t *out, hipStream_t stream) {
   if (!src || !out || (write_bytes_per_wave > 0 && !dst)) return LQ_ERR_NULL;
   const int64_t kMax = int64_t(1) << 30;
   if (read_bytes_per_wave < 1024 || read_bytes_per_wave > kMax || read_bytes_per_wave % 1024 != 0 ||
-      write_bytes_per_wave < 0 || write_bytes_per_wave > kMax || write_bytes_per_wave % 512 != 0 || waves < 1)
+      write_bytes_per_wave < 0 || write_bytes_per_wave > kMax || write_bytes_per_wave % 512 != 0 ||
+      idle_sleeps < 0 || idle_sleeps > 4096 || waves < 1)
     return LQ_ERR_SHAPE;
   if (!aligned(src, 16) || !aligned(out, 4) || (write_bytes_per_wave > 0 && !aligned(dst, 16)))
     return LQ_ERR_ALIGN;
@@ -600,7 +601,8 @@ int leapquant_stream_reference(const void *src, int64_t read_bytes_per_wave, voi
     if (overlap(wr, rd) || overlap(wr, ck)) return LQ_ERR_ALIAS;
   }
   return hip_status(lq::launch_stream_ref(src, static_cast<uint32_t>(read_bytes_per_wave), dst,
-                                          static_cast<uint32_t>(write_bytes_per_wave), waves, out, stream));
+                                          static_cast<uint32_t>(write_bytes_per_wave), idle_sleeps, waves, out,
+                                          stream));
 }
 
 // ---- "BF16 + per-window": dense bf16 boundary state, fp32 window buffer

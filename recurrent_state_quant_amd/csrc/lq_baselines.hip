@@ -401,12 +401,14 @@ hipError_t launch_bf16w_decode(const Bf16WinArgs &a, bool kda, hipStream_t strea
 // bytes, read with 16-byte nontemporal loads in batches of 16 per lane
 // (16 KiB per wave, every load of a batch issued before any is used, as
 // the decode issues its code stream; loads past the block's end return
-// zero without a memory access), then write_bytes bytes written per wave at
-// its end (8 bytes per lane per 512-byte row, as the decode stores its
-// output rows).  Each lane also writes one checksum word.
+// zero without a memory access), then `idle` sleeps of 512 cycles each
+// with nothing in flight (standing in for the work a decode wave does after
+// its loads return), then write_bytes bytes written per wave at its end (8
+// bytes per lane per 512-byte row, as the decode stores its output rows).
+// Each lane also writes one checksum word.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void stream_ref_kernel(const uint8_t *src, uint32_t per_wave, float *dst,
-                                                        uint32_t write_bytes, uint32_t *out) {
+                                                        uint32_t write_bytes, int idle, uint32_t *out) {
   const int lane = threadIdx.x;
   const BufRsrc rs = buf_rsrc(src + (size_t)blockIdx.x * per_wave, (int)per_wave);
   uint32_t acc = 0;
@@ -418,16 +420,17 @@ __global__ __launch_bounds__(64) void stream_ref_kernel(const uint8_t *src, uint
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc += x[j].x ^ x[j].y ^ x[j].z ^ x[j].w;
   }
+  for (int i = 0; i < idle; ++i) __builtin_amdgcn_s_sleep(8);  // 8 x 64 cycles
   const float f = __uint_as_float(acc);
   float *row = dst + (size_t)blockIdx.x * (write_bytes / 4) + 2 * lane;
   for (uint32_t b = 0; b < write_bytes; b += 512, row += 128) st2(row, make_float2(f, f));
   out[(size_t)blockIdx.x * 64 + lane] = acc;
 }
 
-hipError_t launch_stream_ref(const void *src, uint32_t per_wave, void *dst, uint32_t write_bytes, int waves,
-                             uint32_t *out, hipStream_t stream) {
+hipError_t launch_stream_ref(const void *src, uint32_t per_wave, void *dst, uint32_t write_bytes, int idle,
+                             int waves, uint32_t *out, hipStream_t stream) {
   hipLaunchKernelGGL(stream_ref_kernel, dim3(waves), dim3(64), 0, stream, static_cast<const uint8_t *>(src),
-                     per_wave, static_cast<float *>(dst), write_bytes, out);
+                     per_wave, static_cast<float *>(dst), write_bytes, idle, out);
   return hipGetLastError();
 }
 

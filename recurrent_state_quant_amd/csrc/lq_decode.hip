@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
 // waves: with n <= 4,096 this fills the chip where one wave per state would
 // not (measured: +5% at 2,048 states, +18% for KDA at 4,096), while at
 // 8,192 states and more the one-wave kernel is faster (1.6%).
-template <bool KDA, bool DENSE>
+template <bool KDA, bool DENSE, bool LONG>
 __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -118,8 +118,8 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
   // ---- a2 history over this wave's rows, partial dots through LDS
   float P = 1.f;
   float *red = sh_red[w];
-  while (hi > 0) {
-    const int cnt = hi - lo;
+  // record dots of the chunk [lo_, lo_ + cnt), newest record first
+  auto chunk_dots = [&](const int lo_, const int cnt) {
 #pragma unroll
     for (int j = kRecChunk - 1; j >= 0; --j) {
       if (j < cnt) {
@@ -134,9 +134,7 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
         P *= KDA ? gr[j] : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), j));
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    lds_sync<true>();
     {
       const int v = lane & 31, half = lane >> 5;
       float acc = 0.f;
@@ -145,20 +143,19 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
         for (int m = 0; m < 16; ++m) acc += red[(16 * half + m) * kRedStride + v];
       }
       acc += __shfl_xor(acc, 32);
-      if (lane < 2 * cnt) reinterpret_cast<float *>(&sh_hp[w][lo + (lane >> 1)])[lane & 1] = acc;
+      if (lane < 2 * cnt) reinterpret_cast<float *>(&sh_hp[w][lo_ + (lane >> 1)])[lane & 1] = acc;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    hi = lo;
-    lo = hi > kRecChunk ? hi - kRecChunk : 0;
-    if (hi > 0) {
-      // Every load of the chunk just used has returned.  Saying so lets the
-      // next chunk's loads issue back to back: the compiler cannot pair the
-      // guarded loads (j < cnt) with their guarded uses, and would otherwise
-      // wait for each earlier load into the same registers first.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_sync<true>();
+  };
+  // The newest chunk (loaded above) outside any loop, so that its uses wait
+  // for its own loads only; older chunks (windows longer than kRecChunk + 1
+  // tokens) are loaded and used one after the other.
+  if (hi > 0) chunk_dots(lo, hi - lo);
+  if constexpr (LONG) {
+    for (hi = lo; hi > 0; hi = lo) {
+      lo = hi > kRecChunk ? hi - kRecChunk : 0;
       load_chunk(lo, hi - lo);
+      chunk_dots(lo, hi - lo);
     }
   }
   // ---- dense compensator tokens: records written before the window's
@@ -310,7 +307,7 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
       }
     }
     // older records (p > kRecChunk): kOldBatch loads in flight before use
-    for (int i0 = 0; i0 < ulo; i0 += kOldBatch) {
+    for (int i0 = 0; LONG && i0 < ulo; i0 += kOldBatch) {
       float uo[kOldBatch];
 #pragma unroll
       for (int j = 0; j < kOldBatch; ++j)
@@ -338,8 +335,10 @@ __global__ __launch_bounds__(128) void decode_step2_kernel(const DecodeArgs A) {
 
 template <bool KDA, bool DENSE>
 void launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
-  if (a.n <= kSmallSlab)
-    hipLaunchKernelGGL((decode_step2_kernel<KDA, DENSE>), dim3(a.n), dim3(128), 0, stream, a);
+  if (a.n <= kSmallSlab && a.p > kRecChunk + 1)
+    hipLaunchKernelGGL((decode_step2_kernel<KDA, DENSE, true>), dim3(a.n), dim3(128), 0, stream, a);
+  else if (a.n <= kSmallSlab)
+    hipLaunchKernelGGL((decode_step2_kernel<KDA, DENSE, false>), dim3(a.n), dim3(128), 0, stream, a);
   else if (a.p > kRecChunk + 1)
     hipLaunchKernelGGL((decode_step_kernel<KDA, DENSE, true>), dim3(a.n), dim3(64), 0, stream, a);
   else

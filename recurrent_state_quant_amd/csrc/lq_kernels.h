@@ -106,8 +106,8 @@ hipError_t launch_decode_step(const DecodeArgs &a, bool kda, hipStream_t stream)
 hipError_t launch_bf16w_decode(const Bf16WinArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_bf16w_close(const Bf16WinArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_dense_step(const DenseArgs &a, bool kda, bool bf16, hipStream_t stream);
-hipError_t launch_stream_ref(const void *src, uint32_t per_wave, void *dst, uint32_t write_bytes, int waves,
-                             uint32_t *out, hipStream_t stream);
+hipError_t launch_stream_ref(const void *src, uint32_t per_wave, void *dst, uint32_t write_bytes, int idle,
+                             int waves, uint32_t *out, hipStream_t stream);
 hipError_t launch_window_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_decode_close(const CloseArgs &a, bool kda, hipStream_t stream);
 hipError_t launch_quantize_state(const CloseArgs &a, hipStream_t stream);

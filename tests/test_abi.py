@@ -378,20 +378,25 @@ def test_bf16_window_validation(lib):
 
 def test_stream_reference_validation(lib):
     """The stream reference: read blocks a multiple of 1 KiB, written blocks
-    a multiple of 512 bytes, at least one wave, aligned pointers, outputs
-    outside the bytes read and apart from each other."""
+    a multiple of 512 bytes, idle sleeps in [0, 4096], at least one wave,
+    aligned pointers, outputs outside the bytes read and apart from each
+    other."""
     f = lib.leapquant_stream_reference
     src, dst, out = FAKE, FAKE + (1 << 24), FAKE + (1 << 25)
-    assert f(None, 1024, dst, 512, 4, out, None) == L.LQ_ERR_NULL
-    assert f(src, 1024, dst, 512, 4, None, None) == L.LQ_ERR_NULL
-    assert f(src, 1024, None, 512, 4, out, None) == L.LQ_ERR_NULL
-    for rb, wb, waves in ((0, 0, 4), (1000, 0, 4), (1536, 0, 4), ((1 << 30) + 1024, 0, 1), (1024, 0, 0),
-                          (1024, 0, -1), (1024, 256, 4), (1024, -512, 4), (1024, (1 << 30) + 512, 1)):
-        assert f(src, rb, dst, wb, waves, out, None) == L.LQ_ERR_SHAPE, (rb, wb, waves)
-    assert f(src + 8, 1024, dst, 512, 4, out, None) == L.LQ_ERR_ALIGN
-    assert f(src, 1024, dst + 8, 512, 4, out, None) == L.LQ_ERR_ALIGN
-    assert f(src, 1024, dst, 512, 4, out + 2, None) == L.LQ_ERR_ALIGN
-    assert f(src, 1024, dst, 512, 4, src + 4096 - 4, None) == L.LQ_ERR_ALIAS        # checksums over the last block
-    assert f(src, 1024, dst, 512, 4, src - 4 * 64 * 4 + 4, None) == L.LQ_ERR_ALIAS  # ... ending inside the first
-    assert f(src, 1024, src + 1024, 512, 4, out, None) == L.LQ_ERR_ALIAS            # writes over the reads
-    assert f(src, 1024, out - 16, 512, 4, out, None) == L.LQ_ERR_ALIAS              # writes over the checksums
+
+    def call(s_=src, rb=1024, d_=dst, wb=512, idle=0, waves=4, o_=out):
+        return f(s_, rb, d_, wb, idle, waves, o_, None)
+    assert call(s_=None) == L.LQ_ERR_NULL
+    assert call(o_=None) == L.LQ_ERR_NULL
+    assert call(d_=None) == L.LQ_ERR_NULL
+    for kw in (dict(rb=0), dict(rb=1000), dict(rb=1536), dict(rb=(1 << 30) + 1024, waves=1), dict(waves=0),
+               dict(waves=-1), dict(wb=256), dict(wb=-512), dict(wb=(1 << 30) + 512, waves=1), dict(idle=-1),
+               dict(idle=4097)):
+        assert call(**kw) == L.LQ_ERR_SHAPE, kw
+    assert call(s_=src + 8) == L.LQ_ERR_ALIGN
+    assert call(d_=dst + 8) == L.LQ_ERR_ALIGN
+    assert call(o_=out + 2) == L.LQ_ERR_ALIGN
+    assert call(o_=src + 4096 - 4) == L.LQ_ERR_ALIAS        # checksums over the last block
+    assert call(o_=src - 4 * 64 * 4 + 4) == L.LQ_ERR_ALIAS  # ... ending inside the first
+    assert call(d_=src + 1024) == L.LQ_ERR_ALIAS            # writes over the reads
+    assert call(d_=out - 16) == L.LQ_ERR_ALIAS              # writes over the checksums

@@ -22,15 +22,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("rb,wb,waves", [(1024, 512, 3), (5 * 1024, 0, 7), (16384, 1536, 5), (30 * 1024, 2048, 9),
-                                         (48 * 1024, 512, 2)])
-def test_checksums_and_rows(rb, wb, waves):
+@pytest.mark.parametrize("rb,wb,waves,idle", [(1024, 512, 3, 0), (5 * 1024, 0, 7, 2), (16384, 1536, 5, 0),
+                                              (30 * 1024, 2048, 9, 4), (48 * 1024, 512, 2, 0)])
+def test_checksums_and_rows(rb, wb, waves, idle):
     rng = np.random.default_rng(rb + wb + waves)
     host = rng.integers(0, 256, waves * rb, dtype=np.uint8)
     src = torch.as_tensor(host, device=DEV)
     dst = torch.zeros(waves * wb, dtype=torch.uint8, device=DEV) if wb else None
     out = torch.full((waves, 64), -1, dtype=torch.int32, device=DEV)
-    lq.leapquant_stream_reference(src, rb, dst, wb, out)
+    lq.leapquant_stream_reference(src, rb, dst, wb, out, idle_sleeps=idle)
     torch.cuda.synchronize()
     # lane l of wave w reads the 16 bytes at l * 16 of every 1 KiB chunk of its block
     w = host.view(np.uint32).reshape(waves, rb // 1024, 64, 4)

@@ -37,7 +37,7 @@ hipError_t launch_quantize_state(const CloseArgs &, hipStream_t) { return reache
 hipError_t launch_dequantize(const DequantArgs &, hipStream_t) { return reached("dequantize"); }
 hipError_t launch_mixed(const MixedArgs &, bool, hipStream_t) { return reached("mixed"); }
 bool mixed_supported(const CloseArgs &) { return true; }
-hipError_t launch_stream_ref(const void *, uint32_t, void *, uint32_t, int, uint32_t *, hipStream_t) {
+hipError_t launch_stream_ref(const void *, uint32_t, void *, uint32_t, int, int, uint32_t *, hipStream_t) {
   return reached("stream_ref");
 }
 }  // namespace lq
