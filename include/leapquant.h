@@ -275,8 +275,8 @@ int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const 
  * outside [0, p) are left as they are.  The result equals
  * leapquant_decode_step_slots over the positions with p - 1 replaced by -1
  * followed by leapquant_decode_close_list over the listed slots at p - 1,
- * bit for bit.  For slabs of more than 4,096 slots with p <= 16 and at
- * most 8 compensator rows (no dense compensator tokens) it is a single
+ * bit for bit.  For slabs of more than 4,096 slots with 4 <= p <= 16 and
+ * at most 8 compensator rows (no dense compensator tokens) it is a single
  * launch: the closing slots' workgroups run among the decode steps, which
  * keep memory busy around them, so the closes no longer cost a launch of
  * their own; other shapes run the two launches.  Arguments, list rules

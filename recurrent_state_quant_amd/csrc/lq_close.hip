@@ -970,12 +970,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
   }
 }
 
-// The single launch covers slabs above kSmallSlab, where the decode steps
-// it runs are the ones leapquant_decode_step_slots runs (the one-wave
-// kernel), so that both give identical results.
-bool mixed_supported(const CloseArgs &c) {
-  return c.comp_key == nullptr && c.p <= kSplitRecs && c.r <= 8 && c.n > kSmallSlab;
+// Windows the bf16-split close takes: row compensators (r <= 8) and 4 to 16
+// tokens.  Shorter windows take the fp32 close, whose contraction is sized
+// to the record count, where the split's is a fixed 16-record tile: at
+// p = 1 (the per-token baseline) that made the whole step 12% slower; at
+// p = 4 the two closes run even.
+static bool close16_covers(const CloseArgs &c) {
+  return c.comp_key == nullptr && c.p >= 4 && c.p <= kSplitRecs && c.r <= 8;
 }
+
+// The single launch covers the windows the bf16 close takes, on slabs above
+// kSmallSlab, where the decode steps it runs are the ones
+// leapquant_decode_step_slots runs (the one-wave kernel): both forms then
+// run the same kernels' code and give identical results.
+bool mixed_supported(const CloseArgs &c) { return close16_covers(c) && c.n > kSmallSlab; }
 
 hipError_t launch_mixed(const MixedArgs &a, bool kda, hipStream_t stream) {
   const int nd = (a.d.n + 3) / 4;
@@ -1050,9 +1058,7 @@ template <bool FUSED>
 hipError_t launch_close(const CloseArgs &a, bool kda, hipStream_t stream) {
   const dim3 grid(a.slots ? a.n_launch : a.n);
   const bool dense = a.comp_key != nullptr;
-  // windows of at most 16 records with at most 8 compensator rows: the
-  // bf16-split contraction (every record count of such a window is <= 16)
-  if (!dense && a.p <= kSplitRecs && a.r <= 8) {
+  if (close16_covers(a)) {
     if (kda)
       hipLaunchKernelGGL((close16_kernel<true, FUSED>), grid, dim3(256), 0, stream, a);
     else

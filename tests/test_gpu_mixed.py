@@ -4,8 +4,8 @@ over the positions with p - 1 made idle, then decode_close_list over the
 listed slots that sit at p - 1.  Both calls are checked against the oracle
 elsewhere (tests/test_gpu_slot_list.py, tests/test_gpu_sweep_slots.py).
 
-Cases cross the single-launch shapes (more than 4,096 slots, p <= 16,
-r <= 8) with the two-launch path (smaller slabs, p = 32, r = 16), both gates, slab sizes that are not multiples of
+Cases cross the single-launch shapes (more than 4,096 slots, 4 <= p <= 16,
+r <= 8) with the two-launch path (smaller slabs, p = 2 and 32, r = 16), both gates, slab sizes that are not multiples of
 the four slots a decode workgroup takes, idle and out-of-range positions,
 listed slots not at p - 1 (skipped), unlisted slots at p - 1 (untouched),
 ids outside [0, n) and an empty list.
@@ -41,7 +41,7 @@ def _slab(n, m, p, r, gate, b, recs, tile):
 
 @pytest.mark.parametrize("gate", ["gdn", "kda"])
 @pytest.mark.parametrize("n,p,r", [(4097, 16, 4), (4099, 16, 8), (8190, 16, 4), (5001, 16, 0), (13, 16, 4),
-                                   (301, 16, 4), (4201, 32, 4), (4400, 16, 16)])
+                                   (301, 16, 4), (4201, 32, 4), (4400, 16, 16), (4500, 4, 4), (4300, 2, 4)])
 @pytest.mark.parametrize("listing", ["all", "partial", "empty"])
 def test_mixed_equals_the_two_calls(gate, n, p, r, listing):
     rng = np.random.default_rng(9000 + n + 7 * p + r + 3 * (gate == "kda") + len(listing))
