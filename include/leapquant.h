@@ -211,8 +211,12 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t,
                            hipStream_t stream);
 
 /* Write the boundary state B = deQ(codes, a, s) + compensator rows as fp32
- * S_out [n][dk][dv] (the state the next window starts from; used for state
- * error tracking and prefix-cache reads).  S_out must not overlap `st`. */
+ * S_out [n][dk][dv]: the quantized residual plus the compensators that
+ * [EL] Figure 4 splits the state into, i.e. the state the next window
+ * starts from ([EL] Figure 2); used for state error tracking (the MSE of
+ * [EL] Figure 3) and prefix-cache reads.  Row-major, 16-byte aligned;
+ * S_out must not overlap `st` (LQ_ERR_ALIAS); other errors as for
+ * leapquant_quantize_state. */
 int leapquant_dequantize_state(const lq_params *prm, const lq_state *st,
                                float *S_out, hipStream_t stream);
 
