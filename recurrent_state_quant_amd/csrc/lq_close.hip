@@ -959,10 +959,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void m
     float2 *gy = reinterpret_cast<float2 *>(base);
     float2 *hh = gy + D;
     float2 *hc = hh + 64;
-    float2 *zz = hc + 16;
-    uint8_t *dig = reinterpret_cast<uint8_t *>(zz + D);
-    float *red = reinterpret_cast<float *>(dig + 8 * 2 * 64);
-    const DecodeLds Ls{gy, hh, hc, zz, dig, red};
+    float *red = reinterpret_cast<float *>(hc + 16);
+    // z and the digits share the record dots' transpose buffer
+    const DecodeLds Ls{gy, hh, hc, reinterpret_cast<float2 *>(red), reinterpret_cast<uint8_t *>(red) + D * 8, red};
     const DecodeArgs &A = M.d;
     const int lane = threadIdx.x & 63;
     constexpr bool DENSE = false, WAVE = true, LONG = false;  // p <= 16

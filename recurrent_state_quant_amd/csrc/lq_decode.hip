@@ -4,8 +4,11 @@
 
 namespace lq {
 
+// The GDN step of windows up to 17 tokens fits 128 VGPRs and 9,984 bytes
+// of LDS: four waves per SIMD (the others take what they need).
 template <bool KDA, bool DENSE, bool LONG>
-__global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KDA || DENSE || LONG ? 1 : 4))) void
+decode_step_kernel(const DecodeArgs A) {
   const int s = blockIdx.x;
   // per-slot positions (continuous batching): out-of-range slots are idle;
   // with skip_last the window's last position is left to a fused close
@@ -14,10 +17,10 @@ __global__ __launch_bounds__(64) void decode_step_kernel(const DecodeArgs A) {
   __shared__ float2 ls_gy[D];
   __shared__ float2 ls_h[64];
   __shared__ float2 ls_hc[DENSE ? 16 : 1];
-  __shared__ float2 ls_z[D];
-  __shared__ __attribute__((aligned(16))) uint8_t ls_dig[8 * 2 * 64];
   __shared__ __attribute__((aligned(16))) float ls_red[64 * kRedStride];
-  const DecodeLds Ls{ls_gy, ls_h, ls_hc, ls_z, ls_dig, ls_red};
+  // z and the digits share the record dots' transpose buffer
+  const DecodeLds Ls{ls_gy, ls_h, ls_hc, reinterpret_cast<float2 *>(ls_red),
+                     reinterpret_cast<uint8_t *>(ls_red) + D * 8, ls_red};
   const int lane = threadIdx.x;
   constexpr bool WAVE = false;
 #include "lq_decode_body.inc"

@@ -77,7 +77,12 @@ struct DecodeLds {
   uint8_t *dig;  // [8 * 2 * 64] digits [vector*4+digit][half][slot], 16-byte aligned
   float *red;    // [64 * kRedStride] transposed partials
 };
-constexpr int kDecodeLdsBytes = (D + 64 + 16 + D) * 8 + 8 * 2 * 64 + 64 * kRedStride * 4;
+// LDS bytes of one wave's decode step.  The GEMV's arrays (z: D float2,
+// digits: 8 x 2 x 64 bytes) live in the record dots' transpose buffer, which
+// is free by then, so that the one-wave kernel (without dense weights, under
+// 10 KB) fits sixteen workgroups per CU.
+constexpr int kDecodeLdsBytes = (D + 64 + 16) * 8 + 64 * kRedStride * 4;
+static_assert(D * 8 + 8 * 2 * 64 <= 64 * kRedStride * 4, "z and the digits fit in the transpose buffer");
 
 // LDS hand-off between the lanes of one wave: a wave's LDS operations
 // complete in order, so only the compiler must not move them across this
