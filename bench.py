@@ -146,6 +146,10 @@ def parse():
                     help="instead of the headline line, print one line with the stream reference at the "
                          "decode step's launch shape: the rate against an idle phase per wave after its "
                          "loads, and against waves per launch")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="instead of the headline line, print one line with the decode step's and the fused "
+                         "close's launch time against states per launch (the workload's gate, p and r; four "
+                         "layers cycled; 64 tokens; graph launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the short separate-close and KDA-workload runs reported beside the headline")
@@ -314,6 +318,9 @@ def main():
         return
     if args.stream_lab:
         print(json.dumps(stream_lab(cfg, dev)), flush=True)
+        return
+    if args.size_sweep:
+        print(json.dumps(size_sweep(cfg, dev)), flush=True)
         return
     kda = cfg.gate == "kda"
     T = args.tokens or cfg.steps
@@ -702,6 +709,35 @@ def stream_reference(dev, read_bytes, write_bytes, waves, slabs=4, reps=24, idle
     del srcs, dsts, out
     return {"read_bytes_per_wave": read_bytes, "write_bytes_per_wave": write_bytes, "waves": waves,
             "avg_launch_us": round(us, 2), "GBs": round((read_bytes + write_bytes) * waves / (us * 1e-6) / 1e9, 1)}
+
+
+def size_sweep(cfg, dev, sizes=(1, 64, 256, 1024, 2048, 4096, 8192, 16384, 32768), T=64):
+    """Launch time of the decode step and of the fused last-token close
+    against states per launch: the workload's gate, p and r with `size`
+    states per layer, four layers cycled (so that no launch finds its state
+    in a cache), the fused schedule over T tokens replayed from graphs
+    (run_schedule).  Rates use the algorithmic bytes of step_bytes and
+    fused_bytes."""
+    import dataclasses
+    import torch
+    from workloads import generators as G
+    kda = cfg.gate == "kda"
+    rows = []
+    for nl in sizes:
+        c = dataclasses.replace(cfg, batch=nl, heads=1, layers=4, steps=T)
+        g = G.make_generator(c.seed, dev)
+        S_init = G.initial_state(c, c.n_states, g, dev)
+        tok = G.token_inputs(c, c.n_states, T, g, dev)
+        run = run_schedule(c, S_init, tok, T, True, "graph", 2, 1, dev)
+        dec_b = nl * sum(step_bytes(t, c.dk, c.dv, c.r, kda) for t in range(c.p - 1)) / (c.p - 1)
+        fb = nl * fused_bytes(c.p - 1, c.dk, c.dv, c.r, kda)
+        d_us, c_us = run["dec_avg_ms"] * 1e3, run["close_avg_ms"] * 1e3
+        rows.append({"states_per_launch": nl, "decode_us": round(d_us, 2), "decode_TBs": round(dec_b / d_us / 1e6, 3),
+                     "fused_close_us": round(c_us, 2), "fused_close_TBs": round(fb / c_us / 1e6, 3)})
+        del S_init, tok
+        torch.cuda.empty_cache()
+    return {"metric": "launch time against states per launch (us; TB/s of algorithmic bytes)",
+            "workload": cfg.name, "gate": cfg.gate, "p": cfg.p, "r": cfg.r, "tokens": T, "rows": rows}
 
 
 def stream_lab(cfg, dev):
