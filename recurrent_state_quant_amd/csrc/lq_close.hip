@@ -923,21 +923,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void c
 // whose length is one workgroup's lifetime; they run among the decode
 // steps, which keep memory busy around them.
 // ---------------------------------------------------------------------------
+// GDN: 127 VGPRs and 40,448 bytes of LDS, four workgroups per CU; KDA's
+// decode body needs 154 VGPRs (three).
 template <bool KDA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void mixed_kernel(const MixedArgs M) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KDA ? 3 : 4))) void mixed_kernel(const MixedArgs M) {
   constexpr int kBytes = Close16Lds<true>::kBytes > 4 * kDecodeLdsBytes ? Close16Lds<true>::kBytes
                                                                           : 4 * kDecodeLdsBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes];
-  // The close workgroups are spread evenly through the grid (dispatch
-  // order): close i sits at position floor(i T / nc) of the T workgroups, so
-  // at any time about nc / T of the resident workgroups are closes (VALU
-  // work) and the rest decode steps (memory streams).  Workgroup b is a
-  // close iff ceil((b + 1) nc / T) > ceil(b nc / T); closes before it:
-  // ceil(b nc / T).
+  // The close workgroups are spread evenly through the first half of the
+  // grid (dispatch order): close i sits at position floor(i Tc / nc) of
+  // the first Tc = max(T / 2, nc) of the T workgroups, so that about nc / Tc
+  // of the resident workgroups are closes (VALU work) among decode steps
+  // (memory streams), and the last closes (a close workgroup lives several
+  // times as long as a decode step) finish before the decode steps do:
+  // spread over the whole grid they extended the launch's tail (0.86 of
+  // lockstep against 0.90).  Workgroup b < Tc is a close iff
+  // ceil((b + 1) nc / Tc) > ceil(b nc / Tc); closes before it: ceil(b nc /
+  // Tc), all nc of them from Tc on.
   const long long nc = M.c.n_launch;
   const long long T = gridDim.x, b = blockIdx.x;
-  const long long before = (b * nc + T - 1) / T;
-  const long long upto = ((b + 1) * nc + T - 1) / T;
+  const long long Tc = T / 2 > nc ? T / 2 : nc;  // closes within the first half of the grid
+  const long long before = b < Tc ? (b * nc + Tc - 1) / Tc : nc;
+  const long long upto = b < Tc ? ((b + 1) * nc + Tc - 1) / Tc : nc;
   if (upto > before) {
     const int slot = M.c.slots[before];
     if ((unsigned)slot >= (unsigned)M.c.n) return;
