@@ -117,6 +117,61 @@ bool overlaps_state(Range x, const lq_params *prm, const lq_state *st, bool boun
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_HIP; }
 
+// Kernel arguments of a call: the state's arrays (the window buffer too if
+// `buffer`) and the parameters.
+lq::CloseArgs close_args(const lq_params *prm, const lq_state *st, bool buffer) {
+  lq::CloseArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  if (buffer) {
+    a.buf_gate = st->buf_gate;
+    a.buf_k = st->buf_k;
+    a.buf_u = st->buf_u;
+  }
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.flags = prm->flags;
+  a.iters = prm->comp_iters;
+  return a;
+}
+
+// The token's inputs and output
+template <class Args>
+void set_token(Args &a, const float *q, const float *k, const float *v, const float *beta, const float *alpha,
+               float *o) {
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.o = o;
+}
+
+lq::DecodeArgs decode_args(const lq_params *prm, const lq_state *st, const float *q, const float *k,
+                           const float *v, const float *beta, const float *alpha, float *o) {
+  lq::DecodeArgs a{};
+  a.codes = st->codes;
+  a.row_scale = st->row_scale;
+  a.col_scale = st->col_scale;
+  a.comp_idx = st->comp_idx;
+  a.comp_val = st->comp_val;
+  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
+  a.buf_gate = st->buf_gate;
+  a.buf_k = st->buf_k;
+  a.buf_u = st->buf_u;
+  set_token(a, q, k, v, beta, alpha, o);
+  a.n = prm->n;
+  a.p = prm->p;
+  a.r = prm->r;
+  a.flags = prm->flags;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,20 +208,8 @@ int leapquant_quantize_state(const lq_params *prm, const float *S, const lq_stat
       overlap(src, key_span(prm, st)))
     return LQ_ERR_ALIAS;
   if ((rc = check_state_disjoint(prm, st, true, false))) return rc;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.iters = prm->comp_iters;
+  lq::CloseArgs a = close_args(prm, st, false);
   a.S_in = S;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
-  a.len = 0;
-  a.flags = prm->flags;
   return hip_status(lq::launch_quantize_state(a, stream));
 }
 
@@ -211,29 +254,9 @@ int leapquant_decode_step(const lq_params *prm, const lq_state *st, int32_t t, c
                           float *o, hipStream_t stream) {
   const int rc = check_token_call(prm, st, t, q, k, v, beta, alpha, o);
   if (rc) return rc;
-  const bool kda = prm->gate == LQ_GATE_KDA;
-  lq::DecodeArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.alpha = alpha;
-  a.o = o;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
+  lq::DecodeArgs a = decode_args(prm, st, q, k, v, beta, alpha, o);
   a.t = t;
-  a.flags = prm->flags;
-  return hip_status(lq::launch_decode_step(a, kda, stream));
+  return hip_status(lq::launch_decode_step(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
 int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len,
@@ -244,23 +267,8 @@ int leapquant_window_close(const lq_params *prm, const lq_state *st, int32_t len
   if ((rc = check_buffer(prm, st))) return rc;
   if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if (len < 1 || len > prm->p) return LQ_ERR_SHAPE;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.S_in = nullptr;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
+  lq::CloseArgs a = close_args(prm, st, true);
   a.len = len;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -269,29 +277,9 @@ int leapquant_decode_close(const lq_params *prm, const lq_state *st, int32_t t, 
                            float *o, hipStream_t stream) {
   const int rc = check_token_call(prm, st, t, q, k, v, beta, alpha, o);
   if (rc) return rc;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.S_in = nullptr;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.alpha = alpha;
-  a.o = o;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
+  lq::CloseArgs a = close_args(prm, st, true);
+  set_token(a, q, k, v, beta, alpha, o);
   a.len = t;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -312,28 +300,8 @@ int leapquant_decode_step_slots(const lq_params *prm, const lq_state *st, const 
   int rc = check_token_call(prm, st, 0, q, k, v, beta, alpha, o);
   if (rc) return rc;
   if ((rc = check_slots(prm, st, pos, o))) return rc;
-  lq::DecodeArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.alpha = alpha;
-  a.o = o;
+  lq::DecodeArgs a = decode_args(prm, st, q, k, v, beta, alpha, o);
   a.pos = pos;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
-  a.t = 0;
-  a.flags = prm->flags;
   return hip_status(lq::launch_decode_step(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -343,29 +311,9 @@ int leapquant_decode_close_slots(const lq_params *prm, const lq_state *st, const
   int rc = check_token_call(prm, st, 0, q, k, v, beta, alpha, o);
   if (rc) return rc;
   if ((rc = check_slots(prm, st, pos, o))) return rc;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.alpha = alpha;
-  a.o = o;
+  lq::CloseArgs a = close_args(prm, st, true);
+  set_token(a, q, k, v, beta, alpha, o);
   a.lens = pos;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
-  a.len = 0;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -377,23 +325,9 @@ int leapquant_window_close_slots(const lq_params *prm, const lq_state *st, const
   if ((rc = check_buffer(prm, st))) return rc;
   if ((rc = check_state_disjoint(prm, st, true, true))) return rc;
   if ((rc = check_slots(prm, st, len, nullptr))) return rc;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
+  lq::CloseArgs a = close_args(prm, st, true);
   a.lens = len;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
   a.len = 1;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -422,31 +356,11 @@ int leapquant_decode_close_list(const lq_params *prm, const lq_state *st, const 
   if ((rc = check_slots(prm, st, pos, o))) return rc;
   if ((rc = check_list(prm, st, pos, list, count, o))) return rc;
   if (count == 0) return LQ_OK;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.alpha = alpha;
-  a.o = o;
+  lq::CloseArgs a = close_args(prm, st, true);
+  set_token(a, q, k, v, beta, alpha, o);
   a.lens = pos;
   a.slots = list;
   a.n_launch = count;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
-  a.len = 0;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_decode_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 
@@ -460,53 +374,15 @@ int leapquant_decode_step_close_list(const lq_params *prm, const lq_state *st, c
   if ((rc = check_list(prm, st, pos, list, count, o))) return rc;
   lq::MixedArgs m{};
   lq::DecodeArgs &d = m.d;
-  d.codes = st->codes;
-  d.row_scale = st->row_scale;
-  d.col_scale = st->col_scale;
-  d.comp_idx = st->comp_idx;
-  d.comp_val = st->comp_val;
-  d.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  d.buf_gate = st->buf_gate;
-  d.buf_k = st->buf_k;
-  d.buf_u = st->buf_u;
-  d.q = q;
-  d.k = k;
-  d.v = v;
-  d.beta = beta;
-  d.alpha = alpha;
-  d.o = o;
+  d = decode_args(prm, st, q, k, v, beta, alpha, o);
   d.pos = pos;
-  d.n = prm->n;
-  d.p = prm->p;
-  d.r = prm->r;
-  d.t = 0;
-  d.flags = prm->flags;
   d.skip_last = true;
   lq::CloseArgs &c = m.c;
-  c.codes = st->codes;
-  c.row_scale = st->row_scale;
-  c.col_scale = st->col_scale;
-  c.comp_idx = st->comp_idx;
-  c.comp_val = st->comp_val;
-  c.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  c.buf_gate = st->buf_gate;
-  c.buf_k = st->buf_k;
-  c.buf_u = st->buf_u;
-  c.q = q;
-  c.k = k;
-  c.v = v;
-  c.beta = beta;
-  c.alpha = alpha;
-  c.o = o;
+  c = close_args(prm, st, true);
+  set_token(c, q, k, v, beta, alpha, o);
   c.lens = pos;
   c.slots = list;
   c.n_launch = count;
-  c.n = prm->n;
-  c.p = prm->p;
-  c.r = prm->r;
-  c.len = 0;
-  c.flags = prm->flags;
-  c.iters = prm->comp_iters;
   c.only_last = true;
   const bool kda = prm->gate == LQ_GATE_KDA;
   if (lq::mixed_supported(c)) return hip_status(lq::launch_mixed(m, kda, stream));
@@ -525,25 +401,11 @@ int leapquant_window_close_list(const lq_params *prm, const lq_state *st, const 
   if ((rc = check_slots(prm, st, len, nullptr))) return rc;
   if ((rc = check_list(prm, st, len, list, count, nullptr))) return rc;
   if (count == 0) return LQ_OK;
-  lq::CloseArgs a{};
-  a.codes = st->codes;
-  a.row_scale = st->row_scale;
-  a.col_scale = st->col_scale;
-  a.comp_idx = st->comp_idx;
-  a.comp_val = st->comp_val;
-  a.comp_key = dense_comp(prm) ? st->comp_key : nullptr;
-  a.buf_gate = st->buf_gate;
-  a.buf_k = st->buf_k;
-  a.buf_u = st->buf_u;
+  lq::CloseArgs a = close_args(prm, st, true);
   a.lens = len;
   a.slots = list;
   a.n_launch = count;
-  a.n = prm->n;
-  a.p = prm->p;
-  a.r = prm->r;
   a.len = 1;
-  a.flags = prm->flags;
-  a.iters = prm->comp_iters;
   return hip_status(lq::launch_window_close(a, prm->gate == LQ_GATE_KDA, stream));
 }
 

@@ -57,10 +57,11 @@ struct CloseArgs {
 };
 
 // One launch for a continuous-batching token: the fused decode_close of the
-// listed slots at their window's last position (the first workgroups), and
-// the decode step of every slot at positions 0 .. p-2 (four slots per
-// workgroup after those).  Supported for windows of up to 16 records with
-// at most 8 compensator rows (row compensators).
+// listed slots at their window's last position (workgroups spread through
+// the first half of the grid), and the decode step of every slot at
+// positions 0 .. p-2 (four slots per workgroup).  mixed_supported() names
+// the shapes it covers (windows of 4 to 16 tokens, at most 8 compensator
+// rows, slabs above 4,096 slots); others take two launches.
 struct MixedArgs {
   DecodeArgs d;   // pos = the per-slot positions, skip_last = true
   CloseArgs c;    // lens = the same positions, slots = the list, only_last = true
