@@ -11,6 +11,8 @@ distinct states, so that the decode step and the fused close run the
 one-wave decode kernel and large launches.  The cases are fixed by the
 seed, so a failure names a reproducible configuration.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,12 @@ from tests.test_gpu_parity import (_dev, _gate, _oracle_records, _random_window_
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 200
+# Wider runs of the same generators: LQ_SWEEP_SCALE multiplies the case
+# counts, LQ_SWEEP_SEED moves every seed to another family (0, the default:
+# the committed cases).
+SCALE = int(os.environ.get("LQ_SWEEP_SCALE", "1"))
+SEED_SHIFT = 10_000_000 * int(os.environ.get("LQ_SWEEP_SEED", "0"))
+N_CASES = 200 * SCALE
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,7 +44,7 @@ def _gpu():
 
 
 def _case(i):
-    rng = np.random.default_rng(90000 + i)
+    rng = np.random.default_rng(90000 + i + SEED_SHIFT)
     gate = ["gdn", "kda"][rng.integers(2)]
     p = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 31, 32, 48, 64]))
     r = int(rng.choice([0, 1, 2, 4, 7, 8, 16]))
@@ -111,11 +118,11 @@ def test_sweep(i):
 # Slabs above 4,096 states take the one-wave decode kernel (the throughput
 # workload's): a slab is tiled from m distinct states, so that the oracle
 # computes m states while every slot is still compared.
-N_LARGE = 60
+N_LARGE = 60 * SCALE
 
 
 def _large_case(i):
-    rng = np.random.default_rng(5150000 + 11 * i)
+    rng = np.random.default_rng(5150000 + 11 * i + SEED_SHIFT)
     gate = ["gdn", "kda"][rng.integers(2)]
     p = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 31, 32, 48, 64]))
     r = int(rng.choice([0, 1, 2, 4, 7, 8, 16]))

@@ -12,6 +12,8 @@ state within the fp32 tolerance; a bf16 state within one bf16 step plus the
 fp32 error of the terms it sums, with at most 0.1% of elements off the
 oracle's rounding.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,7 +27,12 @@ from tests.test_gpu_parity import (_bf16_ulp, _dev, _gate, _oracle_records, _ran
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 160
+# Wider runs of the same generators: LQ_SWEEP_SCALE multiplies the case
+# counts, LQ_SWEEP_SEED moves every seed to another family (0, the default:
+# the committed cases).
+SCALE = int(os.environ.get("LQ_SWEEP_SCALE", "1"))
+SEED_SHIFT = 10_000_000 * int(os.environ.get("LQ_SWEEP_SEED", "0"))
+N_CASES = 160 * SCALE
 KEYS = ("q", "k", "v", "beta", "alpha")
 
 
@@ -54,7 +61,7 @@ def _bf16_dev(B64, tile):
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_baselines(i):
-    rng = np.random.default_rng(7270000 + 13 * i)
+    rng = np.random.default_rng(7270000 + 13 * i + SEED_SHIFT)
     gate = ["gdn", "kda"][rng.integers(2)]
     flags = O.NO_DELTA if rng.random() < 0.3 else 0
     entry = ["fp32_steps", "bf16_step", "bf16w_decode", "bf16w_close"][rng.integers(4)]

@@ -11,6 +11,8 @@ compared with the oracle at its own position; idle slots, and slots left out
 of a list, must keep their o row (pre-filled with NaN) and their boundary
 state bit for bit.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,7 +25,12 @@ from tests.test_gpu_parity import _dev, _gate, _oracle_records, _random_window_i
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 300
+# Wider runs of the same generators: LQ_SWEEP_SCALE multiplies the case
+# counts, LQ_SWEEP_SEED moves every seed to another family (0, the default:
+# the committed cases).
+SCALE = int(os.environ.get("LQ_SWEEP_SCALE", "1"))
+SEED_SHIFT = 10_000_000 * int(os.environ.get("LQ_SWEEP_SEED", "0"))
+N_CASES = 300 * SCALE
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,7 +44,7 @@ def _gpu():
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_slots(i):
-    rng = np.random.default_rng(6160000 + 7 * i)
+    rng = np.random.default_rng(6160000 + 7 * i + SEED_SHIFT)
     gate = ["gdn", "kda"][rng.integers(2)]
     p = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 32, 64]))
     r = int(rng.choice([0, 2, 4, 8, 16]))
