@@ -91,6 +91,16 @@ __device__ __forceinline__ uint32_t bld1(BufRsrc r, int off) {
 __device__ __forceinline__ void st2(float *p, float2 v) {
   __builtin_nontemporal_store(vf2{v.x, v.y}, reinterpret_cast<vf2 *>(p));
 }
+// The same 8 bytes as an ordinary write-back store.  The GDN decode step
+// writes its three 512-byte rows per state this way: a whole window of the
+// batch-256 workload (60 decode launches and 4 fused closes) ran 0.6-0.85%
+// faster than with nontemporal stores, in alternating runs of the two
+// builds.  Elsewhere nontemporal stores measured faster and stay: the KDA
+// and two-wave steps (KDA's window 1.7%), the fused close (2.8%) and a
+// plain stream of the decode's shape (4%).
+__device__ __forceinline__ void st2_wb(float *p, float2 v) {
+  *reinterpret_cast<vf2 *>(p) = vf2{v.x, v.y};
+}
 __device__ __forceinline__ void st4(float *p, float4 v) {
   __builtin_nontemporal_store(vf4{v.x, v.y, v.z, v.w}, reinterpret_cast<vf4 *>(p));
 }
