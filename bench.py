@@ -526,7 +526,7 @@ def ablations(args, cfg, dev, reps=3):
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True,
                                            dense=bool(flags & lq.LQ_DENSE_COMP) and r > 0)
 
-    def slots(p, r, compact=False, mixed=False, grouped=False):
+    def slots(p, r, compact=False, mixed=False, grouped=False, concurrent=False):
         # continuous batching: every slot has its own window phase (seeded,
         # uniform), so about 1/p of the slots close at every token; the
         # positions live on the device.  (Phases strided by a multiple of 8
@@ -548,10 +548,28 @@ def ablations(args, cfg, dev, reps=3):
         close_pos = [torch.where(x == p - 1, x, -1).to(torch.int32) for x in pos]
         # compact: the ids of the slots that close at token t, one workgroup each
         close_list = [torch.nonzero(x == p - 1).flatten().to(torch.int32) for x in pos]
+        # concurrent: the closing slots' closes on a second stream (default
+        # priority) beside the other slots' decode step; the next token's
+        # step of a layer waits for that layer's closes
+        side = torch.cuda.Stream(device=dev) if concurrent else None
 
         def run():
+            main = torch.cuda.current_stream(dev)
+            joins = [None] * L
             for t in range(T):
                 for l in range(L):
+                    if concurrent:
+                        if joins[l] is not None:
+                            main.wait_event(joins[l])
+                        fork = torch.cuda.Event()
+                        fork.record(main)
+                        side.wait_event(fork)
+                        with torch.cuda.stream(side):
+                            lq.leapquant_decode_close_list(views[l], pos[t], close_list[t], *targs(t, l))
+                        joins[l] = torch.cuda.Event()
+                        joins[l].record(side)
+                        lq.leapquant_decode_step_slots(views[l], step_pos[t], *targs(t, l))
+                        continue
                     if mixed:
                         lq.leapquant_decode_step_close_list(views[l], pos[t], close_list[t], *targs(t, l))
                         continue
@@ -560,6 +578,9 @@ def ablations(args, cfg, dev, reps=3):
                         lq.leapquant_decode_close_list(views[l], pos[t], close_list[t], *targs(t, l))
                     else:
                         lq.leapquant_decode_close_slots(views[l], close_pos[t], *targs(t, l))
+            for e in joins:
+                if e is not None:
+                    main.wait_event(e)
         value = timed(run)
         del slab, views
         return value, bytes_per_head_token(p, cfg.dk, cfg.dv, r, kda, fused=True)
@@ -592,7 +613,9 @@ def ablations(args, cfg, dev, reps=3):
                ("continuous batching, one launch per token (closing slots' workgroups spread among the decode steps)",
                 lambda: slots(cfg.p, cfg.r, mixed=True)),
                ("continuous batching, one launch per token, four consecutive slots sharing a phase",
-                lambda: slots(cfg.p, cfg.r, mixed=True, grouped=True))]
+                lambda: slots(cfg.p, cfg.r, mixed=True, grouped=True)),
+               ("continuous batching, the closing slots' closes on a second stream beside the decode steps",
+                lambda: slots(cfg.p, cfg.r, concurrent=True))]
     DC = lq.LQ_DENSE_COMP
     rows_dc = [("row compensators", lambda: windowed(cfg.p, cfg.r, 0))] + \
         [(f"dense tokens, {i} subspace iteration{'s' if i != 1 else ''}", (lambda i=i: windowed(cfg.p, cfg.r, DC, i)))

@@ -89,3 +89,59 @@ def test_mixed_equals_the_two_calls(gate, n, p, r, listing):
     assert not torch.isnan(oa[torch.as_tensor(decoded, device=DEV)]).any()
     if listing != "empty" and len(ref_list):
         assert not torch.isnan(oa[torch.as_tensor(ref_list.astype(np.int64), device=DEV)]).any()
+
+
+@pytest.mark.parametrize("gate", ["gdn", "kda"])
+def test_two_stream_schedule_equals_single_launch(gate):
+    """The continuous-batching schedule with the closing slots' closes on a
+    second stream beside the other slots' decode step (decode_close_list and
+    decode_step_slots on disjoint slots, joined by events before the next
+    token) gives the single-launch results bit for bit, token after token."""
+    rng = np.random.default_rng(9100 + (gate == "kda"))
+    n, p, r, m, L = 4500, 8, 4, 11, 2
+    T = 2 * p + 3
+    b, recs = _random_window_inputs(rng, m, p, p - 1, gate, r)
+    tile = np.arange(n) % m
+    phase = rng.integers(0, p, n).astype(np.int32)
+    toks = [_token(rng, m, gate) for _ in range(T)]
+    args = [[_dev(tk[x][tile]) for x in ("q", "k", "v", "beta", "alpha")] for tk in toks]
+    a = [_slab(n, m, p, r, gate, b, recs, tile) for _ in range(L)]
+    bb = [_slab(n, m, p, r, gate, b, recs, tile) for _ in range(L)]
+    oa = [[torch.full((n, 128), float("nan"), device=DEV) for _ in range(L)] for _ in range(T)]
+    ob = [[x.clone() for x in row] for row in oa]
+    pos = [(phase + t) % p for t in range(T)]
+    pos_d = [torch.as_tensor(x, device=DEV) for x in pos]
+    lst = [torch.as_tensor(np.nonzero(x == p - 1)[0].astype(np.int32), device=DEV) for x in pos]
+    step = [torch.as_tensor(np.where(x == p - 1, -1, x).astype(np.int32), device=DEV) for x in pos]
+    for t in range(T):
+        for l in range(L):
+            lq.leapquant_decode_step_close_list(a[l], pos_d[t], lst[t], *args[t], oa[t][l])
+    torch.cuda.synchronize()
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    joins = [None] * L
+    for t in range(T):
+        for l in range(L):
+            if joins[l] is not None:
+                main.wait_event(joins[l])
+            fork = torch.cuda.Event()
+            fork.record(main)
+            side.wait_event(fork)
+            with torch.cuda.stream(side):
+                lq.leapquant_decode_close_list(bb[l], pos_d[t], lst[t], *args[t], ob[t][l])
+            joins[l] = torch.cuda.Event()
+            joins[l].record(side)
+            lq.leapquant_decode_step_slots(bb[l], step[t], *args[t], ob[t][l])
+    for e in joins:
+        main.wait_event(e)
+    torch.cuda.synchronize()
+
+    for t in range(T):
+        for l in range(L):
+            assert not torch.isnan(oa[t][l]).any()
+            torch.testing.assert_close(oa[t][l], ob[t][l], rtol=0, atol=0, msg=lambda s, t=t: f"o at token {t}: {s}")
+    for l in range(L):
+        for k in ("codes", "row_scale", "col_scale", "comp_idx", "comp_val", "buf_gate", "buf_k", "buf_u"):
+            torch.testing.assert_close(getattr(a[l], k), getattr(bb[l], k), rtol=0, atol=0,
+                                       msg=lambda s, k=k: f"{k}: {s}")
