@@ -826,8 +826,8 @@ def _oracle_group(job):
 def cpu_baseline(args, cfg, S_init, tok, comp_flags=0, iters=0):
     """The CPU oracle, free-running on bounded samples of the same inputs.
 
-    All cores: one worker process per host core (at most 16, the box's share
-    for one GPU), each decoding its own group of `cpu_sample_states` states
+    All cores: one worker process per host core (at most 16, the host's
+    share for one GPU), each decoding its own group of `cpu_sample_states` states
     of layer 0 over all tokens; the rate is the groups' head-tokens over the
     wall time from the common start to the last worker's end.  One process:
     groups decoded one after another until about `cpu_seconds` have passed.
