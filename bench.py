@@ -376,6 +376,18 @@ def main():
     wr = 512 * (3 + (1 if kda else 0))
     stream_ref = stream_reference(dev, max(1, round((dec_bytes / nl - wr) / 1024)) * 1024, wr, nl)
     stream_ref["decode_frac_of_stream"] = round(dec_gbs / stream_ref["GBs"], 4)
+    # the same plain stream with the close's bytes per state, one wave per
+    # state and as many waves as one close launch: the boundary state it
+    # writes (and o_t when fused) at the end of the wave, the rest read.  A
+    # third of the close's bytes are writes, which the device moves more
+    # slowly than reads; this is the rate of that mix with no arithmetic.
+    if not dense:
+        cw = _boundary_rw(cfg.dk, cfg.dv, cfg.r, False) // 2 + (4 * cfg.dv if fused else 0)
+        cwr = max(512, round(cw / 512) * 512)
+        crd = max(1024, round((close_state_bytes - cw) / 1024) * 1024)
+        close_mix = stream_reference(dev, crd, cwr, close_states)
+        close_mix["close_frac_of_stream"] = round(close_gbs / close_mix["GBs"], 4)
+        stream_ref["close_mix"] = close_mix
     whole_gbs = value * bpht / 1e9
     traffic = {} if dense else measured_traffic(cfg)
     dkey = "decode_fused" if fused else "decode_separate"
