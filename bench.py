@@ -381,7 +381,10 @@ def main():
     # writes (and o_t when fused) at the end of the wave, the rest read.  A
     # third of the close's bytes are writes, which the device moves more
     # slowly than reads; this is the rate of that mix with no arithmetic.
-    if not dense:
+    # Part of the context (skipped with --no-context, as in the profiled
+    # runs, whose stream-reference dispatches then all have the decode's
+    # shape).
+    if not dense and not args.no_context:
         cw = _boundary_rw(cfg.dk, cfg.dv, cfg.r, False) // 2 + (4 * cfg.dv if fused else 0)
         cwr = max(512, round(cw / 512) * 512)
         crd = max(1024, round((close_state_bytes - cw) / 1024) * 1024)
