@@ -38,8 +38,7 @@ constexpr int kSmallSlab = 4096;
 // stream are in flight before the first wait; the records' u rows are
 // issued after the record dots and arrive during the GEMV.  Record t's k~
 // and gate depend only on the inputs and are stored as soon as they are
-// known: stores left to the end of a wave hold it (and its registers) until
-// they drain, which measurably lowers the streaming rate.
+// known; o_t and u_t close the wave.
 // ---------------------------------------------------------------------------
 constexpr int kCompEarly = 4;    // compensator rows loaded with the records
 constexpr int kCompBatch = 4;    // later compensator rows: loads issued together, then used
